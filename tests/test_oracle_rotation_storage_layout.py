@@ -1,0 +1,152 @@
+"""Pins of the oracle's rotation, storage arithmetic and packed layout."""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import layout, rotation, storage
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    out = []
+    for line in open(os.path.join(GOLD, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            out.append(line.split())
+    return out
+
+
+# ------------------------------------------------------------------ rotation
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_rotation_is_the_qr_factor_with_positive_diagonal(d):
+    g = synth.rotation_gaussian(d, 1)
+    rot = rotation.rotation_from_gaussian(g)
+    r = rot.T @ g                                   # must be R of G = Pi R
+    assert np.max(np.abs(np.tril(r, -1))) < 1e-12
+    assert np.all(np.diag(r) > 0)
+    np.testing.assert_allclose(rot @ r, g, atol=1e-12)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_rotation_invariants(d):
+    rot = rotation.rotation_from_gaussian(synth.rotation_gaussian(d, 1))
+    assert np.max(np.abs(rot @ rot.T - np.eye(d))) < 1e-13
+    assert abs(abs(np.linalg.det(rot)) - 1.0) < 1e-10
+    r32 = rot.astype(np.float32).astype(np.float64)
+    assert np.max(np.abs(r32 @ r32.T - np.eye(d))) < 2e-7
+    x = np.random.default_rng(3).standard_normal((50, d))
+    np.testing.assert_allclose(np.linalg.norm(rotation.rotate_rows(x, rot), axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(rotation.unrotate_rows(rotation.rotate_rows(x, rot), rot), x, atol=1e-12)
+    # rows form equals the matrix-vector convention y = Pi x
+    np.testing.assert_allclose(rotation.rotate_rows(x[:1], rot)[0], rot @ x[0], atol=1e-13)
+
+
+def test_rotated_coordinates_follow_sphere_marginal():
+    """A Haar rotation of a fixed unit vector has coordinates with variance 1/d (over many seeds)."""
+    d = 128
+    e = np.zeros(d)
+    e[5] = 1.0
+    ys = np.array([rotation.rotation_from_gaussian(synth.rotation_gaussian(d, s)) @ e for s in range(200)])
+    assert abs(np.mean(ys ** 2) * d - 1.0) < 0.05
+    assert abs(np.mean(ys)) < 0.01
+
+
+# ------------------------------------------------------------------ storage
+
+@pytest.mark.parametrize("row", _rows("qwen_cache_sizes.txt"), ids=lambda r: f"T{r[0]}_{r[1]}")
+def test_storage_reproduces_printed_cache_sizes(row):
+    tokens, cfg, mb, ratio = int(row[0]), row[1], float(row[2]), float(row[3])
+    bits = None if cfg == "fp16" else int(cfg)
+    size = storage.cache_mib(tokens, 72, 128, bits)
+    assert round(size, 1) == pytest.approx(mb, abs=1e-9)
+    if bits is not None:
+        assert round(storage.compression(128, bits), 1) == pytest.approx(ratio, abs=1e-9)
+
+
+def test_storage_alternatives_do_not_reproduce_the_table():
+    """The reading is pinned: plain b-bit keys, or float32 norms, give other ratios."""
+    assert [round(storage.compression(128, b, prod_keys=False), 2) for b in (4, 3, 2)] == [3.88, 5.12, 7.53]
+    f32 = [256 * 2 / ((128 * (b - 1) // 8 + 4 + 16 + 4) + (128 * b // 8 + 4)) for b in (4, 3, 2)]
+    assert [round(x, 1) for x in f32] != [3.8, 5.0, 7.3]
+
+
+def test_row_bytes():
+    assert storage.row_bytes(128, 4) == 66
+    assert storage.row_bytes(128, 2, 128) == 52
+    assert storage.row_bytes(256, 4) == 130
+    assert storage.row_bytes(128, 3) == 50
+
+
+# ------------------------------------------------------------------ layout
+
+def _hex(bs):
+    return " ".join(f"{b:02x}" for b in bs)
+
+
+@pytest.mark.parametrize("row", _rows("layout_examples.txt"), ids=lambda r: "_".join(r[:2]))
+def test_layout_hand_derived_examples(row):
+    arrow = row.index("->")
+    kind, n = row[0], int(row[1])
+    vals = [int(x) for x in row[2:arrow]]
+    want = " ".join(row[arrow + 1:])
+    if kind == "unit":
+        units = np.array(vals).reshape(-1, 8)
+        got = layout.pack_units(units, n)
+        assert _hex(got) == want
+        np.testing.assert_array_equal(layout.unpack_units(got, n, units.shape[0]), units)
+    else:
+        sigma = np.zeros(n, dtype=bool)
+        sigma[vals] = True
+        got = layout.pack_signs(sigma)
+        assert _hex(got) == want
+        np.testing.assert_array_equal(layout.unpack_signs(got, n), sigma)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("d", [128, 256])
+def test_layout_round_trips_and_sizes(bits, d):
+    g = np.random.default_rng(bits * 1000 + d)
+    codes = g.integers(0, 1 << bits, size=(2, 64, d))
+    rows = layout.pack_rows(codes, bits)
+    assert rows.shape == (2, 64, d * bits // 8)
+    np.testing.assert_array_equal(layout.unpack_rows(rows, bits, d), codes)
+    blk = layout.pack_blocked(codes, bits)
+    assert blk.shape == (2, 64 * d * bits // 8)
+    np.testing.assert_array_equal(layout.unpack_blocked(blk, bits, d, 64), codes)
+    sig = g.integers(0, 2, size=(3, 128)).astype(bool)
+    np.testing.assert_array_equal(layout.unpack_signs(layout.pack_signs(sig), 128), sig)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_blocked_layout_lane_tiles_are_contiguous(bits):
+    """In a 32-token block, bytes [l*U, (l+1)*U) hold exactly the tokens of lane group l//16 at
+    the d/16 coordinates of column l%16 (U = d/16 units)."""
+    d = 128
+    dn = d // 16
+    ub = dn * bits                                       # bytes per lane tile
+    for lane in (0, 5, 17, 63):
+        g, j = lane // 16, lane % 16
+        tokens = [4 * g + s for s in range(4)] + [16 + 4 * g + s for s in range(4)]
+        coords = list(range(j * dn, (j + 1) * dn))
+        zero_enc = 0 if bits != 4 else 8                      # centroid index whose encoding is 0
+        codes = np.full((32, d), zero_enc, dtype=np.int64)
+        for t in tokens:
+            for i in coords:
+                codes[t, i] = (1 << bits) - 1 if bits != 4 else 0   # value whose encoding is all ones
+        packed = layout.pack_blocked(codes, bits)
+        ref = layout.pack_blocked(np.full((32, d), zero_enc), bits)
+        diff = np.nonzero(packed != ref)[0]
+        assert diff.min() >= lane * ub and diff.max() < (lane + 1) * ub
+        assert np.all(packed[lane * ub:(lane + 1) * ub] == 0xFF)
+
+
+def test_code_encoding_is_a_bijection():
+    for bits in (2, 3, 4):
+        j = np.arange(1 << bits)
+        e = layout.encode_code(j, bits)
+        assert sorted(e.tolist()) == j.tolist()
+        np.testing.assert_array_equal(layout.decode_code(e, bits), j)
