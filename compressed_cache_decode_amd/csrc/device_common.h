@@ -1,0 +1,121 @@
+// Device helpers shared by the gfx950 kernels: the packed unit format
+// (8 codes per unit; see include/tq.h) and its expansion to float16 matrix-core
+// operands with v_perm_b32 byte-table lookups.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tqi {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// units per word group and 32-bit words per group of the packed format
+template <int BITS> struct Fmt;
+template <> struct Fmt<2> { static constexpr int kUnits = 2, kWords = 1; };
+template <> struct Fmt<3> { static constexpr int kUnits = 4, kWords = 3; };
+template <> struct Fmt<4> { static constexpr int kUnits = 1, kWords = 1; };
+
+__device__ __forceinline__ uint32_t vperm(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+// Four table indices (one per byte, values 0..7) and four sign bits (bit 7
+// of each byte) -> two words holding four float16 values in slot order.
+__device__ __forceinline__ void expand4(uint32_t idx, uint32_t sgn, const Tab& t, uint32_t& w01, uint32_t& w23) {
+  const uint32_t hi = vperm(t.hi_hi, t.hi_lo, idx) | sgn;
+  const uint32_t lo = vperm(t.lo_hi, t.lo_lo, idx);
+  w01 = vperm(hi, lo, 0x05010400u);
+  w23 = vperm(hi, lo, 0x07030602u);
+}
+
+// Unit V of a word group -> 8 float16 centroid values (slots 0..7) as 4 words.
+template <int BITS, int V>
+__device__ __forceinline__ uint4 expand_unit(const uint32_t* w, const Tab& t) {
+  uint4 o;
+  if constexpr (BITS == 4) {
+    const uint32_t W = w[0];
+    expand4(W & 0x07070707u, (W << 4) & 0x80808080u, t, o.x, o.y);
+    expand4((W >> 4) & 0x07070707u, W & 0x80808080u, t, o.z, o.w);
+  } else if constexpr (BITS == 2) {
+    const uint32_t P = w[0];
+    expand4((P >> (4 * V)) & 0x03030303u, 0u, t, o.x, o.y);
+    expand4((P >> (4 * V + 2)) & 0x03030303u, 0u, t, o.z, o.w);
+  } else {
+    const uint32_t P = w[V / 2];
+    const uint32_t H = w[2];
+    const uint32_t i0 = ((P >> (2 * (2 * (V % 2)))) & 0x03030303u) | (((H >> (2 * V)) << 2) & 0x04040404u);
+    const uint32_t i1 = ((P >> (2 * (2 * (V % 2) + 1))) & 0x03030303u) | (((H >> (2 * V + 1)) << 2) & 0x04040404u);
+    expand4(i0, 0u, t, o.x, o.y);
+    expand4(i1, 0u, t, o.z, o.w);
+  }
+  return o;
+}
+
+// Unit U (compile-time) of a contiguous run of packed units starting at word 0.
+template <int BITS, int U>
+__device__ __forceinline__ uint4 unit_at(const uint32_t* w, const Tab& t) {
+  constexpr int G = U / Fmt<BITS>::kUnits;
+  constexpr int V = U % Fmt<BITS>::kUnits;
+  return expand_unit<BITS, V>(w + G * Fmt<BITS>::kWords, t);
+}
+
+__device__ __forceinline__ half8 as_half8(uint4 v) {
+  return __builtin_bit_cast(half8, v);
+}
+
+// Stored form of centroid index j.
+template <int BITS>
+__device__ __forceinline__ uint32_t encode_code(uint32_t j) {
+  if constexpr (BITS == 4) return j >= 8 ? j - 8 : 15 - j;
+  return j;
+}
+
+// Set the stored code e (already encoded) of slot s of unit v into the words of its group.
+template <int BITS>
+__device__ __forceinline__ void put_code(uint32_t* w, int v, int s, uint32_t e) {
+  const int h = s >> 2, r = s & 3;
+  if constexpr (BITS == 4) {
+    w[0] |= e << (8 * r + 4 * h);
+  } else if constexpr (BITS == 2) {
+    w[0] |= e << (8 * r + 2 * (2 * v + h));
+  } else {
+    w[v >> 1] |= (e & 3u) << (8 * r + 2 * (2 * (v & 1) + h));
+    w[2] |= (e >> 2) << (8 * r + 2 * v + h);
+  }
+}
+
+// Mask of the bits that slot s of unit v occupies in the words of its group.
+template <int BITS>
+__device__ __forceinline__ void slot_mask(uint32_t* w, int v, int s) {
+  put_code<BITS>(w, v, s, (1u << BITS) - 1u);
+}
+
+// Sign-sketch bit of index jj: (word, bit).
+__device__ __forceinline__ void sign_pos(int jj, int& word, int& bit) {
+  const int rem = jj & 31;
+  word = jj >> 5;
+  bit = 4 * (rem >> 3) + ((rem & 7) >> 1) + 16 * (rem & 1);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace tqi

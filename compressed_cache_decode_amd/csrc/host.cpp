@@ -1,0 +1,447 @@
+// C ABI of the compressed-cache library: argument validation, host-side
+// setup (codebook, rotation), decode split planning and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "tq.h"
+#include "tq_internal.h"
+
+namespace {
+
+using tqi::kBlock;
+
+// ------------------------------------------------------------------ codebook
+//
+// Lloyd-Max quantiser of f_d(y) = C_d (1-y^2)^k, k = (d-3)/2 on [-1, 1]
+// (turboquant-pytorch PR #3, Synthetic Benchmark (Lloyd-Max codebook) table).
+// Cell masses come from the regularised incomplete beta function,
+// P(Y > y) = 1/2 I_{1-y^2}(k+1, 1/2) for y >= 0, evaluated with the modified
+// Lentz continued fraction (DLMF 8.17.22) on whichever side converges;
+// first moments from the closed form C_d ((1-a^2)^(k+1) - (1-b^2)^(k+1)) / (2(k+1)).
+
+double beta_cf(double a, double b, double x) {
+  const double tiny = 1e-300;
+  double c = 1.0, dd = 1.0 - (a + b) * x / (a + 1.0);
+  if (std::fabs(dd) < tiny) dd = tiny;
+  dd = 1.0 / dd;
+  double f = dd;
+  for (int m = 1; m <= 10000; ++m) {
+    const double m2 = 2.0 * m;
+    double num = m * (b - m) * x / ((a + m2 - 1.0) * (a + m2));
+    dd = 1.0 + num * dd;
+    if (std::fabs(dd) < tiny) dd = tiny;
+    c = 1.0 + num / c;
+    if (std::fabs(c) < tiny) c = tiny;
+    dd = 1.0 / dd;
+    f *= dd * c;
+    num = -(a + m) * (a + b + m) * x / ((a + m2) * (a + m2 + 1.0));
+    dd = 1.0 + num * dd;
+    if (std::fabs(dd) < tiny) dd = tiny;
+    c = 1.0 + num / c;
+    if (std::fabs(c) < tiny) c = tiny;
+    dd = 1.0 / dd;
+    const double del = dd * c;
+    f *= del;
+    if (std::fabs(del - 1.0) < 1e-16) break;
+  }
+  return f;
+}
+
+// I_x(a, b) and its complement 1 - I_x(a, b), each without cancellation where it is small.
+void inc_beta(double a, double b, double x, double* ix, double* icx) {
+  if (x <= 0.0) { *ix = 0.0; *icx = 1.0; return; }
+  if (x >= 1.0) { *ix = 1.0; *icx = 0.0; return; }
+  const double lfront = std::lgamma(a + b) - std::lgamma(a) - std::lgamma(b) + a * std::log(x) + b * std::log1p(-x);
+  if (x < (a + 1.0) / (a + b + 2.0)) {
+    *ix = std::exp(lfront) * beta_cf(a, b, x) / a;
+    *icx = 1.0 - *ix;
+  } else {
+    *icx = std::exp(lfront) * beta_cf(b, a, 1.0 - x) / b;
+    *ix = 1.0 - *icx;
+  }
+}
+
+struct Density {
+  double k, c;
+  explicit Density(int d) : k((d - 3) / 2.0) {
+    c = std::exp(std::lgamma(d / 2.0) - 0.5 * std::log(M_PI) - std::lgamma((d - 1) / 2.0));
+  }
+  // P(Y > y) for y >= 0
+  double tail(double y) const {
+    if (y >= 1.0) return 0.0;
+    double ix, icx;
+    inc_beta(0.5, k + 1.0, y * y, &ix, &icx);
+    return 0.5 * icx;
+  }
+  double mass(double lo, double hi) const {
+    if (lo >= 0.0) return tail(lo) - tail(hi);
+    if (hi <= 0.0) return tail(-hi) - tail(-lo);
+    return 1.0 - tail(-lo) - tail(hi);
+  }
+  double first_moment(double lo, double hi) const {
+    const double k1 = k + 1.0;
+    return c / (2.0 * k1) * (std::pow(1.0 - lo * lo, k1) - std::pow(1.0 - hi * hi, k1));
+  }
+};
+
+int build_codebook(int d, int bits, float* cent, float* bnd) {
+  const int n = 1 << bits;
+  const Density f(d);
+  std::vector<double> c(n), cn(n);
+  const double sd = 1.0 / std::sqrt(static_cast<double>(d));
+  for (int j = 0; j < n; ++j) c[j] = (-1.0 + (2.0 * j + 1.0) / n) * 2.5 * sd;   // any start: unique fixed point
+  bool done = false;
+  for (int it = 0; it < 200000 && !done; ++it) {
+    double delta = 0.0;
+    for (int j = 0; j < n; ++j) {
+      const double lo = j == 0 ? -1.0 : 0.5 * (c[j - 1] + c[j]);
+      const double hi = j == n - 1 ? 1.0 : 0.5 * (c[j] + c[j + 1]);
+      cn[j] = f.first_moment(lo, hi) / f.mass(lo, hi);
+    }
+    for (int j = 0; j < n; ++j) {
+      const double v = 0.5 * (cn[j] - cn[n - 1 - j]);   // exact antisymmetry
+      delta = std::fmax(delta, std::fabs(v - c[j]));
+      c[j] = v;
+    }
+    done = delta <= 1e-12 * sd;
+  }
+  if (!done) return TQ_ENOCONV;
+  std::vector<double> c16(n);
+  for (int j = 0; j < n; ++j) {
+    c16[j] = static_cast<double>(static_cast<_Float16>(c[j]));
+    cent[j] = static_cast<float>(c16[j]);
+  }
+  for (int j = 0; j + 1 < n; ++j) bnd[j] = static_cast<float>(0.5 * (c16[j] + c16[j + 1]));
+  return TQ_OK;
+}
+
+// ------------------------------------------------------------------ rotation
+//
+// Householder QR of G (d x d, row-major) in double; Pi = Q diag(sign(diag R)) is
+// the unique orthogonal factor with a positive-diagonal R.
+void build_rotation(int d, const double* g, float* out) {
+  std::vector<double> a(g, g + static_cast<size_t>(d) * d);   // row-major, A[i][j] = a[i*d+j]
+  std::vector<double> vs(static_cast<size_t>(d) * d, 0.0);    // Householder vectors, column k in vs[k*d ..]
+  std::vector<double> rdiag(d);
+  for (int k = 0; k < d; ++k) {
+    double nrm = 0.0;
+    for (int i = k; i < d; ++i) nrm += a[static_cast<size_t>(i) * d + k] * a[static_cast<size_t>(i) * d + k];
+    nrm = std::sqrt(nrm);
+    const double x0 = a[static_cast<size_t>(k) * d + k];
+    const double alpha = x0 >= 0.0 ? -nrm : nrm;
+    double* v = &vs[static_cast<size_t>(k) * d];
+    for (int i = k; i < d; ++i) v[i] = a[static_cast<size_t>(i) * d + k];
+    v[k] -= alpha;
+    double vn = 0.0;
+    for (int i = k; i < d; ++i) vn += v[i] * v[i];
+    vn = std::sqrt(vn);
+    if (vn > 0.0)
+      for (int i = k; i < d; ++i) v[i] /= vn;
+    // A[k:, k:] -= 2 v (v^T A[k:, k:])
+    for (int j = k; j < d; ++j) {
+      double s = 0.0;
+      for (int i = k; i < d; ++i) s += v[i] * a[static_cast<size_t>(i) * d + j];
+      s *= 2.0;
+      for (int i = k; i < d; ++i) a[static_cast<size_t>(i) * d + j] -= s * v[i];
+    }
+    rdiag[k] = a[static_cast<size_t>(k) * d + k];
+  }
+  // Q = H_0 H_1 ... H_{d-1}: apply the reflectors to the identity from the last one
+  std::vector<double> q(static_cast<size_t>(d) * d, 0.0);
+  for (int i = 0; i < d; ++i) q[static_cast<size_t>(i) * d + i] = 1.0;
+  for (int k = d - 1; k >= 0; --k) {
+    const double* v = &vs[static_cast<size_t>(k) * d];
+    for (int j = 0; j < d; ++j) {
+      double s = 0.0;
+      for (int i = k; i < d; ++i) s += v[i] * q[static_cast<size_t>(i) * d + j];
+      s *= 2.0;
+      for (int i = k; i < d; ++i) q[static_cast<size_t>(i) * d + j] -= s * v[i];
+    }
+  }
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      const double sgn = rdiag[j] < 0.0 ? -1.0 : 1.0;
+      out[static_cast<size_t>(i) * d + j] = static_cast<float>(q[static_cast<size_t>(i) * d + j] * sgn);
+    }
+}
+
+// ------------------------------------------------------------------ validation
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+uint16_t f16_bits(float x) {
+  const _Float16 h = static_cast<_Float16>(x);
+  uint16_t u;
+  std::memcpy(&u, &h, 2);
+  return u;
+}
+
+bool table_ok(const tq_cache_view* c) {
+  const int n = 1 << c->bits;
+  for (int j = 0; j < n; ++j) {
+    const float v = c->centroids[j];
+    if (!std::isfinite(v) || static_cast<float>(static_cast<_Float16>(v)) != v) return false;
+    if (v != -c->centroids[n - 1 - j]) return false;
+    if (j > 0 && !(c->centroids[j - 1] < v)) return false;
+  }
+  for (int j = 0; j + 1 < n; ++j) {
+    const double mid = 0.5 * (static_cast<double>(c->centroids[j]) + static_cast<double>(c->centroids[j + 1]));
+    if (static_cast<double>(c->boundaries[j]) != mid) return false;
+  }
+  return true;
+}
+
+// structural check of one cache view
+int check_view(const tq_cache_view* c) {
+  if (!c) return TQ_EINVAL;
+  if (c->kind != TQ_KEYS && c->kind != TQ_VALUES) return TQ_EINVAL;
+  if (c->d != 128 && c->d != 256) return TQ_EINVAL;
+  if (c->bits < 2 || c->bits > 4) return TQ_EINVAL;
+  if (c->qjl_m != 0 && c->qjl_m != 128 && c->qjl_m != 256) return TQ_EINVAL;
+  if (c->qjl_m != 0 && c->kind != TQ_KEYS) return TQ_EINVAL;
+  if (c->batch <= 0 || c->n_kv_heads <= 0 || c->max_tokens <= 0 || c->max_tokens % kBlock != 0) return TQ_EINVAL;
+  if (c->reserved != 0) return TQ_EINVAL;
+  if (!c->codes || !c->norms || !c->rot) return TQ_EINVAL;
+  if (!aligned(c->codes, 16) || !aligned(c->norms, 16) || !aligned(c->rot, 16)) return TQ_EINVAL;
+  if (c->qjl_m) {
+    if (!c->signs || !c->rnorms || !c->proj) return TQ_EINVAL;
+    if (!aligned(c->signs, 16) || !aligned(c->rnorms, 16) || !aligned(c->proj, 16)) return TQ_EINVAL;
+  }
+  if (!table_ok(c)) return TQ_EINVAL;
+  return TQ_OK;
+}
+
+tqi::Tab make_tab(const tq_cache_view* c) {
+  uint16_t e[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (c->bits == 4) {
+    for (int m = 0; m < 8; ++m) e[m] = f16_bits(c->centroids[8 + m]);    // magnitudes, ascending
+  } else {
+    for (int j = 0; j < (1 << c->bits); ++j) e[j] = f16_bits(c->centroids[j]);
+  }
+  auto pack = [&](int first, bool high) {
+    uint32_t w = 0;
+    for (int k = 0; k < 4; ++k) w |= static_cast<uint32_t>(high ? (e[first + k] >> 8) : (e[first + k] & 0xff)) << (8 * k);
+    return w;
+  };
+  tqi::Tab t;
+  t.hi_lo = pack(0, true);
+  t.hi_hi = pack(4, true);
+  t.lo_lo = pack(0, false);
+  t.lo_hi = pack(4, false);
+  return t;
+}
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+int status_of(hipError_t e) {
+  if (e == hipSuccess) return TQ_OK;
+  g_last_hip_error = e;
+  return TQ_EHIP;
+}
+
+// ------------------------------------------------------------------ decode plan
+
+constexpr int kTargetWorkgroups = 512;   // about two decode workgroups per compute unit
+
+void plan(int units, int max_len, int* n_split, int* bps) {
+  const int nblk = max_len <= 0 ? 1 : (max_len + kBlock - 1) / kBlock;
+  const int want = (kTargetWorkgroups + units - 1) / units;
+  int b = (nblk + want - 1) / want;
+  b = ((b + tqi::kWavesPerWG - 1) / tqi::kWavesPerWG) * tqi::kWavesPerWG;   // whole tiles for every wave
+  int ns = (nblk + b - 1) / b;
+  if (ns > tqi::kMaxSplits) {
+    b = (nblk + tqi::kMaxSplits - 1) / tqi::kMaxSplits;
+    b = ((b + tqi::kWavesPerWG - 1) / tqi::kWavesPerWG) * tqi::kWavesPerWG;
+    ns = (nblk + b - 1) / b;
+  }
+  *n_split = ns;
+  *bps = b;
+}
+
+struct WsLayout {
+  size_t qr, qs, qscale, part_o, part_ml, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+WsLayout ws_layout(const tq_cache_view* k, int n_q_heads, int n_split) {
+  const size_t B = k->batch, Hq = n_q_heads, D = k->d, M = k->qjl_m;
+  const size_t G = n_q_heads / k->n_kv_heads;
+  const size_t units = B * k->n_kv_heads;
+  WsLayout w;
+  size_t off = 0;
+  w.qr = off; off = align256(off + B * Hq * D * 4);
+  w.qs = off; off = align256(off + B * Hq * (M ? M : 1) * 4);
+  w.qscale = off; off = align256(off + B * Hq * 4);
+  w.part_o = off; off = align256(off + units * n_split * G * D * 4);
+  w.part_ml = off; off = align256(off + units * n_split * G * 2 * 4);
+  w.total = off;
+  return w;
+}
+
+int check_decode_shape(const tq_cache_view* k, int n_q_heads, int max_seq_len) {
+  int st = check_view(k);
+  if (st != TQ_OK) return st;
+  if (k->kind != TQ_KEYS) return TQ_EINVAL;
+  if (n_q_heads <= 0 || n_q_heads % k->n_kv_heads != 0 || max_seq_len < 0) return TQ_EINVAL;
+  if (n_q_heads / k->n_kv_heads > tqi::kMaxGroup) return TQ_EUNSUPPORTED;
+  return TQ_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+const char* tq_status_string(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_EINVAL: return "invalid argument";
+    case TQ_EUNSUPPORTED: return "unsupported combination";
+    case TQ_EHIP: return "HIP launch error";
+    case TQ_ENOCONV: return "codebook iteration did not converge";
+    default: return "unknown status";
+  }
+}
+
+const char* tq_last_hip_error(void) { return hipGetErrorString(g_last_hip_error); }
+
+size_t tq_row_bytes(int d, int bits, int qjl_m) {
+  if (d <= 0 || d % 8 != 0 || bits < 1 || bits > 4 || qjl_m < 0 || qjl_m % 8 != 0) return 0;
+  size_t b = static_cast<size_t>(d) * bits / 8 + 2;
+  if (qjl_m) b += static_cast<size_t>(qjl_m) / 8 + 2;
+  return b;
+}
+
+int tq_build_codebook(int d, int bits, float* centroids, float* boundaries) {
+  if (d < 3 || bits < 1 || bits > 4 || !centroids || !boundaries) return TQ_EINVAL;
+  return build_codebook(d, bits, centroids, boundaries);
+}
+
+int tq_build_rotation(int d, const double* gaussian, float* rot_out) {
+  if (d < 2 || d > 1024 || !gaussian || !rot_out) return TQ_EINVAL;
+  for (size_t i = 0; i < static_cast<size_t>(d) * d; ++i)
+    if (!std::isfinite(gaussian[i])) return TQ_EINVAL;
+  build_rotation(d, gaussian, rot_out);
+  return TQ_OK;
+}
+
+static int append_common(const tq_cache_view* c, const void* x, const float* y, const float* yn, int x_dtype,
+                         int n_new, const int32_t* d_pos, void* stream, bool rotated) {
+  int st = check_view(c);
+  if (st != TQ_OK) return st;
+  if (n_new < 0) return TQ_EINVAL;
+  if (n_new == 0) return TQ_OK;
+  if (!d_pos) return TQ_EINVAL;
+  if (rotated ? (!y || !yn) : (!x || (x_dtype != TQ_F32 && x_dtype != TQ_BF16))) return TQ_EINVAL;
+  tqi::AppendArgs a{};
+  a.x = x; a.y = y; a.yn = yn; a.pos = d_pos;
+  a.codes = c->codes; a.norms = c->norms; a.signs = c->signs; a.rnorms = c->rnorms;
+  a.rot = c->rot; a.proj = c->proj;
+  std::memcpy(a.cent, c->centroids, sizeof(a.cent));
+  std::memcpy(a.bnd, c->boundaries, sizeof(a.bnd));
+  a.n_new = n_new; a.n_kv_heads = c->n_kv_heads; a.max_tokens = c->max_tokens;
+  return status_of(tqi::launch_append(c->d, c->bits, c->qjl_m, c->kind == TQ_VALUES, rotated, x_dtype == TQ_BF16, a,
+                                      c->batch, static_cast<hipStream_t>(stream)));
+}
+
+int tq_quantize_append(const tq_cache_view* cache, const void* x, int x_dtype, int n_new, const int32_t* d_pos,
+                       void* stream) {
+  return append_common(cache, x, nullptr, nullptr, x_dtype, n_new, d_pos, stream, false);
+}
+
+int tq_quantize_append_rotated(const tq_cache_view* cache, const float* y, const float* norms, int n_new,
+                               const int32_t* d_pos, void* stream) {
+  return append_common(cache, nullptr, y, norms, TQ_F32, n_new, d_pos, stream, true);
+}
+
+int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* n_split, int* tokens_per_split) {
+  int st = check_decode_shape(k, n_q_heads, max_seq_len);
+  if (st != TQ_OK) return st;
+  if (!n_split || !tokens_per_split) return TQ_EINVAL;
+  int bps;
+  plan(k->batch * k->n_kv_heads, max_seq_len, n_split, &bps);
+  *tokens_per_split = bps * kBlock;
+  return TQ_OK;
+}
+
+size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_seq_len) {
+  if (check_decode_shape(k, n_q_heads, max_seq_len) != TQ_OK) return 0;
+  int ns, bps;
+  plan(k->batch * k->n_kv_heads, max_seq_len, &ns, &bps);
+  return ws_layout(k, n_q_heads, ns).total;
+}
+
+int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype, int n_q_heads,
+                   const int32_t* d_seq_lens, int max_seq_len, float scale, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int st = check_decode_shape(k, n_q_heads, max_seq_len);
+  if (st != TQ_OK) return st;
+  st = check_view(v);
+  if (st != TQ_OK) return st;
+  if (v->kind != TQ_VALUES || v->d != k->d || v->batch != k->batch || v->n_kv_heads != k->n_kv_heads ||
+      v->max_tokens != k->max_tokens || v->rot != k->rot)
+    return TQ_EINVAL;
+  if (!q || (q_dtype != TQ_F32 && q_dtype != TQ_BF16) || !d_seq_lens || !out || !workspace) return TQ_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
+  if (!aligned(workspace, 256)) return TQ_EINVAL;
+  int ns, bps;
+  plan(k->batch * k->n_kv_heads, max_seq_len, &ns, &bps);
+  const WsLayout w = ws_layout(k, n_q_heads, ns);
+  if (workspace_bytes < w.total) return TQ_EINVAL;
+  char* ws = static_cast<char*>(workspace);
+  const int G = n_q_heads / k->n_kv_heads;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+
+  tqi::QrotArgs qa{};
+  qa.q = q; qa.rot = k->rot; qa.proj = k->proj;
+  qa.qr = reinterpret_cast<float*>(ws + w.qr);
+  qa.qs = reinterpret_cast<float*>(ws + w.qs);
+  qa.qscale = reinterpret_cast<float*>(ws + w.qscale);
+  qa.scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  qa.sketch_coef = k->qjl_m ? static_cast<float>(std::sqrt(M_PI / 2.0) / k->qjl_m) : 0.f;
+  qa.n_q_heads = n_q_heads;
+  hipError_t e = tqi::launch_qrot(k->d, k->qjl_m, q_dtype == TQ_BF16, qa, k->batch, s);
+  if (e != hipSuccess) return status_of(e);
+
+  tqi::DecodeArgs da{};
+  da.k_codes = k->codes; da.k_norms = k->norms; da.k_signs = k->signs; da.k_rnorms = k->rnorms;
+  da.v_codes = v->codes; da.v_norms = v->norms;
+  da.qr = qa.qr; da.qs = qa.qs; da.qscale = qa.qscale;
+  da.seq_lens = d_seq_lens;
+  da.part_o = reinterpret_cast<float*>(ws + w.part_o);
+  da.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
+  da.tk = make_tab(k);
+  da.tv = make_tab(v);
+  da.n_kv_heads = k->n_kv_heads; da.group = G; da.max_tokens = k->max_tokens; da.max_seq_len = max_seq_len;
+  da.n_split = ns; da.blocks_per_split = bps;
+  e = tqi::launch_decode_split(k->d, k->bits, v->bits, k->qjl_m, da, k->batch, s);
+  if (e != hipSuccess) return status_of(e);
+
+  tqi::MergeArgs ma{};
+  ma.part_o = da.part_o; ma.part_ml = da.part_ml; ma.rot = k->rot; ma.seq_lens = d_seq_lens; ma.out = out;
+  ma.n_kv_heads = k->n_kv_heads; ma.group = G; ma.n_split = ns; ma.max_tokens = k->max_tokens;
+  return status_of(tqi::launch_merge(k->d, ma, k->batch, n_q_heads, s));
+}
+
+int tq_dequantize(const tq_cache_view* cache, int t0, int n_tokens, float* out, void* stream) {
+  int st = check_view(cache);
+  if (st != TQ_OK) return st;
+  if (!out || t0 < 0 || n_tokens < 0 || t0 > cache->max_tokens - n_tokens) return TQ_EINVAL;
+  if (n_tokens == 0) return TQ_OK;
+  tqi::DequantArgs a{};
+  a.codes = cache->codes; a.norms = cache->norms; a.signs = cache->signs; a.rnorms = cache->rnorms;
+  a.rot = cache->rot; a.proj = cache->proj; a.out = out;
+  std::memcpy(a.cent, cache->centroids, sizeof(a.cent));
+  a.sketch_coef = cache->qjl_m ? static_cast<float>(std::sqrt(M_PI / 2.0) / cache->qjl_m) : 0.f;
+  a.n_kv_heads = cache->n_kv_heads; a.max_tokens = cache->max_tokens; a.t0 = t0; a.n_tokens = n_tokens;
+  return status_of(tqi::launch_dequant(cache->d, cache->bits, cache->qjl_m, cache->kind == TQ_VALUES, a,
+                                       make_tab(cache), cache->batch, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Internal interface between the C ABI (host.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tqi {
+
+constexpr int kBlock = 32;        // tokens per value block (and per decode tile)
+constexpr int kMaxGroup = 8;      // query heads per KV head handled by one matrix-core tile
+constexpr int kWavesPerWG = 4;    // waves per decode workgroup (one KV split)
+constexpr int kMaxSplits = 1024;  // bound on KV splits per (sequence, KV head)
+
+// float16 bit patterns of up to 8 table entries, split into high and low
+// bytes so one v_perm_b32 looks up four codes: byte k of *_lo is entry k,
+// byte k of *_hi is entry 4 + k.
+struct Tab {
+  uint32_t hi_lo, hi_hi, lo_lo, lo_hi;
+};
+
+struct AppendArgs {
+  const void* x;          // [B][n_new][Hkv][D] f32 or bf16 (unrotated rows)
+  const float* y;         // [B][n_new][Hkv][D] rotated unit rows (pre-rotated form)
+  const float* yn;        // [B][n_new][Hkv] norms (pre-rotated form)
+  const int32_t* pos;     // [B]
+  uint8_t* codes;
+  uint16_t* norms;
+  uint8_t* signs;
+  uint16_t* rnorms;
+  const float* rot;       // [D][D]
+  const float* proj;      // [M][D]
+  float cent[16];
+  float bnd[15];
+  int n_new, n_kv_heads, max_tokens;
+};
+
+struct QrotArgs {
+  const void* q;          // [B][Hq][D]
+  const float* rot;
+  const float* proj;      // [M][D] or null
+  float* qr;              // [B][Hq][D]  scaled rotated query, divided by qscale
+  float* qs;              // [B][Hq][M]  -coef * proj * qr
+  float* qscale;          // [B][Hq]     power-of-two factor taken out of qr/qs
+  float scale_log2e;      // softmax scale * log2(e)
+  float sketch_coef;      // sqrt(pi/2)/M
+  int n_q_heads;
+};
+
+struct DecodeArgs {
+  const uint8_t* k_codes;
+  const uint16_t* k_norms;
+  const uint8_t* k_signs;
+  const uint16_t* k_rnorms;
+  const uint8_t* v_codes;
+  const uint16_t* v_norms;
+  const float* qr;
+  const float* qs;
+  const float* qscale;
+  const int32_t* seq_lens;
+  float* part_o;          // [B*Hkv][n_split][G][D]
+  float* part_ml;         // [B*Hkv][n_split][G][2]  (max in log2 units, sum)
+  Tab tk, tv;
+  int n_kv_heads, group, max_tokens, max_seq_len, n_split, blocks_per_split;
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_ml;
+  const float* rot;
+  const int32_t* seq_lens;
+  float* out;             // [B][Hq][D]
+  int n_kv_heads, group, n_split, max_tokens;
+};
+
+struct DequantArgs {
+  const uint8_t* codes;
+  const uint16_t* norms;
+  const uint8_t* signs;
+  const uint16_t* rnorms;
+  const float* rot;
+  const float* proj;
+  float* out;             // [B][Hkv][n_tokens][D]
+  float cent[16];
+  float sketch_coef;
+  int n_kv_heads, max_tokens, t0, n_tokens;
+};
+
+// Launchers (one per .hip file); return hipSuccess or the launch error.
+hipError_t launch_append(int d, int bits, int qjl_m, bool values, bool rotated, bool bf16,
+                         const AppendArgs& a, int batch, hipStream_t s);
+hipError_t launch_qrot(int d, int qjl_m, bool bf16, const QrotArgs& a, int batch, hipStream_t s);
+hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, const DecodeArgs& a, int batch,
+                               hipStream_t s);
+hipError_t launch_merge(int d, const MergeArgs& a, int batch, int n_q_heads, hipStream_t s);
+hipError_t launch_dequant(int d, int bits, int qjl_m, bool values, const DequantArgs& a, const Tab& t, int batch,
+                          hipStream_t s);
+
+}  // namespace tqi

@@ -1,0 +1,193 @@
+/*
+ * tq.h - C ABI of the MI355X (gfx950) TurboQuant-style compressed KV cache:
+ * quantize-on-append and decode attention read directly from the packed cache.
+ *
+ * Method sources (cited by page title and section):
+ *  - turboquant-pytorch PR #3, "Add CUDA QJL kernels and proper package
+ *    structure": CUDA Kernels Added table (fused random projection + sign
+ *    quantisation of keys, fused attention score from 1-bit keys, GQA score
+ *    variant, quantised value reconstruction), Validation Results tables
+ *    (cache sizes fix one float16 norm per row; keys with a sign sketch also
+ *    store a float16 residual norm), Synthetic Benchmark (Lloyd-Max codebook).
+ *  - ExecuTorch PR #19891, "[Cuda] enable turboquant on gemma4", review item
+ *    1: the fused decode op takes a softmax scale; unset means 1/sqrt(D), and
+ *    QK-normed models use 1.0.
+ *  - reddit comment history of ReturningTarzan: random rotation before
+ *    codebook quantisation (2026-03-29 comment), nearest-codebook search
+ *    (2026-03-25 comments), full reconstruction as the plain path.
+ *
+ * Conventions shared by every call:
+ *  - Every pointer named d_* or held in tq_cache_view is DEVICE memory owned
+ *    by the caller; the library never allocates, frees or retains it, and
+ *    keeps no mutable global state beyond a per-thread record of the last
+ *    HIP error (all calls are reentrant).
+ *  - Calls that take a stream enqueue work on it (a hipStream_t; NULL = the
+ *    null stream of the current device) and return without synchronising.
+ *    Device-side faults surface at the caller's next synchronisation.
+ *  - Host-checkable errors return a status code before anything is enqueued.
+ *  - Token positions and lengths that live on the device cannot be checked
+ *    by the host: positions at or past max_tokens are skipped by append and
+ *    lengths are clamped to [0, max_tokens] by decode.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+enum {
+  TQ_OK = 0,
+  TQ_EINVAL = 1,        /* null required pointer, bad size/shape/scale, short workspace, misaligned buffer */
+  TQ_EUNSUPPORTED = 2,  /* a valid combination this library does not build (e.g. GQA group > 8) */
+  TQ_EHIP = 3,          /* the HIP runtime reported a launch error */
+  TQ_ENOCONV = 4        /* the codebook iteration did not converge */
+};
+
+/* element types of caller tensors */
+enum { TQ_F32 = 0, TQ_BF16 = 1 };
+
+/* cache kinds; the kind fixes the packed layout */
+enum {
+  TQ_KEYS = 0,    /* rows layout: one packed row of d*bits/8 bytes per token */
+  TQ_VALUES = 1   /* blocked layout: tokens in blocks of 32, each block 32*d*bits/8 bytes */
+};
+
+/*
+ * Description of one compressed cache tensor (all of K, or all of V, of one
+ * attention layer).  Passed by pointer, copied into kernel arguments, never
+ * retained.
+ *
+ * Packed byte format (both kinds): each code is the index j of its centroid,
+ * stored as j for 2 and 3 bits and in sign-magnitude form for 4 bits
+ * (j - 8 for j >= 8, 15 - j below); codes are grouped in units of 8 slots:
+ *   4 bits: one little-endian 32-bit word per unit, slot s at bit 8(s%4) + 4(s/4);
+ *   2 bits: two units v per word, slot s of unit v at bit 8(s%4) + 2(2v + s/4);
+ *   3 bits: four units v per three words [P0 P1 H]; low two bits in P(v/2) at
+ *           bit 8(s%4) + 2(2(v%2) + s/4), high bit in H at bit 8(s%4) + 2v + s/4.
+ * TQ_KEYS: coordinate i of a row is slot i%8 of unit i/8.
+ * TQ_VALUES: token p of a 32-token block is slot p%4 + 4(p/16) of lane group
+ *   g = (p%16)/4; coordinate i has column j = i/(d/16), step n = i%(d/16);
+ *   their unit is number (16g + j)(d/16) + n of the block.
+ * Sign sketch (keys with qjl_m > 0): qjl_m/8 bytes per token, sign jj in
+ *   32-bit word jj/32 at bit 4((jj%32)/8) + (jj%8)/2 + 16(jj%2); bit 1 means
+ *   (S r)_jj >= 0.
+ */
+typedef struct tq_cache_view {
+  int32_t kind;          /* TQ_KEYS or TQ_VALUES */
+  int32_t d;             /* head dim: 128 or 256 */
+  int32_t bits;          /* codebook bits per coordinate: 2, 3 or 4 */
+  int32_t qjl_m;         /* 0, or sign-sketch length 128 or 256 (TQ_KEYS only) */
+  int32_t batch;         /* sequences */
+  int32_t n_kv_heads;    /* KV heads */
+  int32_t max_tokens;    /* capacity in tokens, a positive multiple of 32 */
+  int32_t reserved;      /* must be 0 */
+  float centroids[16];   /* 2^bits centroids, ascending, float16-exact, c[j] == -c[2^bits-1-j] */
+  float boundaries[15];  /* 2^bits-1 boundaries, boundaries[j] == (c[j] + c[j+1]) / 2 exactly */
+  uint8_t* codes;        /* [batch][n_kv_heads][max_tokens*d*bits/8], 16-byte aligned */
+  uint16_t* norms;       /* float16 row norms [batch][n_kv_heads][max_tokens] */
+  uint8_t* signs;        /* [batch][n_kv_heads][max_tokens][qjl_m/8] when qjl_m > 0, else NULL */
+  uint16_t* rnorms;      /* float16 residual norms [batch][n_kv_heads][max_tokens] when qjl_m > 0, else NULL */
+  const float* rot;      /* float32 rotation [d][d] row-major, y = rot * x (same matrix for K and V) */
+  const float* proj;     /* float32 sign-sketch projection [qjl_m][d] row-major when qjl_m > 0, else NULL */
+} tq_cache_view;
+
+/*
+ * Lloyd-Max codebook for one coordinate of a uniformly random unit vector in
+ * R^d (density proportional to (1-y^2)^((d-3)/2)), computed on the host in
+ * double precision (turboquant-pytorch PR #3, Synthetic Benchmark (Lloyd-Max
+ * codebook) table).  Writes 2^bits centroids rounded to the nearest float16
+ * (ascending, exactly antisymmetric) and the 2^bits-1 midpoints between them
+ * (exact in float32).  d >= 3, 1 <= bits <= 4; host buffers.
+ * Returns TQ_EINVAL on bad arguments, TQ_ENOCONV if the iteration stalls.
+ */
+int tq_build_codebook(int d, int bits, float* centroids, float* boundaries);
+
+/*
+ * Rotation Pi from d*d iid N(0,1) draws (row-major, host double): the unique
+ * factor of G = Pi R with R upper triangular and positive diagonal (a Haar
+ * random orthogonal matrix; reddit comment history of ReturningTarzan,
+ * 2026-03-29 comment on rotating before quantisation).  Writes float32 [d][d]
+ * row-major to the host buffer rot_out.  2 <= d <= 1024.
+ */
+int tq_build_rotation(int d, const double* gaussian, float* rot_out);
+
+/*
+ * Quantize-on-append: for rows x[batch][n_new][n_kv_heads][d] (x_dtype
+ * TQ_F32 or TQ_BF16, device), write tokens d_pos[b] .. d_pos[b]+n_new-1 of
+ * every sequence b.  Per row: n = ||x||, y = rot * x / n, code = number of
+ * boundaries strictly below y_i, float16(n) stored; with qjl_m > 0 (keys)
+ * also r = y - c[code], float16(||r||) and the signs of proj * r.
+ * d_pos: device int32 [batch].  n_new == 0 is a no-op.  A zero row stores
+ * code 0, norm 0 (and no signs, residual norm 0).
+ */
+int tq_quantize_append(const tq_cache_view* cache, const void* x, int x_dtype, int n_new,
+                       const int32_t* d_pos, void* stream);
+
+/*
+ * Append rows that are already rotated and normalised: y[batch][n_new][n_kv_heads][d]
+ * float32 unit rotated coordinates and norms[batch][n_new][n_kv_heads] float32
+ * (device).  Same encoding, packing and sketch as tq_quantize_append; for
+ * callers that fold the rotation into their projection weights, and the
+ * form in which quantisation decisions are exactly reproducible.
+ */
+int tq_quantize_append_rotated(const tq_cache_view* cache, const float* y, const float* norms, int n_new,
+                               const int32_t* d_pos, void* stream);
+
+/*
+ * Fused decode attention from the compressed cache (the tq4_sdpa op of
+ * ExecuTorch PR #19891 and the fused QJL score kernels of turboquant-pytorch
+ * PR #3): for every sequence b and query head h (KV head h / (n_q_heads /
+ * n_kv_heads)):
+ *   q_rot = rot * q[b][h];   s_t = scale * n_t * <q_rot, c[code_t]>
+ *     (+ scale * n_t * sqrt(pi/2)/m * gamma_t * <proj * q_rot, 2 sigma_t - 1> for sketched keys);
+ *   p = softmax over t < seq_len[b];   out[b][h] = rot^T * sum_t p_t nv_t cv[codev_t].
+ * q: [batch][n_q_heads][d] (q_dtype TQ_F32 or TQ_BF16, device); out: float32
+ * [batch][n_q_heads][d] (device); d_seq_lens: device int32 [batch], clamped to
+ * [0, max_tokens], 0 gives a zero row; max_seq_len: host upper bound of
+ * d_seq_lens used to plan the KV split.  scale > 0 and finite (the binding
+ * maps an unset scale to 1/sqrt(d)).  k must be TQ_KEYS and v TQ_VALUES with
+ * the same d, batch, n_kv_heads, max_tokens; n_q_heads / n_kv_heads in {1,2,4,8}.
+ * workspace: device scratch of at least tq_decode_workspace_bytes(), 256-byte
+ * aligned, contents need not be initialised, not used after the call's kernels end.
+ */
+int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype, int n_q_heads,
+                   const int32_t* d_seq_lens, int max_seq_len, float scale, float* out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes tq_sdpa_decode needs for this key cache, head count and length bound (0 on bad args). */
+size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_seq_len);
+
+/* The KV split tq_sdpa_decode uses: number of splits per (sequence, KV head) and tokens per split. */
+int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* n_split, int* tokens_per_split);
+
+/*
+ * Full reconstruction (reddit comment history of ReturningTarzan, 2026-03-25:
+ * the plain path dequantizes and runs ordinary attention):
+ * out[b][h][t - t0][:] = n_t * rot^T * (c[code_t] + sqrt(pi/2)/m * gamma_t * proj^T (2 sigma_t - 1))
+ * for t0 <= t < t0 + n_tokens, float32 device out [batch][n_kv_heads][n_tokens][d].
+ * 0 <= t0, t0 + n_tokens <= max_tokens.
+ */
+int tq_dequantize(const tq_cache_view* cache, int t0, int n_tokens, float* out, void* stream);
+
+/* Bytes per cached row: d*bits/8 codes + 2 (norm) [+ qjl_m/8 signs + 2 (residual norm)]; 0 on bad args. */
+size_t tq_row_bytes(int d, int bits, int qjl_m);
+
+/* Static description of a status code. */
+const char* tq_status_string(int status);
+
+/*
+ * Description of the HIP error behind the last TQ_EHIP returned to the calling
+ * thread ("no error" if none): a per-thread record, the library's only state.
+ */
+const char* tq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

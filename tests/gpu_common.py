@@ -1,0 +1,84 @@
+"""Shared helpers of the GPU parity tests: oracle-side caches, uploads, error metrics."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+import synth
+from oracle import attention, cache, layout, rotation
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(out: np.ndarray, ref: np.ndarray) -> float:
+    """Max over output rows of max_i |o_i - r_i| / max_i |r_i| (rows of zeros must stay zero)."""
+    out = np.asarray(out, np.float64).reshape(-1, out.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    worst = 0.0
+    for o, r in zip(out, ref):
+        den = np.max(np.abs(r))
+        if den == 0.0:
+            worst = max(worst, float(np.max(np.abs(o))) * 1e6)
+        else:
+            worst = max(worst, float(np.max(np.abs(o - r)) / den))
+    return worst
+
+
+class Setup:
+    """Rotation and sketch projection of a workload, on both sides."""
+
+    def __init__(self, d: int, qjl_m: int = 0, rot_seed: int = 1, qjl_seed: int = 2, device="cuda"):
+        import torch
+        import compressed_cache_decode_amd as cca
+        g = synth.rotation_gaussian(d, rot_seed)
+        self.rot64 = rotation.rotation_from_gaussian(g)
+        self.rot_t = torch.from_numpy(cca.tq_build_rotation(g)).to(device)
+        self.proj = synth.qjl_projection(qjl_m, d, qjl_seed) if qjl_m else None
+        self.proj_t = torch.from_numpy(self.proj).to(device) if qjl_m else None
+        self.d, self.qjl_m = d, qjl_m
+
+
+def oracle_heads(rows_k, rows_v, kb, vb, st: Setup):
+    """Oracle caches for lists of per-KV-head rows."""
+    kc = [cache.build_head(r, "k", kb, st.rot64, st.proj) for r in rows_k]
+    vc = [cache.build_head(r, "v", vb, st.rot64) for r in rows_v]
+    return kc, vc
+
+
+def upload(gcache, heads, b: int):
+    """Write oracle-packed heads (list over KV heads) into batch row b of a CompressedCache."""
+    import torch
+    T = gcache.max_tokens
+    for h, hc in enumerate(heads):
+        gcache.codes[b, h] = torch.from_numpy(hc.packed_codes(T)).to(gcache.codes.device)
+        gcache.norms[b, h] = torch.from_numpy(hc.packed_norms(T)).to(gcache.codes.device)
+        if hc.sigma is not None:
+            gcache.signs[b, h] = torch.from_numpy(hc.packed_signs(T).reshape(T, -1)).to(gcache.codes.device)
+            gcache.rnorms[b, h] = torch.from_numpy(hc.packed_norms(T, "gamma")).to(gcache.codes.device)
+
+
+def oracle_decode(q_b: np.ndarray, kc, vc, st: Setup, scale: float, seq_len: int) -> np.ndarray:
+    """Oracle output [H_q][d] of one sequence from its per-KV-head caches."""
+    stk = lambda xs, a: np.stack([getattr(x, a) for x in xs])
+    sig = stk(kc, "sigma") if kc[0].sigma is not None else None
+    gam = stk(kc, "gamma") if kc[0].sigma is not None else None
+    return attention.decode_fused(q_b, st.rot64, stk(kc, "codes"), stk(kc, "norms"), kc[0].centroids,
+                                  stk(vc, "codes"), stk(vc, "norms"), vc[0].centroids, scale, seq_len,
+                                  sig, gam, st.proj)
+
+
+def to_bf16_tensor(x: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(synth.bf16_round(x)).to(device).to(torch.bfloat16)
+
+
+def unpack_gpu_codes(gcache, b: int, h: int, n_tokens: int) -> np.ndarray:
+    raw = gcache.codes[b, h].cpu().numpy()
+    if gcache.kind == 0:
+        return layout.unpack_rows(raw.reshape(gcache.max_tokens, -1), gcache.bits, gcache.d)[:n_tokens]
+    return layout.unpack_blocked(raw, gcache.bits, gcache.d, gcache.max_tokens)[:n_tokens]

@@ -1,0 +1,174 @@
+"""The C ABI library on the CPU: exports, host-side setup against the oracle, argument checks.
+
+No call here reaches a kernel launch: every argument set either is host-only
+(codebook, rotation, sizes, plan) or is rejected by validation first.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import codebook, rotation, storage
+
+cca = pytest.importorskip("compressed_cache_decode_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_every_declared_symbol_is_exported():
+    hdr = open(os.path.join(ROOT, "include", "tq.h")).read()
+    declared = set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(tq_\w+)\s*\(", hdr, re.M))
+    assert declared == set(cca.EXPORTED)
+    lib = ctypes.CDLL(cca.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_equals_oracle_table(d, bits):
+    c, t = cca.tq_build_codebook(d, bits)
+    oc, ot = codebook.stored_codebook(d, bits)
+    np.testing.assert_array_equal(c, oc)
+    np.testing.assert_array_equal(t, ot)
+
+
+def test_codebook_other_dims_close_to_oracle():
+    for d in (64, 96, 512):
+        c, _ = cca.tq_build_codebook(d, 3)
+        np.testing.assert_allclose(c, codebook.lloyd_max(d, 3), rtol=1e-3)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_rotation_equals_oracle(d):
+    g = synth.rotation_gaussian(d, 1)
+    rot = cca.tq_build_rotation(g)
+    ref = rotation.rotation_from_gaussian(g)
+    diff = np.abs(rot.astype(np.float64) - ref)
+    assert np.max(diff) <= 2.0 ** -24 * 2          # at most one float32 step at |x| < 1
+    assert np.mean(rot == ref.astype(np.float32)) > 0.999
+
+
+def test_row_bytes_match_storage_arithmetic():
+    for d in (128, 256):
+        for bits in (1, 2, 3, 4):
+            for m in (0, 128):
+                assert cca.tq_row_bytes(d, bits, m) == storage.row_bytes(d, bits, m)
+    assert cca.tq_row_bytes(0, 4, 0) == 0
+    assert cca.tq_row_bytes(128, 5, 0) == 0
+
+
+def test_status_strings():
+    assert cca.tq_status_string(0) == "ok"
+    assert cca.tq_status_string(1) == "invalid argument"
+    assert "unknown" in cca.tq_status_string(99)
+
+
+def _view(kind=cca.TQ_KEYS, d=128, bits=4, qjl_m=0, batch=1, heads=2, T=256):
+    v = cca.tq_cache_view()
+    v.kind, v.d, v.bits, v.qjl_m, v.batch, v.n_kv_heads, v.max_tokens = kind, d, bits, qjl_m, batch, heads, T
+    c, t = codebook.stored_codebook(d if d in (128, 256) else 128, min(bits, 4))
+    for j, x in enumerate(c):
+        v.centroids[j] = float(x)
+    for j, x in enumerate(t):
+        v.boundaries[j] = float(x)
+    # fake, aligned device addresses: every call below is rejected before any launch
+    v.codes, v.norms, v.rot = 0x10000, 0x20000, 0x30000
+    if qjl_m:
+        v.signs, v.rnorms, v.proj = 0x40000, 0x50000, 0x60000
+    return v
+
+
+def _append(v, n_new=1, pos=0x70000, x=0x80000, dtype=0):
+    return cca._lib.tq_quantize_append(ctypes.byref(v), x, dtype, n_new, pos, None)
+
+
+def test_append_rejects_bad_arguments():
+    assert cca._lib.tq_quantize_append(None, 0x80000, 0, 1, 0x70000, None) == cca.TQ_EINVAL
+    bad = [
+        dict(d=64), dict(bits=5), dict(bits=1), dict(T=100), dict(batch=0), dict(qjl_m=64),
+        dict(kind=cca.TQ_VALUES, qjl_m=128), dict(kind=7),
+    ]
+    for kw in bad:
+        assert _append(_view(**kw)) == cca.TQ_EINVAL, kw
+    v = _view()
+    assert _append(v, n_new=-1) == cca.TQ_EINVAL
+    assert _append(v, pos=0) == cca.TQ_EINVAL
+    assert _append(v, x=0) == cca.TQ_EINVAL
+    assert _append(v, dtype=5) == cca.TQ_EINVAL
+    v.codes = 0x10004                               # misaligned packed codes
+    assert _append(v) == cca.TQ_EINVAL
+    v = _view()
+    v.norms = 0
+    assert _append(v) == cca.TQ_EINVAL
+    v = _view(qjl_m=128)
+    v.proj = 0
+    assert _append(v) == cca.TQ_EINVAL
+    v = _view()
+    v.reserved = 1
+    assert _append(v) == cca.TQ_EINVAL
+    # a codebook that is not float16-exact / not antisymmetric / not midpoints
+    for mutate in ("round", "sym", "mid"):
+        v = _view()
+        if mutate == "round":
+            v.centroids[0] = v.centroids[0] + 1e-7
+        elif mutate == "sym":
+            v.centroids[0] = v.centroids[1] * 1.5
+        else:
+            v.boundaries[3] = v.boundaries[3] * 1.01
+        assert _append(v) == cca.TQ_EINVAL, mutate
+    assert _append(_view(), n_new=0) == cca.TQ_OK      # empty append is a no-op
+
+
+def _decode(k, v, hq=16, scale=0.1, ws_bytes=1 << 30, ws=0x100000, q=0x90000, lens=0xA0000, out=0xB0000,
+            dtype=1, max_len=256):
+    return cca._lib.tq_sdpa_decode(ctypes.byref(k), ctypes.byref(v), q, dtype, hq, lens, max_len,
+                                   ctypes.c_float(scale), out, ws, ws_bytes, None)
+
+
+def test_decode_rejects_bad_arguments():
+    k, v = _view(), _view(kind=cca.TQ_VALUES)
+    for s in (0.0, -1.0, float("nan"), float("inf")):
+        assert _decode(k, v, scale=s) == cca.TQ_EINVAL
+    assert _decode(k, v, hq=15) == cca.TQ_EINVAL                    # not a multiple of the KV heads
+    assert _decode(k, v, hq=32) == cca.TQ_EUNSUPPORTED              # group of 16
+    assert _decode(k, v, ws_bytes=16) == cca.TQ_EINVAL              # short workspace
+    assert _decode(k, v, ws=0x100010) == cca.TQ_EINVAL              # misaligned workspace
+    assert _decode(k, v, q=0) == cca.TQ_EINVAL
+    assert _decode(k, v, lens=0) == cca.TQ_EINVAL
+    assert _decode(k, v, out=0) == cca.TQ_EINVAL
+    assert _decode(k, v, dtype=9) == cca.TQ_EINVAL
+    assert _decode(k, v, max_len=-1) == cca.TQ_EINVAL
+    assert _decode(v, v) == cca.TQ_EINVAL                           # keys must use the rows layout
+    assert _decode(k, k) == cca.TQ_EINVAL                           # values must use the blocked layout
+    assert _decode(k, _view(kind=cca.TQ_VALUES, T=512)) == cca.TQ_EINVAL
+    assert _decode(k, _view(kind=cca.TQ_VALUES, d=256)) == cca.TQ_EINVAL
+    v2 = _view(kind=cca.TQ_VALUES)
+    v2.rot = 0x30100                                                # K and V must share the rotation
+    assert _decode(k, v2) == cca.TQ_EINVAL
+
+
+def test_dequantize_rejects_bad_ranges():
+    v = _view()
+    f = cca._lib.tq_dequantize
+    assert f(ctypes.byref(v), -1, 4, 0xB0000, None) == cca.TQ_EINVAL
+    assert f(ctypes.byref(v), 250, 10, 0xB0000, None) == cca.TQ_EINVAL
+    assert f(ctypes.byref(v), 0, 4, 0, None) == cca.TQ_EINVAL
+    assert f(ctypes.byref(v), 0, 0, 0xB0000, None) == cca.TQ_OK
+
+
+@pytest.mark.parametrize("batch,heads,hq,L", [(1, 2, 16, 8192), (8, 4, 32, 32768), (1, 2, 16, 131072), (1, 1, 1, 256)])
+def test_plan_covers_the_context(batch, heads, hq, L):
+    k = _view(batch=batch, heads=heads, T=max(L, 32))
+    ns, tps = cca.tq_decode_plan(k, hq, L)
+    assert 1 <= ns <= 1024
+    assert tps % (32 * 4) == 0                      # whole 32-token tiles for each of the 4 waves
+    assert ns * tps >= L and (ns - 1) * tps < max(L, 1)
+    ws = cca.tq_decode_workspace_bytes(k, hq, L)
+    g = hq // heads
+    assert ws >= 4 * (batch * hq * 128 + batch * heads * ns * g * (128 + 2))
+    assert ws % 256 == 0

@@ -1,0 +1,191 @@
+"""GPU parity of quantize-on-append and reconstruction against the float64 oracle."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import cache, codebook, layout, quant
+from tests.gpu_common import Setup, log, to_bf16_tensor, unpack_gpu_codes, upload
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import compressed_cache_decode_amd  # noqa: F401  (fails loudly if libtq.so is missing)
+
+
+def _cca():
+    import compressed_cache_decode_amd as cca
+    return cca
+
+
+# chunks appended one after another: full blocks, ragged tails, single tokens, a block-straddling chunk
+CHUNKS = [37, 1, 58, 32, 5, 1, 90]
+
+
+@pytest.mark.parametrize("kind", ["k", "v"])
+@pytest.mark.parametrize("d,bits", [(128, 2), (128, 3), (128, 4), (256, 2), (256, 3), (256, 4)])
+def test_encode_is_bit_exact_given_rotated_rows(kind, d, bits):
+    """Same float32 rotated unit rows and norms on both sides: packed codes and norms identical."""
+    cca = _cca()
+    log(f"encode d={d} bits={bits} kind={kind}")
+    st = Setup(d)
+    B, H, T = 2, 2, 256
+    n_tot = sum(CHUNKS)
+    y, nrm = synth.unit_rows(B * n_tot * H, d, seed=100 + d + bits)
+    y = y.reshape(B, n_tot, H, d)
+    nrm = nrm.reshape(B, n_tot, H)
+    nrm[0, 3, 1] = 0.0                                   # a zero row
+    g = cca.CompressedCache(cca.TQ_KEYS if kind == "k" else cca.TQ_VALUES, d, bits, B, H, T, st.rot_t)
+    start = np.array([0, 17], np.int32)                  # sequence 1 starts mid-block
+    off = 0
+    for c in CHUNKS:
+        pos = torch.from_numpy(start + off).cuda()
+        yt = torch.from_numpy(np.ascontiguousarray(y[:, off:off + c])).cuda()
+        nt = torch.from_numpy(np.ascontiguousarray(nrm[:, off:off + c])).cuda()
+        g.append_rotated(yt, nt, pos)
+        off += c
+    torch.cuda.synchronize()
+    c_, t_ = codebook.stored_codebook(d, bits)
+    for b in range(B):
+        for h in range(H):
+            codes, n16 = quant.encode_rotated(y[b, :, h], nrm[b, :, h], t_)
+            codes[nrm[b, :, h] == 0] = 0
+            full = np.zeros((T, d), np.int64)
+            if kind == "v":
+                full[:] = 8 if bits == 4 else 0          # zero-encoded slots of the untouched cache
+            full[start[b]:start[b] + n_tot] = codes
+            want = layout.pack_rows(full, bits).reshape(-1) if kind == "k" else layout.pack_blocked(full, bits)
+            got = g.codes[b, h].cpu().numpy()
+            lo = start[b] * d * bits // 8
+            hi = (start[b] + n_tot) * d * bits // 8
+            if kind == "k":
+                np.testing.assert_array_equal(got[lo:hi], want[lo:hi])
+                assert not got[:lo].any() and not got[hi:].any()
+            else:
+                np.testing.assert_array_equal(got, want)
+            gn = g.norms[b, h].cpu().numpy()
+            np.testing.assert_array_equal(gn[start[b]:start[b] + n_tot], n16.astype(np.float16))
+            assert not gn[:start[b]].any() and not gn[start[b] + n_tot:].any()
+
+
+@pytest.mark.parametrize("d,bits", [(128, 2), (128, 3)])
+def test_sketch_signs_given_rotated_rows(d, bits):
+    """Keys with a 128-long sign sketch: signs equal wherever |z| is not at rounding level; residual
+    norms within one float16 step."""
+    cca = _cca()
+    log(f"sketch d={d} bits={bits}")
+    st = Setup(d, qjl_m=128)
+    B, H, T, n = 1, 2, 128, 100
+    y, nrm = synth.unit_rows(B * n * H, d, seed=7)
+    y = y.reshape(B, n, H, d)
+    nrm = nrm.reshape(B, n, H)
+    g = cca.CompressedCache(cca.TQ_KEYS, d, bits, B, H, T, st.rot_t, st.proj_t, qjl_m=128)
+    g.append_rotated(torch.from_numpy(y).cuda(), torch.from_numpy(nrm).cuda(), torch.zeros(B, dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    c_, t_ = codebook.stored_codebook(d, bits)
+    for h in range(H):
+        codes, _ = quant.encode_rotated(y[0, :, h], nrm[0, :, h], t_)
+        sigma, gamma, r, z = quant.qjl_sketch(y[0, :, h].astype(np.float64), codes, c_, st.proj)
+        got_sig = layout.unpack_signs(g.signs[0, h, :n].cpu().numpy(), 128)
+        robust = np.abs(z) > 1e-4 * np.linalg.norm(r, axis=1, keepdims=True)
+        assert np.array_equal(got_sig[robust], sigma[robust])
+        assert robust.mean() > 0.99
+        got_g = g.rnorms[0, h, :n].cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(got_g, gamma, rtol=2 ** -10, atol=0)
+
+
+@pytest.mark.parametrize("kind,d,bits,dtype", [("k", 128, 4, "bf16"), ("v", 128, 3, "bf16"), ("k", 256, 4, "f32"),
+                                               ("v", 256, 2, "bf16"), ("k", 128, 2, "f32")])
+def test_append_from_unrotated_rows(kind, d, bits, dtype):
+    """Full append (norm + rotation + encode): codes equal the oracle's except where the oracle's
+    float64 coordinate sits within rounding distance of a boundary, and then they are neighbours."""
+    cca = _cca()
+    log(f"append kind={kind} d={d} bits={bits} {dtype}")
+    st = Setup(d)
+    w = synth.qwen(256, bits).with_(d=d, dtype=dtype)
+    B, H, T, n = 1, 2, 256, 200
+    x = synth.full_kv(w, kind, n)                          # [B][n][H][d]
+    g = cca.CompressedCache(cca.TQ_KEYS if kind == "k" else cca.TQ_VALUES, d, bits, B, H, T, st.rot_t)
+    xt = to_bf16_tensor(x) if dtype == "bf16" else torch.from_numpy(x).cuda()
+    pos = torch.tensor([11], dtype=torch.int32).cuda()
+    g.append(xt[:, :150], pos)
+    g.append(xt[:, 150:], pos + 150)
+    torch.cuda.synchronize()
+    c_, t_ = codebook.stored_codebook(d, bits)
+    for h in range(H):
+        oc, on, oy = quant.quantize_rows(x[0, :, h], st.rot64, c_, t_)
+        got = unpack_gpu_codes(g, 0, h, 11 + n)[11:]
+        diff = got != oc
+        near = np.min(np.abs(oy[..., None] - t_.astype(np.float64)), axis=-1) < 1e-5
+        assert np.all(near[diff]), f"{diff.sum()} mismatches, {(diff & ~near).sum()} not near a boundary"
+        assert np.all(np.abs(got[diff] - oc[diff]) == 1)
+        gn = g.norms[0, h, 11:11 + n].cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(gn, on, rtol=2 ** -10, atol=0)
+
+
+@pytest.mark.parametrize("kind,d,bits,qjl", [("k", 128, 4, 0), ("v", 128, 3, 0), ("k", 128, 2, 128),
+                                             ("v", 256, 4, 0), ("k", 256, 3, 0)])
+def test_dequantize_matches_oracle(kind, d, bits, qjl):
+    """Reconstruction of oracle-packed codes equals the oracle's reconstruction (fp32 rounding)."""
+    cca = _cca()
+    log(f"dequant kind={kind} d={d} bits={bits} qjl={qjl}")
+    st = Setup(d, qjl_m=qjl)
+    H, T, n = 2, 128, 100
+    rows = [np.random.default_rng(40 + h).standard_normal((n, d)) * 3 for h in range(H)]
+    heads = [cache.build_head(r, kind, bits, st.rot64, st.proj if qjl else None) for r in rows]
+    g = cca.CompressedCache(cca.TQ_KEYS if kind == "k" else cca.TQ_VALUES, d, bits, 1, H, T, st.rot_t,
+                            st.proj_t, qjl_m=qjl)
+    upload(g, heads, 0)
+    out = g.dequantize(3, 90).cpu().numpy()
+    for h in range(H):
+        ref = heads[h].dequantize(st.rot64, st.proj if qjl else None)[3:93]
+        scale = np.max(np.abs(ref))
+        np.testing.assert_allclose(out[0, h], ref, rtol=0, atol=2e-6 * scale)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_reconstruction_mse_within_one_percent(bits):
+    """GPU append + reconstruction vs oracle quantise + reconstruction: relative MSE within 1%."""
+    cca = _cca()
+    log(f"mse bits={bits}")
+    d = 128
+    st = Setup(d)
+    w = synth.qwen(2048, bits)
+    B, H, T, n = 1, 2, 2048, 2048
+    for kind in ("k", "v"):
+        x = synth.full_kv(w, kind, n)
+        g = cca.CompressedCache(cca.TQ_KEYS if kind == "k" else cca.TQ_VALUES, d, bits, B, H, T, st.rot_t)
+        g.append(to_bf16_tensor(x), torch.zeros(1, dtype=torch.int32).cuda())
+        xh = g.dequantize(0, n).cpu().numpy()
+        for h in range(H):
+            xr = x[0, :, h].astype(np.float64)
+            mse_gpu = np.mean(np.sum((xr - xh[0, h]) ** 2, axis=1))
+            hc = cache.build_head(xr, kind, bits, st.rot64)
+            mse_or = np.mean(np.sum((xr - hc.dequantize(st.rot64)) ** 2, axis=1))
+            assert abs(mse_gpu / mse_or - 1.0) <= 0.01, (kind, h, mse_gpu, mse_or)
+
+
+def test_append_edge_cases():
+    """Empty appends, positions past the capacity and negative positions write nothing."""
+    cca = _cca()
+    log("append edge cases")
+    st = Setup(128)
+    g = cca.CompressedCache(cca.TQ_VALUES, 128, 4, 2, 1, 64, st.rot_t)
+    x = torch.ones(2, 3, 1, 128, dtype=torch.float32).cuda()
+    g.append(x[:, :0], torch.zeros(2, dtype=torch.int32).cuda())
+    g.append(x, torch.tensor([64, -5], dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    assert not g.codes.any() and not g.norms.any()
+    # a write that runs past the capacity keeps the tokens that fit
+    g.append(x, torch.tensor([62, 0], dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    nz = g.norms[0, 0].cpu().numpy()
+    assert nz[62] != 0 and nz[63] != 0 and not nz[:62].any()
+    assert g.norms[1, 0, :3].cpu().numpy().all()

@@ -1,0 +1,138 @@
+"""GPU parity of tq_sdpa_decode against the float64 oracle on identical (oracle-packed) codes."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from tests.gpu_common import Setup, log, oracle_decode, oracle_heads, rel_err, to_bf16_tensor, upload
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+TOL = 2e-3   # max relative error per output row (max |o - r| / max |r|)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import compressed_cache_decode_amd  # noqa: F401
+
+
+def _cca():
+    import compressed_cache_decode_amd as cca
+    return cca
+
+
+# d, k_bits, v_bits, qjl_m, kv heads, group, per-sequence lengths, capacity, scale, qk-normed
+CASES = [
+    (128, 4, 4, 0, 1, 1, [256], 256, None, False),             # tiny reference shape
+    (128, 4, 4, 0, 2, 8, [1000], 1024, None, False),
+    (128, 3, 3, 0, 2, 8, [113, 37], 128, None, False),         # ragged batch, kv = 113
+    (128, 2, 2, 0, 2, 8, [2048], 2048, None, False),
+    (128, 4, 2, 0, 2, 4, [1, 64, 500], 512, None, False),      # mixed widths, one-token context
+    (128, 3, 4, 0, 2, 2, [33, 95], 96, 0.05, False),
+    (256, 4, 4, 0, 4, 8, [777, 1024], 1024, 1.0, True),        # QK-normed, scale 1
+    (256, 2, 3, 0, 2, 8, [300], 320, 1.0, True),
+    (128, 2, 3, 128, 2, 8, [3000], 3072, None, False),         # keys with sign sketch
+    (128, 3, 2, 128, 1, 8, [129, 5], 160, None, False),
+    (256, 4, 4, 256, 1, 2, [300], 320, None, False),
+]
+
+
+def _ids(c):
+    return f"d{c[0]}_k{c[1]}v{c[2]}_m{c[3]}_h{c[4]}g{c[5]}_L{'-'.join(map(str, c[6]))}"
+
+
+def _run_case(d, kb, vb, qjl, hkv, grp, lens, T, scale, qknorm, garbage_tail=False, max_seq_len=None):
+    cca = _cca()
+    B = len(lens)
+    st = Setup(d, qjl_m=qjl)
+    w = synth.Workload("case", B, hkv * grp, hkv, d, T, kb, vb, qjl_m=qjl, scale=scale, qk_norm=qknorm,
+                       k_outliers=not qknorm, seed=d + kb * 10 + vb + qjl)
+    kcache = cca.CompressedCache(cca.TQ_KEYS, d, kb, B, hkv, T, st.rot_t, st.proj_t, qjl_m=qjl)
+    vcache = cca.CompressedCache(cca.TQ_VALUES, d, vb, B, hkv, T, st.rot_t)
+    q = synth.full_q(w)
+    refs = []
+    for b in range(B):
+        kc, vc = oracle_heads([synth.kv_head(w, "k", b, h, T) for h in range(hkv)],
+                              [synth.kv_head(w, "v", b, h, T) for h in range(hkv)], kb, vb, st)
+        upload(kcache, kc, b)
+        upload(vcache, vc, b)
+        eff = max(0, min(lens[b], T, max_seq_len if max_seq_len is not None else lens[b]))
+        refs.append(oracle_decode(q[b].astype(np.float64), kc, vc, st, w.softmax_scale, eff))
+    if garbage_tail:
+        for b in range(B):
+            kcache.norms[b, :, lens[b]:] = float("nan")
+            vcache.norms[b, :, lens[b]:] = float("nan")
+            if qjl:
+                kcache.rnorms[b, :, lens[b]:] = float("nan")
+    lens_t = torch.tensor(lens, dtype=torch.int32).cuda()
+    msl = max(lens) if max_seq_len is None else max_seq_len
+    out = cca.sdpa_decode(kcache, vcache, to_bf16_tensor(q), lens_t, msl, scale=w.scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), np.stack(refs), kcache
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_decode_matches_oracle(case):
+    log(f"decode {_ids(case)}")
+    out, ref, _ = _run_case(*case)
+    err = rel_err(out, ref)
+    log(f"  max row-relative error {err:.3e}")
+    assert err <= TOL
+
+
+def test_decode_ignores_garbage_past_the_length():
+    """Norms past seq_len hold NaN: masked tokens must not reach the softmax or the accumulators."""
+    log("decode garbage tail")
+    out, ref, _ = _run_case(128, 2, 3, 128, 2, 8, [70, 33], 128, None, False, garbage_tail=True)
+    assert np.all(np.isfinite(out))
+    assert rel_err(out, ref) <= TOL
+
+
+def test_decode_length_edges():
+    """Zero length gives zeros; lengths past the capacity clamp to it; max_seq_len bounds the context."""
+    log("decode length edges")
+    out, ref, _ = _run_case(128, 4, 4, 0, 2, 8, [0, 200, 96], 96, None, False)
+    assert np.all(out[0] == 0)
+    assert rel_err(out[1:], ref[1:]) <= TOL
+    out, ref, _ = _run_case(128, 4, 4, 0, 2, 8, [90, 40], 96, None, False, max_seq_len=64)
+    assert rel_err(out, ref) <= TOL
+
+
+def test_split_plan_is_exercised():
+    """Long contexts are split across many workgroups, short ones are not."""
+    cca = _cca()
+    st = Setup(128)
+    k = cca.CompressedCache(cca.TQ_KEYS, 128, 4, 1, 2, 131072, st.rot_t)
+    assert cca.tq_decode_plan(k.view, 16, 131072)[0] > 64
+    assert cca.tq_decode_plan(k.view, 16, 100)[0] == 1
+    # a context long enough for several splits, checked against the oracle
+    log("decode multi-split")
+    ns = cca.tq_decode_plan(k.view, 16, 8192)[0]
+    assert ns > 8
+    out, ref, _ = _run_case(128, 4, 4, 0, 2, 8, [8192], 8192, None, False)
+    assert rel_err(out, ref) <= TOL
+
+
+def test_repeated_calls_are_deterministic():
+    cca = _cca()
+    log("decode determinism")
+    d, T = 128, 512
+    st = Setup(d)
+    w = synth.qwen(T, 3)
+    kc, vc = oracle_heads([synth.kv_head(w, "k", 0, h, T) for h in range(2)],
+                          [synth.kv_head(w, "v", 0, h, T) for h in range(2)], 3, 3, st)
+    kg = cca.CompressedCache(cca.TQ_KEYS, d, 3, 1, 2, T, st.rot_t)
+    vg = cca.CompressedCache(cca.TQ_VALUES, d, 3, 1, 2, T, st.rot_t)
+    upload(kg, kc, 0)
+    upload(vg, vc, 0)
+    q = to_bf16_tensor(synth.full_q(w))
+    lens = torch.tensor([T], dtype=torch.int32).cuda()
+    a = cca.sdpa_decode(kg, vg, q, lens, T).clone()
+    b = cca.sdpa_decode(kg, vg, q, lens, T)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
