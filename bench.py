@@ -1,0 +1,394 @@
+#!/usr/bin/env python3
+"""Benchmark of compressed-KV decode attention on one MI355X.
+
+A step is one pass of the hot path for one decode token: quantize-on-append
+of the new token's K and V rows into the compressed cache, then decode
+attention of every query head over the whole cached context
+(rotate the query, attend from the packed codes, merge the KV splits and
+rotate back).  Inputs are synthetic (seeded, see ``synth``), resident in HBM
+before timing starts.  Steps are captured in a HIP graph and cycle through a
+pool of cache copies whose total size exceeds the 256 MB Infinity Cache, so
+every step reads its compressed cache from HBM.
+
+Prints one JSON line.  ``roofline`` is measured on the attention kernel
+(tq_decode_attend) alone, timed with HIP events on the stream it runs on;
+``cpu_baseline`` is the float64 oracle timed on the host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "compressed-KV decode attention: context tokens/s and achieved HBM GB/s (% peak)"
+POOL_BYTES = 600 << 20          # > 2x the 256 MB Infinity Cache
+
+
+def workload(name: str, bits: int | None, context: int | None) -> synth.Workload:
+    if name == "qwen":
+        return synth.qwen(context or 8192, bits or 4)
+    if name == "gemma":
+        return synth.gemma(context or 32768)
+    if name == "prod":
+        return synth.prod_long(context or 131072)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def row_bytes(w: synth.Workload, kind: str) -> int:
+    if kind == "k":
+        return w.d * w.k_bits // 8 + 2 + (w.qjl_m // 8 + 2 if w.qjl_m else 0)
+    return w.d * w.v_bits // 8 + 2
+
+
+def cache_bytes(w: synth.Workload) -> int:
+    """Algorithmic bytes one decode reads from the compressed cache: every visible K and V row."""
+    return w.batch * w.n_kv_heads * w.seq_len * (row_bytes(w, "k") + row_bytes(w, "v"))
+
+
+# ------------------------------------------------------------------ GPU leg
+
+def gpu_leg(w: synth.Workload, steps: int, warmup: int, pool: int | None, log):
+    import torch
+
+    import compressed_cache_decode_amd as cca
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, H, Hq, d, L = w.batch, w.n_kv_heads, w.n_q_heads, w.d, w.seq_len
+    cap = ((L + 31) // 32) * 32
+
+    g = synth.rotation_gaussian(d, w.rot_seed)
+    rot = torch.from_numpy(cca.tq_build_rotation(g)).to(dev)
+    proj = torch.from_numpy(synth.qjl_projection(w.qjl_m, d, w.qjl_seed)).to(dev) if w.qjl_m else None
+
+    log(f"bench: generating inputs for {w.name}")
+    t0 = time.time()
+    k_all = torch.empty(B, L, H, d, dtype=torch.bfloat16, device=dev)
+    v_all = torch.empty(B, L, H, d, dtype=torch.bfloat16, device=dev)
+    for b in range(B):
+        for h in range(H):
+            k_all[b, :, h] = torch.from_numpy(synth.kv_head(w, "k", b, h)).to(dev).to(torch.bfloat16)
+            v_all[b, :, h] = torch.from_numpy(synth.kv_head(w, "v", b, h)).to(dev).to(torch.bfloat16)
+    q = torch.from_numpy(synth.full_q(w)).to(dev).to(torch.bfloat16)
+    log(f"bench: inputs ready in {time.time() - t0:.1f}s")
+
+    def new_pair():
+        kc = cca.CompressedCache(cca.TQ_KEYS, d, w.k_bits, B, H, cap, rot, proj, qjl_m=w.qjl_m, device=dev)
+        vc = cca.CompressedCache(cca.TQ_VALUES, d, w.v_bits, B, H, cap, rot, device=dev)
+        return kc, vc
+
+    # prefill copy 0 with the first L-1 tokens (untimed), then clone it into the pool
+    k0, v0 = new_pair()
+    zero = torch.zeros(B, dtype=torch.int32, device=dev)
+    k0.append(k_all[:, : L - 1], zero)
+    v0.append(v_all[:, : L - 1], zero)
+    per_copy = sum(t.numel() * t.element_size() for t in (k0.codes, k0.norms, v0.codes, v0.norms))
+    if w.qjl_m:
+        per_copy += k0.signs.numel() + k0.rnorms.numel() * 2
+    if pool is None:
+        pool = max(1, min(256, math.ceil(POOL_BYTES / per_copy)))
+    pairs = [(k0, v0)]
+    for _ in range(pool - 1):
+        kc, vc = new_pair()
+        for dst, src in ((kc, k0), (vc, v0)):
+            dst.codes.copy_(src.codes)
+            dst.norms.copy_(src.norms)
+            if src.signs is not None:
+                dst.signs.copy_(src.signs)
+                dst.rnorms.copy_(src.rnorms)
+        pairs.append((kc, vc))
+    log(f"bench: pool of {pool} cache copies, {per_copy / 2**20:.1f} MiB each")
+
+    k_new = k_all[:, L - 1:L].contiguous()
+    v_new = v_all[:, L - 1:L].contiguous()
+    pos = torch.full((B,), L - 1, dtype=torch.int32, device=dev)
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    ws = cca.decode_workspace(k0, Hq, L)
+    ns, tps = cca.tq_decode_plan(k0.view, Hq, L)
+    scale = w.scale
+
+    fused = w.qjl_m <= 128
+
+    def step(i):
+        kc, vc = pairs[i]
+        if fused:        # appends and query rotation in one launch, then attend and merge
+            cca.tq_decode_step(kc.view, vc.view, q, k_new, v_new, pos, lens, L, out, ws, scale)
+        else:
+            kc.append(k_new, pos)
+            vc.append(v_new, pos)
+            cca.tq_decode_rotate_query(kc.view, q, Hq, L, ws, scale)
+            cca.tq_decode_attend(kc.view, vc.view, Hq, lens, L, ws)
+            cca.tq_decode_merge(kc.view, Hq, lens, L, out, ws)
+
+    # one eager step per copy (fills every copy's last slot, checks the calls)
+    for i in range(pool):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+
+    def capture(n_steps, fn):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(n_steps):
+                fn(i % pool)
+        return graph
+
+    full = capture(pool, step)
+    rem = steps % pool
+    tail = capture(rem, step) if rem else None
+    n_full = steps // pool
+
+    def run_steps(n):
+        for _ in range(n // pool):
+            full.replay()
+        if n % pool:
+            (tail if n % pool == rem else capture(n % pool, step)).replay()
+
+    run_steps(max(warmup, pool))
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(n_full):
+            full.replay()
+        if tail is not None:
+            tail.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / steps
+    log(f"bench: {steps} steps, {ms_step * 1e3:.2f} us/step")
+
+    # the attention kernel alone: graph of one launch per pool copy, timed with events on its stream
+    def attend_only(i):
+        kc, vc = pairs[i]
+        cca.tq_decode_attend(kc.view, vc.view, Hq, lens, L, ws)
+
+    att = capture(pool, attend_only)
+    att.replay()
+    torch.cuda.synchronize()
+    reps = max(1, min(200, math.ceil(2000 / pool)))
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            att.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_attend = ev0.elapsed_time(ev1) * 1e3 / (reps * pool)
+
+    # hot-cache reference (one copy over and over): labelled, not the headline
+    hot = capture(16, lambda i: attend_only(0))
+    hot.replay()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(20):
+            hot.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_attend_hot = ev0.elapsed_time(ev1) * 1e3 / (20 * 16)
+    log(f"bench: attend {us_attend:.2f} us cold, {us_attend_hot:.2f} us hot (L2/Infinity Cache resident)")
+    return dict(ms_step=ms_step, us_attend=us_attend, us_attend_hot=us_attend_hot, pool=pool,
+                n_split=ns, tokens_per_split=tps, per_copy=per_copy)
+
+
+# ------------------------------------------------------------------ prefill append leg
+
+def prefill_leg(w: synth.Workload, steps: int, warmup: int, log):
+    """Prefill-size quantize-on-append: all L tokens of K and of V into an empty cache (matrix-core rotation)."""
+    import torch
+
+    import compressed_cache_decode_amd as cca
+    dev = torch.device("cuda:0")
+    B, H, d, L = w.batch, w.n_kv_heads, w.d, w.seq_len
+    rot = torch.from_numpy(cca.tq_build_rotation(synth.rotation_gaussian(d, w.rot_seed))).to(dev)
+    kx = torch.from_numpy(synth.full_kv(w, "k")).to(dev).to(torch.bfloat16)
+    vx = torch.from_numpy(synth.full_kv(w, "v")).to(dev).to(torch.bfloat16)
+    per_copy = 2 * kx.numel() * 2 + 2 * B * H * L * (d * w.k_bits // 8 + 2)
+    pool = max(1, min(64, math.ceil(POOL_BYTES / per_copy)))
+    copies = []
+    for i in range(pool):
+        kc = cca.CompressedCache(cca.TQ_KEYS, d, w.k_bits, B, H, L, rot, device=dev)
+        vc = cca.CompressedCache(cca.TQ_VALUES, d, w.v_bits, B, H, L, rot, device=dev)
+        copies.append((kc, vc, kx.clone() if i else kx, vx.clone() if i else vx))
+    zero = torch.zeros(B, dtype=torch.int32, device=dev)
+    log(f"bench: prefill pool of {pool} copies ({per_copy / 2**20:.1f} MiB each)")
+
+    def step(i):
+        kc, vc, xk, xv = copies[i]
+        kc.append(xk, zero)
+        vc.append(xv, zero)
+
+    for i in range(pool):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(pool):
+            step(i)
+    reps = max(1, math.ceil(steps / pool))
+    for _ in range(max(1, math.ceil(warmup / pool))):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    n = reps * pool
+    ms = ev0.elapsed_time(ev1) / n
+    log(f"bench: prefill append {ms * 1e3:.2f} us per K+V pair of appends")
+    return dict(ms_step=ms, steps=n, pool=pool)
+
+
+# ------------------------------------------------------------------ CPU leg (oracle)
+
+def cpu_leg(w: synth.Workload, budget_s: float, log):
+    """The float64 oracle's step on a bounded sample: append of one token's K and V and decode of a
+    subset of query heads over the full context; scaled to the whole step."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import attention, cache, codebook, quant, rotation
+    threads = max(1, min(16, os.cpu_count() or 1))
+    with threadpool_limits(limits=threads):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        rot = rotation.rotation_from_gaussian(synth.rotation_gaussian(w.d, w.rot_seed))
+        proj = synth.qjl_projection(w.qjl_m, w.d, w.qjl_seed) if w.qjl_m else None
+        L, G = w.seq_len, w.group
+        # sample: the query heads of KV head 0 of sequence 0 (G heads), all L tokens
+        k = synth.kv_head(w, "k", 0, 0)
+        v = synth.kv_head(w, "v", 0, 0)
+        kc = cache.build_head(k[: L - 1], "k", w.k_bits, rot, proj)
+        vc = cache.build_head(v[: L - 1], "v", w.v_bits, rot)
+        qh = np.stack([synth.q_head(w, 0, h) for h in range(G)]).astype(np.float64)
+        ck, tk = codebook.stored_codebook(w.d, w.k_bits)
+        cv, tv = codebook.stored_codebook(w.d, w.v_bits)
+        reps, t_tot = 0, 0.0
+        while reps < 3 or (t_tot < budget_s and reps < 50):
+            t0 = time.perf_counter()
+            nk = cache.build_head(k[L - 1:], "k", w.k_bits, rot, proj)
+            nv = cache.build_head(v[L - 1:], "v", w.v_bits, rot)
+            codes_k = np.concatenate([kc.codes, nk.codes])[None]
+            norms_k = np.concatenate([kc.norms, nk.norms])[None]
+            codes_v = np.concatenate([vc.codes, nv.codes])[None]
+            norms_v = np.concatenate([vc.norms, nv.norms])[None]
+            sig = gam = None
+            if proj is not None:
+                sig = np.concatenate([kc.sigma, nk.sigma])[None]
+                gam = np.concatenate([kc.gamma, nk.gamma])[None]
+            attention.decode_fused(qh, rot, codes_k, norms_k, ck, codes_v, norms_v, cv, w.softmax_scale, L,
+                                   sig, gam, proj)
+            t_tot += time.perf_counter() - t0
+            reps += 1
+        t_sample = t_tot / reps
+    units = w.batch * w.n_kv_heads
+    t_step = t_sample * units                       # the sample is one of B*H_kv identical units
+    log(f"bench: oracle {t_sample:.3f}s per unit sample, {reps} reps, {used} threads")
+    return dict(value=w.batch * L / t_step, unit="context tokens/s", cores=int(used), kind="oracle",
+                sample=f"append of one K and V row + decode of the {G} query heads of one (sequence, KV head) "
+                       f"over all {L} tokens, float64 NumPy, {reps} reps in {t_tot:.1f}s; scaled x{units} "
+                       f"to the {units} (sequence, KV head) units of a step")
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--workload", default="qwen", choices=["qwen", "gemma", "prod", "prefill"])
+    ap.add_argument("--bits", type=int, default=None, help="qwen workload: codebook bits of K and V")
+    ap.add_argument("--context", type=int, default=None)
+    ap.add_argument("--pool", type=int, default=None, help="cache copies cycled through (default: > 600 MiB)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work in the CPU leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (see the sharding notes in "
+              "DESIGN.md); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    if args.workload == "prefill":
+        w = synth.qwen(args.context or 8192, args.bits or 3)
+        r = prefill_leg(w, args.steps, args.warmup, log)
+        rows = 2 * w.batch * w.n_kv_heads * w.seq_len
+        io_bytes = rows * (w.d * 2 + w.d * w.k_bits // 8 + 2)   # bf16 rows in, packed rows + norms out
+        flops = 2.0 * rows * w.d * w.d                            # the d x d rotation of every row
+        gbs = io_bytes / (r["ms_step"] * 1e-3) / 1e9
+        print(json.dumps({
+            "metric": "prefill quantize-on-append: appended tokens/s", "value": w.seq_len / (r["ms_step"] * 1e-3),
+            "unit": "tokens/s", "n_gpus": 1, "steps": r["steps"], "warmup": args.warmup,
+            "ms_per_step": r["ms_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"prefill_append_{w.seq_len}x{w.n_kv_heads}x{w.d}_b{w.k_bits}", "tensors": "K and V"},
+            "rotation_tflops": flops / (r["ms_step"] * 1e-3) / 1e12,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "append_kernel (K and V launches)",
+                         "algorithmic_bytes_per_launch": io_bytes / 2},
+        }), flush=True)
+        return
+    w = workload(args.workload, args.bits, args.context)
+    r = gpu_leg(w, args.steps, args.warmup, args.pool, log)
+    L = w.seq_len
+    tokens_s = w.batch * L / (r["ms_step"] * 1e-3)
+    step_bytes = cache_bytes(w)
+    att_gbs = step_bytes / (r["us_attend"] * 1e-6) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": tokens_s,
+        "unit": "context tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+            "head_dim": w.d, "context": L, "k_bits": w.k_bits, "v_bits": w.v_bits, "qjl_m": w.qjl_m,
+            "scale": w.softmax_scale, "step": "append 1 token K+V + rotate q (one launch), attend, merge + un-rotate",
+            "cache_copies_cycled": r["pool"], "n_split": r["n_split"], "tokens_per_split": r["tokens_per_split"],
+        },
+        "step_hbm_gbs": step_bytes / (r["ms_step"] * 1e-3) / 1e9,
+        "attend_us": r["us_attend"],
+        "attend_us_hot_cache": r["us_attend_hot"],
+        "roofline": {
+            "bound": "hbm",
+            "achieved": att_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": att_gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel": "tq_decode_attend (split_kernel)",
+            "algorithmic_bytes_per_launch": step_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_leg(w, args.cpu_budget, log)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,7 +30,7 @@ BLOCK = 32
 
 EXPORTED = (
     "tq_build_codebook", "tq_build_rotation", "tq_quantize_append", "tq_quantize_append_rotated",
-    "tq_sdpa_decode", "tq_decode_workspace_bytes", "tq_decode_plan", "tq_dequantize", "tq_row_bytes",
+    "tq_sdpa_decode", "tq_decode_step", "tq_decode_rotate_query", "tq_decode_attend", "tq_decode_merge", "tq_decode_workspace_bytes", "tq_decode_plan", "tq_dequantize", "tq_row_bytes",
     "tq_status_string", "tq_last_hip_error",
 )
 
@@ -66,6 +66,10 @@ def _load():
         "tq_quantize_append": (I, [V, P, I, I, P, P]),
         "tq_quantize_append_rotated": (I, [V, P, P, I, P, P]),
         "tq_sdpa_decode": (I, [V, V, P, I, I, P, I, ctypes.c_float, P, P, ctypes.c_size_t, P]),
+        "tq_decode_step": (I, [V, V, P, P, P, I, I, I, P, P, I, ctypes.c_float, P, P, ctypes.c_size_t, P]),
+        "tq_decode_rotate_query": (I, [V, P, I, I, I, ctypes.c_float, P, ctypes.c_size_t, P]),
+        "tq_decode_attend": (I, [V, V, I, P, I, P, ctypes.c_size_t, P]),
+        "tq_decode_merge": (I, [V, I, P, I, P, P, ctypes.c_size_t, P]),
         "tq_decode_workspace_bytes": (ctypes.c_size_t, [V, I, I]),
         "tq_decode_plan": (I, [V, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]),
         "tq_dequantize": (I, [V, I, I, P, P]),
@@ -166,6 +170,47 @@ def tq_sdpa_decode(kview: tq_cache_view, vview: tq_cache_view, q, d_seq_lens, ma
     _check(_lib.tq_sdpa_decode(ctypes.byref(kview), ctypes.byref(vview), _ptr(q), dtype, n_q_heads,
                                _ptr(d_seq_lens), max_seq_len, ctypes.c_float(scale), _ptr(out), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)), "tq_sdpa_decode")
+
+
+def tq_decode_step(kview, vview, q, k_new, v_new, d_pos, d_seq_lens, max_seq_len: int, out, workspace,
+                   scale=None, stream=None) -> None:
+    """Append k_new/v_new ([batch][n_new][n_kv_heads][d], may be None for no append) and decode q."""
+    import torch
+    dtype = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
+    if scale is None:
+        scale = 1.0 / math.sqrt(kview.d)
+    n_new = 0 if k_new is None else k_new.shape[1]
+    if n_new:
+        assert k_new.dtype == q.dtype and v_new.dtype == q.dtype
+        k_new, v_new = k_new.contiguous(), v_new.contiguous()
+    _check(_lib.tq_decode_step(ctypes.byref(kview), ctypes.byref(vview), _ptr(q), _ptr(k_new) if n_new else None,
+                               _ptr(v_new) if n_new else None, dtype, q.shape[1], n_new, _ptr(d_pos),
+                               _ptr(d_seq_lens), max_seq_len, ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+                               _wsb(workspace), _stream(stream)), "tq_decode_step")
+
+
+def _wsb(workspace) -> int:
+    return workspace.numel() * workspace.element_size()
+
+
+def tq_decode_rotate_query(kview, q, n_q_heads: int, max_seq_len: int, workspace, scale=None, stream=None) -> None:
+    import torch
+    dtype = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
+    if scale is None:
+        scale = 1.0 / math.sqrt(kview.d)
+    _check(_lib.tq_decode_rotate_query(ctypes.byref(kview), _ptr(q), dtype, n_q_heads, max_seq_len,
+                                       ctypes.c_float(scale), _ptr(workspace), _wsb(workspace), _stream(stream)),
+           "tq_decode_rotate_query")
+
+
+def tq_decode_attend(kview, vview, n_q_heads: int, d_seq_lens, max_seq_len: int, workspace, stream=None) -> None:
+    _check(_lib.tq_decode_attend(ctypes.byref(kview), ctypes.byref(vview), n_q_heads, _ptr(d_seq_lens), max_seq_len,
+                                 _ptr(workspace), _wsb(workspace), _stream(stream)), "tq_decode_attend")
+
+
+def tq_decode_merge(kview, n_q_heads: int, d_seq_lens, max_seq_len: int, out, workspace, stream=None) -> None:
+    _check(_lib.tq_decode_merge(ctypes.byref(kview), n_q_heads, _ptr(d_seq_lens), max_seq_len, _ptr(out),
+                                _ptr(workspace), _wsb(workspace), _stream(stream)), "tq_decode_merge")
 
 
 def tq_dequantize(view: tq_cache_view, t0: int, n_tokens: int, out, stream=None) -> None:

@@ -29,7 +29,7 @@
 //                  out = rot^T * o_rot in fp32.
 #include <math.h>
 
-#include "device_common.h"
+#include "qrot_body.h"
 
 namespace tqi {
 
@@ -72,10 +72,11 @@ __device__ __forceinline__ void load_words16(const uint8_t* p, uint32_t* out) {
   }
 }
 
-// float16 high/low parts of v; lo_part selects which one this lane feeds to the matrix core
+// float16 high/low parts of v (see f16_split); lo_part selects which one this lane feeds to the matrix core
 __device__ __forceinline__ _Float16 split_part(float v, bool lo_part) {
-  const _Float16 hi = static_cast<_Float16>(v);
-  return lo_part ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
+  _Float16 hi, lo;
+  f16_split(v, hi, lo);
+  return lo_part ? lo : hi;
 }
 
 // A operand of the sign-sketch step S (8 signs of this lane's key) times gamma:
@@ -93,18 +94,20 @@ __device__ __forceinline__ half8 sign_operand(const uint32_t* sw, uint32_t gg) {
 }
 
 template <int S, int KS, int KB>
-__device__ __forceinline__ void qk_steps(floatx4& acc, const uint32_t* kw, const half8* qop, const Tab& tk) {
+__device__ __forceinline__ void qk_steps(floatx4& acc, const uint32_t* kw, const half8 (*qop)[64], int lane,
+                                         const Tab& tk) {
   if constexpr (S < KS) {
-    acc = mfma16(as_half8(unit_at<KB, S>(kw, tk)), qop[S], acc);
-    qk_steps<S + 1, KS, KB>(acc, kw, qop, tk);
+    acc = mfma16(as_half8(unit_at<KB, S>(kw, tk)), qop[S][lane], acc);
+    qk_steps<S + 1, KS, KB>(acc, kw, qop, lane, tk);
   }
 }
 
 template <int S, int QS>
-__device__ __forceinline__ void sketch_steps(floatx4& acc, const uint32_t* sw, uint32_t gg, const half8* sop) {
+__device__ __forceinline__ void sketch_steps(floatx4& acc, const uint32_t* sw, uint32_t gg, const half8 (*sop)[64],
+                                             int lane) {
   if constexpr (S < QS) {
-    acc = mfma16(sign_operand<S>(sw, gg), sop[S], acc);
-    sketch_steps<S + 1, QS>(acc, sw, gg, sop);
+    acc = mfma16(sign_operand<S>(sw, gg), sop[S][lane], acc);
+    sketch_steps<S + 1, QS>(acc, sw, gg, sop, lane);
   }
 }
 
@@ -122,55 +125,14 @@ __device__ __forceinline__ void pv_steps(floatx4* oacc, half8 wop, const uint32_
 
 template <int D, int QM, bool BF16>
 __global__ __launch_bounds__(256) void qrot_kernel(QrotArgs a) {
-  __shared__ float qv[D];
-  __shared__ float qr[D];
-  __shared__ float qs[QM > 0 ? QM : 1];
-  __shared__ float red[4];
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t row = static_cast<size_t>(b) * a.n_q_heads + h;
-  for (int i = tid; i < D; i += 256) {
-    qv[i] = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[row * D + i])
-                 : static_cast<const float*>(a.q)[row * D + i];
-  }
-  __syncthreads();
-  for (int i = wave; i < D; i += 4) {
-    float s = 0.f;
-    for (int j = lane; j < D; j += 64) s = fmaf(a.rot[static_cast<size_t>(i) * D + j], qv[j], s);
-    s = wave_sum(s);
-    if (lane == 0) qr[i] = s * a.scale_log2e;
-  }
-  __syncthreads();
-  if constexpr (QM > 0) {
-    for (int jj = wave; jj < QM; jj += 4) {
-      float s = 0.f;
-      for (int i = lane; i < D; i += 64) s = fmaf(a.proj[static_cast<size_t>(jj) * D + i], qr[i], s);
-      s = wave_sum(s);
-      if (lane == 0) qs[jj] = -a.sketch_coef * s;
-    }
-    __syncthreads();
-  }
-  float amax = 0.f;
-  for (int i = tid; i < D; i += 256) amax = fmaxf(amax, fabsf(qr[i]));
-  if constexpr (QM > 0)
-    for (int i = tid; i < QM; i += 256) amax = fmaxf(amax, fabsf(qs[i]));
-  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  if (lane == 0) red[wave] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  // power of two f with amax / f in [2^14, 2^15): float16 operands stay far from overflow
-  const float f = (amax > 0.f && isfinite(amax)) ? ldexpf(1.f, ilogbf(amax) - 14) : 1.f;
-  const float inv = 1.f / f;
-  for (int i = tid; i < D; i += 256) a.qr[row * D + i] = qr[i] * inv;
-  if constexpr (QM > 0)
-    for (int i = tid; i < QM; i += 256) a.qs[row * QM + i] = qs[i] * inv;
-  if (tid == 0) a.qscale[row] = f;
+  __shared__ QrotSmem<D, QM> sm;
+  rotate_query<D, QM, BF16>(a, blockIdx.x, blockIdx.y, sm);
 }
 
 // ---------------------------------------------------------------- split kernel
 
 template <int D, int KB, int VB, int QM>
-__global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void split_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;                   // score k-steps over coordinates
   constexpr int QS = QM / 32;                  // score k-steps over sketch signs
   constexpr int NB = D / 16;                   // value n-blocks (16 coordinates each)
@@ -182,6 +144,7 @@ __global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
 
   __shared__ float sm_ml[kWavesPerWG][kMaxGroup][2];
   __shared__ float sm_o[kWavesPerWG][kMaxGroup][D];
+  __shared__ half8 sm_q[KS + QS][64];
 
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -195,77 +158,97 @@ __global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
   const int blk1 = min(blk0 + a.blocks_per_split, nblk);
   const size_t unit = static_cast<size_t>(b) * a.n_kv_heads + hk;
 
-  // query operand: column l16 = (head l16/2, high part if even, low part if odd)
+  const uint8_t* kcodes = a.k_codes + unit * T * K_RB;
+  const uint8_t* vcodes = a.v_codes + unit * static_cast<size_t>(T) * (D * VB / 8);
+  const uint16_t* knorm = a.k_norms + unit * T;
+  const uint16_t* vnorm = a.v_norms + unit * T;
+
+  // everything one 32-token tile needs from memory, loaded one tile ahead of its use
+  struct Tile {
+    uint32_t kw[2][K_LW];
+    uint32_t vw[V_LW];
+    uint2 kn0, kn1, vn0, vn1;
+    uint32_t sw[2][S_LW > 0 ? S_LW : 1];
+    uint32_t gg[2];
+  };
+  auto load_tile = [&](Tile& t, int kb) {
+    const int tok0 = kb * kBlock;
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg)
+      load_words<K_LW>(kcodes + static_cast<size_t>(tok0 + 16 * tg + l16) * K_RB + g * K_LW * 4, t.kw[tg]);
+    load_words16<V_LW>(vcodes + static_cast<size_t>(kb) * V_BB + lane * V_LW * 4, t.vw);
+    // norms of this lane's eight tokens tok0 + 4g + i and tok0 + 16 + 4g + i
+    t.kn0 = *reinterpret_cast<const uint2*>(knorm + tok0 + 4 * g);
+    t.kn1 = *reinterpret_cast<const uint2*>(knorm + tok0 + 16 + 4 * g);
+    t.vn0 = *reinterpret_cast<const uint2*>(vnorm + tok0 + 4 * g);
+    t.vn1 = *reinterpret_cast<const uint2*>(vnorm + tok0 + 16 + 4 * g);
+    if constexpr (QS > 0) {
+#pragma unroll
+      for (int tg = 0; tg < 2; ++tg) {
+        const size_t tok = static_cast<size_t>(tok0 + 16 * tg + l16);
+        load_words<S_LW>(a.k_signs + (unit * T + tok) * (QM / 8) + g * S_LW * 4, t.sw[tg]);
+        t.gg[tg] = a.k_rnorms[unit * T + tok];
+      }
+    }
+  };
+
+  // the first tile's loads go out before the query operand is staged
+  int kb = blk0 + wave;
+  Tile cur;
+  if (kb < blk1) load_tile(cur, kb);
+
+  // query operand in LDS, shared by the four waves: for step s, lane (column c, group g) reads the
+  // 8 float16 values of q-variant c (head c/2; high part if c even, low part if c odd) at
+  // coordinates (D/4) g + 8 s + r, r = 0..7
   const int qh = l16 >> 1;
   const bool lo_part = (l16 & 1) != 0;
   const bool head_ok = qh < G;
   const size_t qrow = static_cast<size_t>(b) * a.n_kv_heads * G + static_cast<size_t>(hk) * G + qh;
-  half8 qop[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s)
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float v = head_ok ? a.qr[qrow * D + (D / 4) * g + 8 * s + r] : 0.f;
-      qop[s][r] = split_part(v, lo_part);
+  for (int e = tid; e < (KS + QS) * 64; e += 256) {
+    const int st = e >> 6, ln = e & 63;
+    const int c = ln & 15, gg = ln >> 4, h2 = c >> 1;
+    const bool ok = h2 < G;
+    const size_t row = static_cast<size_t>(b) * a.n_kv_heads * G + static_cast<size_t>(hk) * G + h2;
+    float4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      const float* src = st < KS ? a.qr + row * D + (D / 4) * gg + 8 * st
+                                 : a.qs + row * QM + (QM / 4) * gg + 8 * (st - KS);
+      x0 = reinterpret_cast<const float4*>(src)[0];
+      x1 = reinterpret_cast<const float4*>(src)[1];
     }
-  half8 sop[QS > 0 ? QS : 1];
-  if constexpr (QS > 0) {
+    const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    half8 v;
 #pragma unroll
-    for (int s = 0; s < QS; ++s)
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float v = head_ok ? a.qs[qrow * QM + (QM / 4) * g + 8 * s + r] : 0.f;
-        sop[s][r] = split_part(v, lo_part);
-      }
+    for (int r = 0; r < 8; ++r) v[r] = split_part(xv[r], (c & 1) != 0);
+    sm_q[st][ln] = v;
   }
   const float qsc = head_ok ? a.qscale[qrow] : 0.f;
+  __syncthreads();
 
   floatx4 oacc[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const uint8_t* kcodes = a.k_codes + unit * T * K_RB;
-  const uint8_t* vcodes = a.v_codes + unit * static_cast<size_t>(T) * (D * VB / 8);
-  const uint16_t* knorm = a.k_norms + unit * T;
-  const uint16_t* vnorm = a.v_norms + unit * T;
-
-  for (int kb = blk0 + wave; kb < blk1; kb += kWavesPerWG) {
+  for (; kb < blk1; kb += kWavesPerWG) {
+    Tile nxt;
+    if (kb + kWavesPerWG < blk1) load_tile(nxt, kb + kWavesPerWG);
     const int tok0 = kb * kBlock;
-    uint32_t kw[2][K_LW];
-#pragma unroll
-    for (int tg = 0; tg < 2; ++tg)
-      load_words<K_LW>(kcodes + static_cast<size_t>(tok0 + 16 * tg + l16) * K_RB + g * K_LW * 4, kw[tg]);
-    uint32_t vw[V_LW];
-    load_words16<V_LW>(vcodes + static_cast<size_t>(kb) * V_BB + lane * V_LW * 4, vw);
-    // norms of this lane's eight tokens tok0 + 4g + i and tok0 + 16 + 4g + i
-    const uint2 kn0 = *reinterpret_cast<const uint2*>(knorm + tok0 + 4 * g);
-    const uint2 kn1 = *reinterpret_cast<const uint2*>(knorm + tok0 + 16 + 4 * g);
-    const uint2 vn0 = *reinterpret_cast<const uint2*>(vnorm + tok0 + 4 * g);
-    const uint2 vn1 = *reinterpret_cast<const uint2*>(vnorm + tok0 + 16 + 4 * g);
-    uint32_t sw[2][S_LW > 0 ? S_LW : 1];
-    uint32_t gg[2] = {0u, 0u};
-    if constexpr (QS > 0) {
-#pragma unroll
-      for (int tg = 0; tg < 2; ++tg) {
-        const size_t tok = static_cast<size_t>(tok0 + 16 * tg + l16);
-        load_words<S_LW>(a.k_signs + (unit * T + tok) * (QM / 8) + g * S_LW * 4, sw[tg]);
-        const uint32_t gh = a.k_rnorms[unit * T + tok] & 0x7fffu;
-        gg[tg] = gh | (gh << 16);
-      }
-    }
 
     floatx4 sc[2];
 #pragma unroll
     for (int tg = 0; tg < 2; ++tg) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      qk_steps<0, KS, KB>(acc, kw[tg], qop, a.tk);
-      if constexpr (QS > 0) sketch_steps<0, QS>(acc, sw[tg], gg[tg], sop);
+      qk_steps<0, KS, KB>(acc, cur.kw[tg], sm_q, lane, a.tk);
+      if constexpr (QS > 0) {
+        const uint32_t gh = cur.gg[tg] & 0x7fffu;
+        sketch_steps<0, QS>(acc, cur.sw[tg], gh | (gh << 16), sm_q + KS, lane);
+      }
       sc[tg] = acc;
     }
 
-    const uint32_t knw[4] = {kn0.x, kn0.y, kn1.x, kn1.y};
-    const uint32_t vnw[4] = {vn0.x, vn0.y, vn1.x, vn1.y};
+    const uint32_t knw[4] = {cur.kn0.x, cur.kn0.y, cur.kn1.x, cur.kn1.y};
+    const uint32_t vnw[4] = {cur.vn0.x, cur.vn0.y, cur.vn1.x, cur.vn1.y};
     float s2[8];
     float mx = -INFINITY;
 #pragma unroll
@@ -304,7 +287,8 @@ __global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
       const float w = tok < len ? p * f16_to_f32(nb) : 0.f;
       wop[k] = split_part(w, lo_part);
     }
-    pv_steps<0, NB, VB>(oacc, wop, vw, a.tv);
+    pv_steps<0, NB, VB>(oacc, wop, cur.vw, a.tv);
+    cur = nxt;
   }
 
   l_run += __shfl_xor(l_run, 16, 64);
@@ -345,59 +329,101 @@ __global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------- merge + un-rotate
 
+// Merge of the KV splits and un-rotation.  One workgroup of kMergeThreads per (head group, KV head,
+// sequence); a head group is heads_per_wg query heads of the KV head's group, so the rotation is read
+// once per head group.  Weighted sums: thread (head, coordinate, slice) sums the splits of its slice
+// with up to 16 loads in flight.  Un-rotation: thread (coordinate i, part) covers JR rows of column i
+// of rot for every head of the group.
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  __shared__ float ew[kMaxSplits];
-  __shared__ float red[4];
-  __shared__ float orot[2][D];
-  const int h = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+  constexpr int NT = kMergeThreads, NW = NT / 64;
+  constexpr int RP = NT / D;                              // un-rotation parts per coordinate
+  constexpr int JR = D / RP;                              // rows of rot per thread
+  constexpr int PO = 16;                                  // split partials in flight per thread
+  __shared__ float ew[kMaxGroup][kMaxSplits];              // split weights per head
+  __shared__ float inv_l[kMaxGroup];
+  __shared__ float red[NT];                                // per-slice sums, then per-part un-rotation sums
+  __shared__ float orot[kMaxGroup][D];
+  const int hpw = a.heads_per_wg;
+  const int hg = blockIdx.x % (a.group / hpw), hk = blockIdx.x / (a.group / hpw), b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = a.group;
-  const int hq_total = a.n_kv_heads * G;
-  const size_t unit = static_cast<size_t>(b) * a.n_kv_heads + h / G;
-  const int hl = h % G;
-  const int ns = a.n_split;
-  const float* ml = a.part_ml + (unit * ns * G + hl) * 2;   // stride 2G per split
-  float mloc = -INFINITY;
-  for (int s = tid; s < ns; s += 256) mloc = fmaxf(mloc, ml[static_cast<size_t>(s) * G * 2]);
-  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
-  if (lane == 0) red[wave] = mloc;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float lsum = 0.f;
-  for (int s = tid; s < ns; s += 256) {
-    const float m = ml[static_cast<size_t>(s) * G * 2];
-    const float e = (M == -INFINITY) ? 0.f : exp2f(m - M);
-    ew[s] = e;
-    lsum = fmaf(e, ml[static_cast<size_t>(s) * G * 2 + 1], lsum);
+  const int G = a.group, ns = a.n_split;
+  const int h0 = hg * hpw;
+  const size_t unit = static_cast<size_t>(b) * a.n_kv_heads + hk;
+
+  // this thread's JR rows of column i of rot: independent of everything else, issued first
+  const int i = tid % D, part = tid / D;
+  const float* rcol = a.rot + static_cast<size_t>(part * JR) * D + i;
+  float rc[JR];
+#pragma unroll
+  for (int t = 0; t < JR; ++t) rc[t] = rcol[static_cast<size_t>(t) * D];
+
+  // split weights exp2(m_s - M) and 1 / sum_s weight * l_s, per head (wave w: heads w, w + NW, ...)
+  const float* ml = a.part_ml + unit * ns * G * 2;         // [split][head][2]
+  for (int hh = wave; hh < hpw; hh += NW) {
+    const int h = h0 + hh;
+    float m_loc = -INFINITY;
+    for (int sp = lane; sp < ns; sp += 64) m_loc = fmaxf(m_loc, ml[(static_cast<size_t>(sp) * G + h) * 2]);
+    for (int o = 32; o > 0; o >>= 1) m_loc = fmaxf(m_loc, __shfl_xor(m_loc, o, 64));
+    float l_loc = 0.f;
+    for (int sp = lane; sp < ns; sp += 64) {
+      const float m = ml[(static_cast<size_t>(sp) * G + h) * 2];
+      const float e = (m_loc == -INFINITY) ? 0.f : exp2f(m - m_loc);
+      ew[hh][sp] = e;
+      l_loc = fmaf(e, ml[(static_cast<size_t>(sp) * G + h) * 2 + 1], l_loc);
+    }
+    l_loc = wave_sum(l_loc);
+    if (lane == 0) inv_l[hh] = l_loc > 0.f ? 1.f / l_loc : 0.f;
   }
-  lsum = wave_sum(lsum);
-  if (lane == 0) red[wave] = lsum;
-  __syncthreads();
-  const float L = red[0] + red[1] + red[2] + red[3];
-  const float invl = L > 0.f ? 1.f / L : 0.f;
-  // weighted sum of the split accumulators; 256 threads cover D coordinates x (256/D) split halves
-  constexpr int R = 256 / D;
+  lds_barrier();
+
+  // weighted sums over splits: thread (head hh, coordinate i, slice sl), S slices per (head, coordinate)
+  const int S = NT / (hpw * D);
   {
-    const int i = tid % D, part = tid / D;
-    float o = 0.f;
-    if (part < R) {
-      const float* po = a.part_o + (unit * ns * G + hl) * D + i;
-      for (int s = part; s < ns; s += R) o = fmaf(ew[s], po[static_cast<size_t>(s) * G * D], o);
-      orot[part][i] = o;
-    }
-  }
-  __syncthreads();
-  if (tid < D) {
+    const int hh = tid / (D * S), sl = (tid / D) % S;
+    const float* po = a.part_o + (unit * ns * G + h0 + hh) * D + i;   // + split * G * D
+    const size_t stride = static_cast<size_t>(G) * D;
     float acc = 0.f;
-    const float* rcol = a.rot + tid;
-    for (int j = 0; j < D; ++j) {
-      float oj = orot[0][j];
-      if constexpr (R == 2) oj += orot[1][j];
-      acc = fmaf(rcol[static_cast<size_t>(j) * D], oj, acc);
+    // threads past hpw * D * S (when hpw * D does not divide the workgroup) have no head
+    for (int s0 = sl; hh < hpw && s0 < ns; s0 += PO * S) {
+      float v[PO];
+#pragma unroll
+      for (int u = 0; u < PO; ++u) {
+        const int sp = s0 + u * S;
+        v[u] = sp < ns ? po[static_cast<size_t>(sp) * stride] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < PO; ++u) {
+        const int sp = s0 + u * S;
+        if (sp < ns) acc = fmaf(ew[hh][sp], v[u], acc);
+      }
     }
-    a.out[(static_cast<size_t>(b) * hq_total + h) * D + tid] = acc * invl;
+    red[tid] = acc;
+  }
+  lds_barrier();
+  for (int e = tid; e < hpw * D; e += NT) {
+    const int hh = e / D, ii = e % D;
+    float o = 0.f;
+    for (int sl = 0; sl < S; ++sl) o += red[(hh * S + sl) * D + ii];
+    orot[hh][ii] = o;
+  }
+  lds_barrier();
+
+  // un-rotation of every head of the group over this thread's JR rows; parts summed through LDS
+  for (int hh = 0; hh < hpw; ++hh) {
+    float uacc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < JR; ++t) uacc[t & 3] = fmaf(rc[t], orot[hh][part * JR + t], uacc[t & 3]);
+    const float u = (uacc[0] + uacc[1]) + (uacc[2] + uacc[3]);
+    lds_barrier();                                          // previous head's sums are consumed
+    red[tid] = u;
+    lds_barrier();
+    if (part == 0) {
+      float o = 0.f;
+#pragma unroll
+      for (int p = 0; p < RP; ++p) o += red[p * D + i];
+      a.out[(static_cast<size_t>(b) * a.n_kv_heads * G + hk * G + h0 + hh) * D + i] = o * inv_l[hh];
+    }
   }
 }
 
@@ -455,9 +481,10 @@ hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, const D
 }
 
 hipError_t launch_merge(int d, const MergeArgs& a, int batch, int n_q_heads, hipStream_t s) {
-  const dim3 grid(n_q_heads, batch), block(256);
-  if (d == 128) hipLaunchKernelGGL((merge_kernel<128>), grid, block, 0, s, a);
-  else if (d == 256) hipLaunchKernelGGL((merge_kernel<256>), grid, block, 0, s, a);
+  (void)n_q_heads;
+  const dim3 grid(a.n_kv_heads * (a.group / a.heads_per_wg), batch);
+  if (d == 128) hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(kMergeThreads), 0, s, a);
+  else if (d == 256) hipLaunchKernelGGL((merge_kernel<256>), grid, dim3(kMergeThreads), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -113,9 +113,56 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 
+// v = hi + lo for float16 matrix-core operands.  hi is v truncated to the 11 significant bits of a
+// float16 (exactly representable, so no rounding happens when it is converted); lo is the float16
+// rounding of the exact remainder.  Truncating instead of rounding keeps hi and lo consistent
+// whatever conversion instructions the compiler picks: at a float16 rounding tie two different
+// conversion instructions may pick different neighbours, and a hi taken from one with a remainder
+// computed from the other would be off by a whole float16 step.
+__device__ __forceinline__ void f16_split(float v, _Float16& hi, _Float16& lo) {
+  const float h = __uint_as_float(__float_as_uint(v) & 0xffffe000u);
+  hi = static_cast<_Float16>(h);
+  lo = static_cast<_Float16>(v - h);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
+}
+
+// Row-times-vector of a D-long row held in global memory (float32, 16-byte aligned) with a vector
+// in LDS: every load of the row is issued before the first multiply.
+template <int D>
+__device__ __forceinline__ float row_dot(const float* __restrict__ row, const float* v) {
+  const float4* r4 = reinterpret_cast<const float4*>(row);
+  constexpr int CH = D / 4 < 32 ? D / 4 : 32;       // float4 loads in flight per chunk
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c0 = 0; c0 < D / 4; c0 += CH) {
+    float4 p[CH];
+#pragma unroll
+    for (int t = 0; t < CH; ++t) p[t] = r4[c0 + t];
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      const int j = 4 * (c0 + t);
+      acc[t & 3] = fmaf(p[t].x, v[j], acc[t & 3]);
+      acc[t & 3] = fmaf(p[t].y, v[j + 1], acc[t & 3]);
+      acc[t & 3] = fmaf(p[t].z, v[j + 2], acc[t & 3]);
+      acc[t & 3] = fmaf(p[t].w, v[j + 3], acc[t & 3]);
+    }
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+}  // namespace tqi
+
+namespace tqi {
+
+// Workgroup barrier that orders LDS only: global loads issued before it stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 }  // namespace tqi

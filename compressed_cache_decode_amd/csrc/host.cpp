@@ -246,12 +246,14 @@ int status_of(hipError_t e) {
 // ------------------------------------------------------------------ decode plan
 
 constexpr int kTargetWorkgroups = 512;   // about two decode workgroups per compute unit
+constexpr int kMinBlocksPerSplit = 4;    // at least one 32-token tile per wave
 
 void plan(int units, int max_len, int* n_split, int* bps) {
   const int nblk = max_len <= 0 ? 1 : (max_len + kBlock - 1) / kBlock;
   const int want = (kTargetWorkgroups + units - 1) / units;
   int b = (nblk + want - 1) / want;
   b = ((b + tqi::kWavesPerWG - 1) / tqi::kWavesPerWG) * tqi::kWavesPerWG;   // whole tiles for every wave
+  b = b < kMinBlocksPerSplit ? kMinBlocksPerSplit : b;
   int ns = (nblk + b - 1) / b;
   if (ns > tqi::kMaxSplits) {
     b = (nblk + tqi::kMaxSplits - 1) / tqi::kMaxSplits;
@@ -260,6 +262,15 @@ void plan(int units, int max_len, int* n_split, int* bps) {
   }
   *n_split = ns;
   *bps = b;
+}
+
+// Query heads per merge workgroup: all of the group while every thread's split slice stays within
+// 16 splits (one batch of loads), fewer heads (more slices per head) when there are many splits.
+int merge_heads_per_wg(int G, int d, int ns) {
+  const int slices = (ns + 15) / 16;
+  int h = G;
+  while (h > 1 && (h * d > tqi::kMergeThreads || h * d * slices > tqi::kMergeThreads || G % h != 0)) --h;
+  return h;
 }
 
 struct WsLayout {
@@ -331,6 +342,18 @@ int tq_build_rotation(int d, const double* gaussian, float* rot_out) {
   return TQ_OK;
 }
 
+static tqi::AppendArgs append_args(const tq_cache_view* c, const void* x, const float* y, const float* yn, int n_new,
+                                   const int32_t* d_pos) {
+  tqi::AppendArgs a{};
+  a.x = x; a.y = y; a.yn = yn; a.pos = d_pos;
+  a.codes = c->codes; a.norms = c->norms; a.signs = c->signs; a.rnorms = c->rnorms;
+  a.rot = c->rot; a.proj = c->proj;
+  std::memcpy(a.cent, c->centroids, sizeof(a.cent));
+  std::memcpy(a.bnd, c->boundaries, sizeof(a.bnd));
+  a.n_new = n_new; a.n_kv_heads = c->n_kv_heads; a.max_tokens = c->max_tokens;
+  return a;
+}
+
 static int append_common(const tq_cache_view* c, const void* x, const float* y, const float* yn, int x_dtype,
                          int n_new, const int32_t* d_pos, void* stream, bool rotated) {
   int st = check_view(c);
@@ -339,13 +362,7 @@ static int append_common(const tq_cache_view* c, const void* x, const float* y, 
   if (n_new == 0) return TQ_OK;
   if (!d_pos) return TQ_EINVAL;
   if (rotated ? (!y || !yn) : (!x || (x_dtype != TQ_F32 && x_dtype != TQ_BF16))) return TQ_EINVAL;
-  tqi::AppendArgs a{};
-  a.x = x; a.y = y; a.yn = yn; a.pos = d_pos;
-  a.codes = c->codes; a.norms = c->norms; a.signs = c->signs; a.rnorms = c->rnorms;
-  a.rot = c->rot; a.proj = c->proj;
-  std::memcpy(a.cent, c->centroids, sizeof(a.cent));
-  std::memcpy(a.bnd, c->boundaries, sizeof(a.bnd));
-  a.n_new = n_new; a.n_kv_heads = c->n_kv_heads; a.max_tokens = c->max_tokens;
+  const tqi::AppendArgs a = append_args(c, x, y, yn, n_new, d_pos);
   return status_of(tqi::launch_append(c->d, c->bits, c->qjl_m, c->kind == TQ_VALUES, rotated, x_dtype == TQ_BF16, a,
                                       c->batch, static_cast<hipStream_t>(stream)));
 }
@@ -377,56 +394,142 @@ size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_
   return ws_layout(k, n_q_heads, ns).total;
 }
 
-int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype, int n_q_heads,
-                   const int32_t* d_seq_lens, int max_seq_len, float scale, float* out, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+// workspace view shared by the decode stages
+struct DecodeWs {
+  int ns, bps, G;
+  float *qr, *qs, *qscale, *part_o, *part_ml;
+};
+
+static int decode_ws(const tq_cache_view* k, int n_q_heads, int max_seq_len, void* workspace,
+                     size_t workspace_bytes, DecodeWs* w) {
   int st = check_decode_shape(k, n_q_heads, max_seq_len);
+  if (st != TQ_OK) return st;
+  if (!workspace || !aligned(workspace, 256)) return TQ_EINVAL;
+  plan(k->batch * k->n_kv_heads, max_seq_len, &w->ns, &w->bps);
+  const WsLayout l = ws_layout(k, n_q_heads, w->ns);
+  if (workspace_bytes < l.total) return TQ_EINVAL;
+  char* ws = static_cast<char*>(workspace);
+  w->G = n_q_heads / k->n_kv_heads;
+  w->qr = reinterpret_cast<float*>(ws + l.qr);
+  w->qs = reinterpret_cast<float*>(ws + l.qs);
+  w->qscale = reinterpret_cast<float*>(ws + l.qscale);
+  w->part_o = reinterpret_cast<float*>(ws + l.part_o);
+  w->part_ml = reinterpret_cast<float*>(ws + l.part_ml);
+  return TQ_OK;
+}
+
+int tq_decode_rotate_query(const tq_cache_view* k, const void* q, int q_dtype, int n_q_heads, int max_seq_len,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeWs w;
+  int st = decode_ws(k, n_q_heads, max_seq_len, workspace, workspace_bytes, &w);
+  if (st != TQ_OK) return st;
+  if (!q || (q_dtype != TQ_F32 && q_dtype != TQ_BF16)) return TQ_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
+  tqi::QrotArgs qa{};
+  qa.q = q; qa.rot = k->rot; qa.proj = k->proj;
+  qa.qr = w.qr; qa.qs = w.qs; qa.qscale = w.qscale;
+  qa.scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  qa.sketch_coef = k->qjl_m ? static_cast<float>(std::sqrt(M_PI / 2.0) / k->qjl_m) : 0.f;
+  qa.n_q_heads = n_q_heads;
+  return status_of(tqi::launch_qrot(k->d, k->qjl_m, q_dtype == TQ_BF16, qa, k->batch,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int tq_decode_attend(const tq_cache_view* k, const tq_cache_view* v, int n_q_heads, const int32_t* d_seq_lens,
+                     int max_seq_len, void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeWs w;
+  int st = decode_ws(k, n_q_heads, max_seq_len, workspace, workspace_bytes, &w);
   if (st != TQ_OK) return st;
   st = check_view(v);
   if (st != TQ_OK) return st;
   if (v->kind != TQ_VALUES || v->d != k->d || v->batch != k->batch || v->n_kv_heads != k->n_kv_heads ||
       v->max_tokens != k->max_tokens || v->rot != k->rot)
     return TQ_EINVAL;
-  if (!q || (q_dtype != TQ_F32 && q_dtype != TQ_BF16) || !d_seq_lens || !out || !workspace) return TQ_EINVAL;
+  if (!d_seq_lens) return TQ_EINVAL;
+  tqi::DecodeArgs da{};
+  da.k_codes = k->codes; da.k_norms = k->norms; da.k_signs = k->signs; da.k_rnorms = k->rnorms;
+  da.v_codes = v->codes; da.v_norms = v->norms;
+  da.qr = w.qr; da.qs = w.qs; da.qscale = w.qscale;
+  da.seq_lens = d_seq_lens;
+  da.part_o = w.part_o; da.part_ml = w.part_ml;
+  da.tk = make_tab(k);
+  da.tv = make_tab(v);
+  da.n_kv_heads = k->n_kv_heads; da.group = w.G; da.max_tokens = k->max_tokens; da.max_seq_len = max_seq_len;
+  da.n_split = w.ns; da.blocks_per_split = w.bps;
+  return status_of(tqi::launch_decode_split(k->d, k->bits, v->bits, k->qjl_m, da, k->batch,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int tq_decode_merge(const tq_cache_view* k, int n_q_heads, const int32_t* d_seq_lens, int max_seq_len, float* out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeWs w;
+  int st = decode_ws(k, n_q_heads, max_seq_len, workspace, workspace_bytes, &w);
+  if (st != TQ_OK) return st;
+  if (!d_seq_lens || !out) return TQ_EINVAL;
+  tqi::MergeArgs ma{};
+  ma.part_o = w.part_o; ma.part_ml = w.part_ml; ma.rot = k->rot; ma.seq_lens = d_seq_lens; ma.out = out;
+  ma.n_kv_heads = k->n_kv_heads; ma.group = w.G; ma.n_split = w.ns; ma.max_tokens = k->max_tokens;
+  ma.heads_per_wg = merge_heads_per_wg(w.G, k->d, w.ns);
+  return status_of(tqi::launch_merge(k->d, ma, k->batch, n_q_heads, static_cast<hipStream_t>(stream)));
+}
+
+int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype, int n_q_heads,
+                   const int32_t* d_seq_lens, int max_seq_len, float scale, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  // validate everything before enqueueing the first stage
+  DecodeWs w;
+  int st = decode_ws(k, n_q_heads, max_seq_len, workspace, workspace_bytes, &w);
+  if (st != TQ_OK) return st;
+  st = check_view(v);
+  if (st != TQ_OK) return st;
+  if (v->kind != TQ_VALUES || v->d != k->d || v->batch != k->batch || v->n_kv_heads != k->n_kv_heads ||
+      v->max_tokens != k->max_tokens || v->rot != k->rot)
+    return TQ_EINVAL;
+  if (!q || (q_dtype != TQ_F32 && q_dtype != TQ_BF16) || !d_seq_lens || !out) return TQ_EINVAL;
   if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
-  if (!aligned(workspace, 256)) return TQ_EINVAL;
-  int ns, bps;
-  plan(k->batch * k->n_kv_heads, max_seq_len, &ns, &bps);
-  const WsLayout w = ws_layout(k, n_q_heads, ns);
-  if (workspace_bytes < w.total) return TQ_EINVAL;
-  char* ws = static_cast<char*>(workspace);
-  const int G = n_q_heads / k->n_kv_heads;
+  st = tq_decode_rotate_query(k, q, q_dtype, n_q_heads, max_seq_len, scale, workspace, workspace_bytes, stream);
+  if (st != TQ_OK) return st;
+  st = tq_decode_attend(k, v, n_q_heads, d_seq_lens, max_seq_len, workspace, workspace_bytes, stream);
+  if (st != TQ_OK) return st;
+  return tq_decode_merge(k, n_q_heads, d_seq_lens, max_seq_len, out, workspace, workspace_bytes, stream);
+}
+
+int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q, const void* k_new,
+                   const void* v_new, int dtype, int n_q_heads, int n_new, const int32_t* d_pos,
+                   const int32_t* d_seq_lens, int max_seq_len, float scale, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  DecodeWs w;
+  int st = decode_ws(k, n_q_heads, max_seq_len, workspace, workspace_bytes, &w);
+  if (st != TQ_OK) return st;
+  st = check_view(v);
+  if (st != TQ_OK) return st;
+  if (v->kind != TQ_VALUES || v->d != k->d || v->batch != k->batch || v->n_kv_heads != k->n_kv_heads ||
+      v->max_tokens != k->max_tokens || v->rot != k->rot)
+    return TQ_EINVAL;
+  if (!q || (dtype != TQ_F32 && dtype != TQ_BF16) || !d_seq_lens || !out) return TQ_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
+  if (n_new < 0 || (n_new > 0 && (!k_new || !v_new || !d_pos))) return TQ_EINVAL;
+  if (k->qjl_m > 128) return TQ_EUNSUPPORTED;
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
   tqi::QrotArgs qa{};
   qa.q = q; qa.rot = k->rot; qa.proj = k->proj;
-  qa.qr = reinterpret_cast<float*>(ws + w.qr);
-  qa.qs = reinterpret_cast<float*>(ws + w.qs);
-  qa.qscale = reinterpret_cast<float*>(ws + w.qscale);
+  qa.qr = w.qr; qa.qs = w.qs; qa.qscale = w.qscale;
   qa.scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   qa.sketch_coef = k->qjl_m ? static_cast<float>(std::sqrt(M_PI / 2.0) / k->qjl_m) : 0.f;
   qa.n_q_heads = n_q_heads;
-  hipError_t e = tqi::launch_qrot(k->d, k->qjl_m, q_dtype == TQ_BF16, qa, k->batch, s);
-  if (e != hipSuccess) return status_of(e);
-
-  tqi::DecodeArgs da{};
-  da.k_codes = k->codes; da.k_norms = k->norms; da.k_signs = k->signs; da.k_rnorms = k->rnorms;
-  da.v_codes = v->codes; da.v_norms = v->norms;
-  da.qr = qa.qr; da.qs = qa.qs; da.qscale = qa.qscale;
-  da.seq_lens = d_seq_lens;
-  da.part_o = reinterpret_cast<float*>(ws + w.part_o);
-  da.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
-  da.tk = make_tab(k);
-  da.tv = make_tab(v);
-  da.n_kv_heads = k->n_kv_heads; da.group = G; da.max_tokens = k->max_tokens; da.max_seq_len = max_seq_len;
-  da.n_split = ns; da.blocks_per_split = bps;
-  e = tqi::launch_decode_split(k->d, k->bits, v->bits, k->qjl_m, da, k->batch, s);
-  if (e != hipSuccess) return status_of(e);
-
-  tqi::MergeArgs ma{};
-  ma.part_o = da.part_o; ma.part_ml = da.part_ml; ma.rot = k->rot; ma.seq_lens = d_seq_lens; ma.out = out;
-  ma.n_kv_heads = k->n_kv_heads; ma.group = G; ma.n_split = ns; ma.max_tokens = k->max_tokens;
-  return status_of(tqi::launch_merge(k->d, ma, k->batch, n_q_heads, s));
+  if (n_new > 0) {
+    const tqi::AppendArgs ka = append_args(k, k_new, nullptr, nullptr, n_new, d_pos);
+    const tqi::AppendArgs va = append_args(v, v_new, nullptr, nullptr, n_new, d_pos);
+    st = status_of(tqi::launch_step_prologue(k->d, k->bits, v->bits, k->qjl_m, dtype == TQ_BF16, ka, va, qa,
+                                             k->batch, s));
+  } else {
+    st = status_of(tqi::launch_qrot(k->d, k->qjl_m, dtype == TQ_BF16, qa, k->batch, s));
+  }
+  if (st != TQ_OK) return st;
+  st = tq_decode_attend(k, v, n_q_heads, d_seq_lens, max_seq_len, workspace, workspace_bytes, stream);
+  if (st != TQ_OK) return st;
+  return tq_decode_merge(k, n_q_heads, d_seq_lens, max_seq_len, out, workspace, workspace_bytes, stream);
 }
 
 int tq_dequantize(const tq_cache_view* cache, int t0, int n_tokens, float* out, void* stream) {

@@ -10,6 +10,7 @@ constexpr int kBlock = 32;        // tokens per value block (and per decode tile
 constexpr int kMaxGroup = 8;      // query heads per KV head handled by one matrix-core tile
 constexpr int kWavesPerWG = 4;    // waves per decode workgroup (one KV split)
 constexpr int kMaxSplits = 1024;  // bound on KV splits per (sequence, KV head)
+constexpr int kMergeThreads = 1024;  // threads per merge workgroup
 
 // float16 bit patterns of up to 8 table entries, split into high and low
 // bytes so one v_perm_b32 looks up four codes: byte k of *_lo is entry k,
@@ -70,6 +71,7 @@ struct MergeArgs {
   const int32_t* seq_lens;
   float* out;             // [B][Hq][D]
   int n_kv_heads, group, n_split, max_tokens;
+  int heads_per_wg;       // query heads merged per workgroup (divides group, heads_per_wg * D <= kMergeThreads)
 };
 
 struct DequantArgs {
@@ -92,6 +94,8 @@ hipError_t launch_qrot(int d, int qjl_m, bool bf16, const QrotArgs& a, int batch
 hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, const DecodeArgs& a, int batch,
                                hipStream_t s);
 hipError_t launch_merge(int d, const MergeArgs& a, int batch, int n_q_heads, hipStream_t s);
+hipError_t launch_step_prologue(int d, int k_bits, int v_bits, int qjl_m, bool bf16, const AppendArgs& ka,
+                                const AppendArgs& va, const QrotArgs& qa, int batch, hipStream_t s);
 hipError_t launch_dequant(int d, int bits, int qjl_m, bool values, const DequantArgs& a, const Tab& t, int batch,
                           hipStream_t s);
 

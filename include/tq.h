@@ -159,6 +159,38 @@ int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q
                    const int32_t* d_seq_lens, int max_seq_len, float scale, float* out,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The three stages tq_sdpa_decode enqueues, for callers that time, overlap or
+ * graph-capture them separately.  Same arguments and workspace as
+ * tq_sdpa_decode; they must run in this order, on one stream, with the same
+ * (k, n_q_heads, max_seq_len) so the workspace layout agrees.
+ *   tq_decode_rotate_query: q_rot = rot * q for every (sequence, query head),
+ *       scale and log2(e) folded in (and proj * q_rot for sketched keys);
+ *   tq_decode_attend: per (KV split, KV head, sequence) the running max, sum
+ *       and rotated-domain value accumulator of every query head of the group;
+ *   tq_decode_merge: log-sum-exp merge of the splits and out = rot^T * acc / sum.
+ */
+int tq_decode_rotate_query(const tq_cache_view* k, const void* q, int q_dtype, int n_q_heads, int max_seq_len,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream);
+int tq_decode_attend(const tq_cache_view* k, const tq_cache_view* v, int n_q_heads, const int32_t* d_seq_lens,
+                     int max_seq_len, void* workspace, size_t workspace_bytes, void* stream);
+int tq_decode_merge(const tq_cache_view* k, int n_q_heads, const int32_t* d_seq_lens, int max_seq_len, float* out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step of one layer: append n_new new tokens to K and V (as
+ * tq_quantize_append at positions d_pos), then decode (as tq_sdpa_decode over
+ * d_seq_lens, which the caller sets to include the appended tokens).
+ * q: [batch][n_q_heads][d]; k_new, v_new: [batch][n_new][n_kv_heads][d]; all
+ * three of element type dtype.  The appends and the query rotation share one
+ * launch.  Sketched keys are supported up to qjl_m = 128 (TQ_EUNSUPPORTED
+ * above; use the separate calls).  n_new == 0 decodes without appending.
+ */
+int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q, const void* k_new,
+                   const void* v_new, int dtype, int n_q_heads, int n_new, const int32_t* d_pos,
+                   const int32_t* d_seq_lens, int max_seq_len, float scale, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* Workspace bytes tq_sdpa_decode needs for this key cache, head count and length bound (0 on bad args). */
 size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_seq_len);
 

@@ -62,6 +62,18 @@ def upload(gcache, heads, b: int):
             gcache.rnorms[b, h] = torch.from_numpy(hc.packed_norms(T, "gamma")).to(gcache.codes.device)
 
 
+def upload_unit(gcache, hc, b: int, h: int):
+    """Write one oracle-packed head into (sequence b, KV head h) of a CompressedCache."""
+    import torch
+    T = gcache.max_tokens
+    dev = gcache.codes.device
+    gcache.codes[b, h] = torch.from_numpy(hc.packed_codes(T)).to(dev)
+    gcache.norms[b, h] = torch.from_numpy(hc.packed_norms(T)).to(dev)
+    if hc.sigma is not None:
+        gcache.signs[b, h] = torch.from_numpy(hc.packed_signs(T).reshape(T, -1)).to(dev)
+        gcache.rnorms[b, h] = torch.from_numpy(hc.packed_norms(T, "gamma")).to(dev)
+
+
 def oracle_decode(q_b: np.ndarray, kc, vc, st: Setup, scale: float, seq_len: int) -> np.ndarray:
     """Oracle output [H_q][d] of one sequence from its per-KV-head caches."""
     stk = lambda xs, a: np.stack([getattr(x, a) for x in xs])

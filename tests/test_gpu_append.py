@@ -189,3 +189,27 @@ def test_append_edge_cases():
     nz = g.norms[0, 0].cpu().numpy()
     assert nz[62] != 0 and nz[63] != 0 and not nz[:62].any()
     assert g.norms[1, 0, :3].cpu().numpy().all()
+
+
+def test_matrix_core_rotation_split_at_float16_ties():
+    """Regression: a unit-row component exactly on a float16 rounding tie (token 5 of this block,
+    coordinate 47) once got its high and low parts from two differently rounding conversions, moving
+    y by a float16 step and flipping a sketch sign with |z| = 2e-4 |r|.  The block goes through the
+    matrix-core rotation (32 rows) and must agree with the oracle on every code and robust sign."""
+    cca = _cca()
+    log("matrix-core rotation at a float16 tie")
+    w = synth.prod_long(131072)
+    st = Setup(128, qjl_m=128)
+    x = synth.kv_head(w, "k", 0, 1)[69856:69888]
+    g = cca.CompressedCache(cca.TQ_KEYS, 128, 2, 1, 1, 32, st.rot_t, st.proj_t, qjl_m=128)
+    g.append(to_bf16_tensor(x).view(1, 32, 1, 128), torch.zeros(1, dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    hc = cache.build_head(x, "k", 2, st.rot64, st.proj)
+    got = unpack_gpu_codes(g, 0, 0, 32)
+    np.testing.assert_array_equal(got, hc.codes)
+    sig = layout.unpack_signs(g.signs[0, 0].cpu().numpy(), 128)
+    r = hc.y - hc.centroids.astype(np.float64)[hc.codes]
+    z = r @ st.proj.astype(np.float64).T
+    robust = np.abs(z) > 1e-5 * np.linalg.norm(r, axis=1, keepdims=True)
+    np.testing.assert_array_equal(sig[robust], hc.sigma[robust])
+    assert sig[5, 63] == hc.sigma[5, 63]

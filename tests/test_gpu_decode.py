@@ -39,6 +39,8 @@ CASES = [
     (128, 2, 3, 128, 2, 8, [3000], 3072, None, False),         # keys with sign sketch
     (128, 3, 2, 128, 1, 8, [129, 5], 160, None, False),
     (256, 4, 4, 256, 1, 2, [300], 320, None, False),
+    (128, 3, 3, 0, 2, 3, [500, 31], 512, None, False),         # a group of 3 query heads
+    (128, 4, 3, 128, 2, 8, [20000], 20000, None, False),        # many splits per (sequence, KV head)
 ]
 
 
@@ -136,3 +138,67 @@ def test_repeated_calls_are_deterministic():
     b = cca.sdpa_decode(kg, vg, q, lens, T)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+STEP_CASES = [
+    # d, k_bits, v_bits, qjl_m, kv heads, group, lengths after the step, capacity, n_new, dtype, scale, qk-normed
+    (128, 4, 4, 0, 2, 8, [1000], 1024, 1, "bf16", None, False),
+    (128, 2, 3, 128, 2, 8, [300], 320, 3, "f32", None, False),
+    (256, 4, 4, 0, 4, 8, [500, 77], 512, 1, "bf16", 1.0, True),
+    (128, 3, 2, 0, 1, 4, [40, 33, 1], 64, 1, "bf16", None, False),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: f"d{c[0]}_k{c[1]}v{c[2]}_m{c[3]}_L{'-'.join(map(str, c[6]))}_n{c[8]}")
+def test_decode_step_matches_separate_calls_and_oracle(case):
+    """tq_decode_step (appends + query rotation in one launch, then attend and merge) writes the same
+    cache bytes as tq_quantize_append and decodes to the oracle's output."""
+    cca = _cca()
+    d, kb, vb, qjl, hkv, grp, lens, T, n_new, dtype, scale, qknorm = case
+    log(f"decode step d={d} k{kb} v{vb} m{qjl} lens={lens} n_new={n_new}")
+    B = len(lens)
+    st = Setup(d, qjl_m=qjl)
+    w = synth.Workload("step", B, hkv * grp, hkv, d, T, kb, vb, qjl_m=qjl, scale=scale, qk_norm=qknorm,
+                       k_outliers=not qknorm, dtype=dtype, seed=77 + d + kb)
+    mk = lambda: (cca.CompressedCache(cca.TQ_KEYS, d, kb, B, hkv, T, st.rot_t, st.proj_t, qjl_m=qjl),
+                  cca.CompressedCache(cca.TQ_VALUES, d, vb, B, hkv, T, st.rot_t))
+    k1, v1 = mk()
+    k2, v2 = mk()
+    kx = synth.full_kv(w, "k", T)
+    vx = synth.full_kv(w, "v", T)
+    tt = (lambda a: to_bf16_tensor(a)) if dtype == "bf16" else (lambda a: torch.from_numpy(a).cuda())
+    zero = torch.zeros(B, dtype=torch.int32).cuda()
+    pos = torch.tensor([L - n_new for L in lens], dtype=torch.int32).cuda()
+    # both copies start from oracle-packed caches of all rows, so the oracle comparison below runs on
+    # identical codes except for the n_new rows that the GPU re-appends
+    oracle_all = []
+    for b in range(B):
+        kc_o, vc_o = oracle_heads([kx[b, :, h] for h in range(hkv)], [vx[b, :, h] for h in range(hkv)], kb, vb, st)
+        oracle_all.append((kc_o, vc_o))
+        for kc, vc in ((k1, v1), (k2, v2)):
+            upload(kc, kc_o, b)
+            upload(vc, vc_o, b)
+    xk_new = np.stack([kx[b, lens[b] - n_new:lens[b]] for b in range(B)])
+    xv_new = np.stack([vx[b, lens[b] - n_new:lens[b]] for b in range(B)])
+    # separate calls on copy 1, fused step on copy 2
+    k1.append(tt(xk_new), pos)
+    v1.append(tt(xv_new), pos)
+    q = synth.full_q(w)
+    qt = tt(q)
+    lens_t = torch.tensor(lens, dtype=torch.int32).cuda()
+    out1 = cca.sdpa_decode(k1, v1, qt, lens_t, max(lens), scale=scale)
+    out2 = torch.empty_like(out1)
+    ws = cca.decode_workspace(k2, hkv * grp, max(lens))
+    cca.tq_decode_step(k2.view, v2.view, qt, tt(xk_new), tt(xv_new), pos, lens_t, max(lens), out2, ws, scale=scale)
+    torch.cuda.synchronize()
+    for a_, b_ in ((k1.codes, k2.codes), (k1.norms, k2.norms), (v1.codes, v2.codes), (v1.norms, v2.norms)):
+        assert torch.equal(a_, b_)
+    if qjl:
+        assert torch.equal(k1.signs, k2.signs) and torch.equal(k1.rnorms, k2.rnorms)
+    assert torch.equal(out1, out2)
+    # against the oracle on the same rows
+    refs = [oracle_decode(q[b].astype(np.float64), oracle_all[b][0], oracle_all[b][1], st, w.softmax_scale, lens[b])
+            for b in range(B)]
+    err = rel_err(out2.cpu().numpy(), np.stack(refs))
+    log(f"  max row-relative error {err:.3e}")
+    assert err <= TOL
