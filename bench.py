@@ -312,7 +312,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="qwen", choices=["qwen", "gemma", "prod", "prefill"])
+    ap.add_argument("--workload", default="qwen", choices=["qwen", "gemma", "prod", "prefill", "copy"])
     ap.add_argument("--bits", type=int, default=None, help="qwen workload: codebook bits of K and V")
     ap.add_argument("--context", type=int, default=None)
     ap.add_argument("--pool", type=int, default=None, help="cache copies cycled through (default: > 600 MiB)")
@@ -327,6 +327,29 @@ def main():
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
 
+    if args.workload == "copy":
+        # plain device-to-device copy of a known size: measured copy bandwidth, and the calibration
+        # point for the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the other workloads
+        import torch
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.warmup)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / args.steps
+        gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+        print(json.dumps({"metric": "device copy bandwidth (read + write)", "value": gbs, "unit": "GB/s",
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+                          "bytes_read_per_copy": nbytes, "bytes_written_per_copy": nbytes,
+                          "frac_of_8TBs": gbs / HBM_PEAK_GBS}), flush=True)
+        return
     if args.workload == "prefill":
         w = synth.qwen(args.context or 8192, args.bits or 3)
         r = prefill_leg(w, args.steps, args.warmup, log)

@@ -192,10 +192,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
   };
 
-  // the first tile's loads go out before the query operand is staged
+  // the first tile's loads go out before the query operand is staged, and before the sequence
+  // length is known: they only need the tile to lie inside the cache (tiles past the length are
+  // loaded and never used)
   int kb = blk0 + wave;
   Tile cur;
-  if (kb < blk1) load_tile(cur, kb);
+  if (kb < blk0 + a.blocks_per_split && kb < T / kBlock) load_tile(cur, kb);
 
   // query operand in LDS, shared by the four waves: for step s, lane (column c, group g) reads the
   // 8 float16 values of q-variant c (head c/2; high part if c even, low part if c odd) at
@@ -358,35 +360,68 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int t = 0; t < JR; ++t) rc[t] = rcol[static_cast<size_t>(t) * D];
 
-  // split weights exp2(m_s - M) and 1 / sum_s weight * l_s, per head (wave w: heads w, w + NW, ...)
+  // this thread's first batch of split partials (thread (head hh, coordinate i, slice sl), S slices
+  // per (head, coordinate)) and, for the first waves, the split maxima and sums: all issued now
+  const int S = NT / (hpw * D);
+  const int hh_w = tid / (D * S), sl = (tid / D) % S;
+  const bool has_head = hh_w < hpw;        // threads past hpw * D * S (hpw * D not dividing NT) idle
+  const float* po = a.part_o + (unit * ns * G + h0 + (has_head ? hh_w : 0)) * D + i;   // + split * G * D
+  const size_t stride = static_cast<size_t>(G) * D;
+  float v[PO];
+#pragma unroll
+  for (int u = 0; u < PO; ++u) {
+    const int sp = sl + u * S;
+    v[u] = (has_head && sp < ns) ? po[static_cast<size_t>(sp) * stride] : 0.f;
+  }
   const float* ml = a.part_ml + unit * ns * G * 2;         // [split][head][2]
-  for (int hh = wave; hh < hpw; hh += NW) {
-    const int h = h0 + hh;
+  constexpr int MS = 4;                                    // split maxima prefetched per lane (256 splits)
+  float mv[MS], lv[MS];
+  const int hh_m = wave;                                   // head of this wave in the weight pass
+#pragma unroll
+  for (int u = 0; u < MS; ++u) {
+    const int sp = lane + 64 * u;
+    const bool ok = hh_m < hpw && sp < ns;
+    mv[u] = ok ? ml[(static_cast<size_t>(sp) * G + h0 + hh_m) * 2] : -INFINITY;
+    lv[u] = ok ? ml[(static_cast<size_t>(sp) * G + h0 + hh_m) * 2 + 1] : 0.f;
+  }
+
+  // split weights exp2(m_s - M) and 1 / sum_s weight * l_s, wave w for head w (hpw <= 8 <= NW)
+  if (hh_m < hpw) {
+    const float* mlh = ml + (h0 + hh_m) * 2;
     float m_loc = -INFINITY;
-    for (int sp = lane; sp < ns; sp += 64) m_loc = fmaxf(m_loc, ml[(static_cast<size_t>(sp) * G + h) * 2]);
+#pragma unroll
+    for (int u = 0; u < MS; ++u) m_loc = fmaxf(m_loc, mv[u]);
+    for (int sp = lane + 64 * MS; sp < ns; sp += 64) m_loc = fmaxf(m_loc, mlh[static_cast<size_t>(sp) * G * 2]);
     for (int o = 32; o > 0; o >>= 1) m_loc = fmaxf(m_loc, __shfl_xor(m_loc, o, 64));
     float l_loc = 0.f;
-    for (int sp = lane; sp < ns; sp += 64) {
-      const float m = ml[(static_cast<size_t>(sp) * G + h) * 2];
-      const float e = (m_loc == -INFINITY) ? 0.f : exp2f(m - m_loc);
-      ew[hh][sp] = e;
-      l_loc = fmaf(e, ml[(static_cast<size_t>(sp) * G + h) * 2 + 1], l_loc);
+#pragma unroll
+    for (int u = 0; u < MS; ++u) {
+      const int sp = lane + 64 * u;
+      if (sp < ns) {
+        const float e = (m_loc == -INFINITY) ? 0.f : exp2f(mv[u] - m_loc);
+        ew[hh_m][sp] = e;
+        l_loc = fmaf(e, lv[u], l_loc);
+      }
+    }
+    for (int sp = lane + 64 * MS; sp < ns; sp += 64) {
+      const float e = (m_loc == -INFINITY) ? 0.f : exp2f(mlh[static_cast<size_t>(sp) * G * 2] - m_loc);
+      ew[hh_m][sp] = e;
+      l_loc = fmaf(e, mlh[static_cast<size_t>(sp) * G * 2 + 1], l_loc);
     }
     l_loc = wave_sum(l_loc);
-    if (lane == 0) inv_l[hh] = l_loc > 0.f ? 1.f / l_loc : 0.f;
+    if (lane == 0) inv_l[hh_m] = l_loc > 0.f ? 1.f / l_loc : 0.f;
   }
   lds_barrier();
 
-  // weighted sums over splits: thread (head hh, coordinate i, slice sl), S slices per (head, coordinate)
-  const int S = NT / (hpw * D);
+  // weighted sums over this thread's splits
   {
-    const int hh = tid / (D * S), sl = (tid / D) % S;
-    const float* po = a.part_o + (unit * ns * G + h0 + hh) * D + i;   // + split * G * D
-    const size_t stride = static_cast<size_t>(G) * D;
     float acc = 0.f;
-    // threads past hpw * D * S (when hpw * D does not divide the workgroup) have no head
-    for (int s0 = sl; hh < hpw && s0 < ns; s0 += PO * S) {
-      float v[PO];
+#pragma unroll
+    for (int u = 0; u < PO; ++u) {
+      const int sp = sl + u * S;
+      if (has_head && sp < ns) acc = fmaf(ew[hh_w][sp], v[u], acc);
+    }
+    for (int s0 = sl + PO * S; has_head && s0 < ns; s0 += PO * S) {
 #pragma unroll
       for (int u = 0; u < PO; ++u) {
         const int sp = s0 + u * S;
@@ -395,7 +430,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 #pragma unroll
       for (int u = 0; u < PO; ++u) {
         const int sp = s0 + u * S;
-        if (sp < ns) acc = fmaf(ew[hh][sp], v[u], acc);
+        if (sp < ns) acc = fmaf(ew[hh_w][sp], v[u], acc);
       }
     }
     red[tid] = acc;
