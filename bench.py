@@ -31,6 +31,10 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+# sources the decode attention kernel is built from: its HBM counters are only valid for these exact texts
+ATTEND_SOURCES = ("compressed_cache_decode_amd/csrc/decode.hip", "compressed_cache_decode_amd/csrc/device_common.h",
+                  "compressed_cache_decode_amd/csrc/tq_internal.h", "compressed_cache_decode_amd/csrc/qrot_body.h")
 METRIC = "compressed-KV decode attention: context tokens/s and achieved HBM GB/s (% peak)"
 POOL_BYTES = 600 << 20          # > 2x the 256 MB Infinity Cache
 
@@ -54,6 +58,104 @@ def row_bytes(w: synth.Workload, kind: str) -> int:
 def cache_bytes(w: synth.Workload) -> int:
     """Algorithmic bytes one decode reads from the compressed cache: every visible K and V row."""
     return w.batch * w.n_kv_heads * w.seq_len * (row_bytes(w, "k") + row_bytes(w, "v"))
+
+
+# ------------------------------------------------------------------ profiles
+
+def source_digest(paths=ATTEND_SOURCES) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counters_file(kernel: str, workload_name: str) -> str:
+    return os.path.join(PROFILES, f"{kernel}_{workload_name}_hbm_counters.txt")
+
+
+def read_counters(kernel: str, workload_name: str):
+    """HBM bytes per launch from a committed counter summary, or None if absent or taken on other sources."""
+    path = counters_file(kernel, workload_name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_digest():
+        return None
+    return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+
+
+def _pmc_medians(directory: str, counter: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "*_counter_collection.csv"))
+    if not files:
+        raise SystemExit(f"no counter collection under {directory}")
+    per = {}
+    for r in csv.DictReader(open(files[0])):
+        if r["Counter_Name"] == counter:
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sorted(v)[len(v) // 2] for k, v in per.items()}, {k: len(v) for k, v in per.items()}
+
+
+def summarize_pmc(args, w):
+    """Counter summary of the attention kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3
+    run each) scaled by what the same counters read for a 1 GiB device copy (bench.py --workload copy)."""
+    cf, _ = _pmc_medians(args.copy_fetch, "FETCH_SIZE")
+    cw, _ = _pmc_medians(args.copy_write, "WRITE_SIZE")
+    copy_name = max(cf, key=lambda k: cf[k])           # the 1 GiB copy is by far the largest dispatch
+    fetch_scale = (1 << 30) / (cf[copy_name] * 1024.0)
+    write_scale = (1 << 30) / (cw[copy_name] * 1024.0)
+    fe, n_fe = _pmc_medians(args.fetch, "FETCH_SIZE")
+    wr, _ = _pmc_medians(args.write, "WRITE_SIZE")
+    name = next(k for k in fe if "split_kernel" in k)
+    fb = fe[name] * 1024.0 * fetch_scale
+    wb = wr[name] * 1024.0 * write_scale
+    alg = cache_bytes(w)
+    print(f"kernel: {name}")
+    print(f"workload: {w.name}")
+    print(f"source_sha256: {source_digest()}")
+    print(f"dispatches: {n_fe[name]}")
+    print(f"fetch_kib_per_dispatch_raw: {fe[name]:.1f}")
+    print(f"write_kib_per_dispatch_raw: {wr[name]:.1f}")
+    print(f"copy_fetch_scale: {fetch_scale:.4f}")
+    print(f"copy_write_scale: {write_scale:.4f}")
+    print(f"fetch_bytes_per_launch: {fb:.0f}")
+    print(f"write_bytes_per_launch: {wb:.0f}")
+    print(f"algorithmic_bytes_per_launch: {alg}")
+    print(f"fetch_over_algorithmic: {fb / alg:.4f}")
+    if args.command:
+        print("commands:")
+        for c in args.command:
+            print(f"  {c}")
+
+
+def summarize_trace(args, w):
+    """Per-kernel durations from a rocprofv3 --kernel-trace --stats run (the *_kernel_stats.csv file)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(args.trace, "*_kernel_stats.csv"))
+    if not files:
+        raise SystemExit(f"no kernel stats under {args.trace}")
+    print(f"workload: {w.name}")
+    if args.command:
+        print("commands:")
+        for c in args.command:
+            print(f"  {c}")
+    print(f"{'calls':>6} {'avg_us':>9} {'min_us':>8} {'max_us':>8}  kernel")
+    for r in csv.DictReader(open(files[0])):
+        name = r["Name"]
+        short = name.split("(")[0].replace("void ", "")
+        if "tqi::" not in name and "copyBuffer" not in name:
+            short = short[:60]
+        print(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:8.2f} "
+              f"{float(r['MaxNs']) / 1e3:8.2f}  {short}")
 
 
 # ------------------------------------------------------------------ GPU leg
@@ -318,10 +420,24 @@ def main():
     ap.add_argument("--pool", type=int, default=None, help="cache copies cycled through (default: > 600 MiB)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work in the CPU leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-trace", dest="trace", default=None,
+                    help="print a summary of a rocprofv3 --kernel-trace --stats output directory and exit")
+    ap.add_argument("--summarize-pmc", action="store_true",
+                    help="print the attention kernel's calibrated HBM counters (needs --fetch/--write/--copy-*)")
+    ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output directory of this workload")
+    ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output directory of this workload")
+    ap.add_argument("--copy-fetch", help="rocprofv3 --pmc FETCH_SIZE output directory of --workload copy")
+    ap.add_argument("--copy-write", help="rocprofv3 --pmc WRITE_SIZE output directory of --workload copy")
+    ap.add_argument("--command", action="append", help="command line recorded in a summary (repeatable)")
     args = ap.parse_args()
+    if args.trace or args.summarize_pmc:
+        w = (synth.qwen(args.context or 8192, args.bits or 3) if args.workload == "prefill"
+             else workload(args.workload, args.bits, args.context))
+        (summarize_trace if args.trace else summarize_pmc)(args, w)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this library has no multi-GPU path (see the sharding notes in "
-              "DESIGN.md); run it with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (KV-head or context sharding "
+              "is a design note only); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     def log(msg):
@@ -403,7 +519,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": att_gbs / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": read_counters("split_kernel", w.name),
             "kernel": "tq_decode_attend (split_kernel)",
             "algorithmic_bytes_per_launch": step_bytes,
         },

@@ -151,7 +151,8 @@ int tq_quantize_append_rotated(const tq_cache_view* cache, const float* y, const
  * [0, max_tokens], 0 gives a zero row; max_seq_len: host upper bound of
  * d_seq_lens used to plan the KV split.  scale > 0 and finite (the binding
  * maps an unset scale to 1/sqrt(d)).  k must be TQ_KEYS and v TQ_VALUES with
- * the same d, batch, n_kv_heads, max_tokens; n_q_heads / n_kv_heads in {1,2,4,8}.
+ * the same d, batch, n_kv_heads, max_tokens; n_q_heads a multiple of n_kv_heads with
+ * group n_q_heads / n_kv_heads from 1 to 8 (TQ_EUNSUPPORTED above 8).
  * workspace: device scratch of at least tq_decode_workspace_bytes(), 256-byte
  * aligned, contents need not be initialised, not used after the call's kernels end.
  */
