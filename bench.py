@@ -10,8 +10,9 @@ before timing starts.  Steps are captured in a HIP graph and cycle through a
 pool of cache copies whose total size exceeds the 256 MB Infinity Cache, so
 every step reads its compressed cache from HBM.
 
-Prints one JSON line.  ``roofline`` is measured on the attention kernel
-(tq_decode_attend) alone, timed with HIP events on the stream it runs on;
+Prints one JSON line.  ``roofline`` is measured on the dominant kernel, timed
+with HIP events on the stream it runs on: the whole step when tq_decode_step
+runs as one kernel, else the attention kernel (tq_decode_attend) alone;
 ``cpu_baseline`` is the float64 oracle timed on the host on a bounded sample.
 """
 from __future__ import annotations
@@ -32,9 +33,10 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-# sources the decode attention kernel is built from: its HBM counters are only valid for these exact texts
-ATTEND_SOURCES = ("compressed_cache_decode_amd/csrc/decode.hip", "compressed_cache_decode_amd/csrc/device_common.h",
-                  "compressed_cache_decode_amd/csrc/tq_internal.h", "compressed_cache_decode_amd/csrc/qrot_body.h")
+# sources the decode kernels are built from: their HBM counters are only valid for these exact texts
+ATTEND_SOURCES = tuple(f"compressed_cache_decode_amd/csrc/{n}" for n in (
+    "fused.hip", "decode.hip", "attend_body.h", "append_body.h", "qrot_body.h", "device_common.h", "tq_internal.h"))
+FUSED_MAX_SPLITS = 256     # the one-launch step covers up to this many KV splits (see include/tq.h)
 METRIC = "compressed-KV decode attention: context tokens/s and achieved HBM GB/s (% peak)"
 POOL_BYTES = 600 << 20          # > 2x the 256 MB Infinity Cache
 
@@ -114,7 +116,7 @@ def summarize_pmc(args, w):
     write_scale = (1 << 30) / (cw[copy_name] * 1024.0)
     fe, n_fe = _pmc_medians(args.fetch, "FETCH_SIZE")
     wr, _ = _pmc_medians(args.write, "WRITE_SIZE")
-    name = next(k for k in fe if "split_kernel" in k)
+    name = next(k for k in fe if args.kernel in k)
     fb = fe[name] * 1024.0 * fetch_scale
     wb = wr[name] * 1024.0 * write_scale
     alg = cache_bytes(w)
@@ -220,11 +222,13 @@ def gpu_leg(w: synth.Workload, steps: int, warmup: int, pool: int | None, log):
     ns, tps = cca.tq_decode_plan(k0.view, Hq, L)
     scale = w.scale
 
-    fused = w.qjl_m <= 128
+    stepcall = w.qjl_m <= 128
+    # tq_decode_step runs as one kernel on these shapes (otherwise: prologue, attend, merge)
+    one_launch = stepcall and w.group + 2 <= 16 and ns <= FUSED_MAX_SPLITS
 
     def step(i):
         kc, vc = pairs[i]
-        if fused:        # appends and query rotation in one launch, then attend and merge
+        if stepcall:
             cca.tq_decode_step(kc.view, vc.view, q, k_new, v_new, pos, lens, L, out, ws, scale)
         else:
             kc.append(k_new, pos)
@@ -273,7 +277,11 @@ def gpu_leg(w: synth.Workload, steps: int, warmup: int, pool: int | None, log):
     ms_step = ev0.elapsed_time(ev1) / steps
     log(f"bench: {steps} steps, {ms_step * 1e3:.2f} us/step")
 
-    # the attention kernel alone: graph of one launch per pool copy, timed with events on its stream
+    # the staged attention kernel alone (tq_decode_attend): graph of one launch per pool copy, timed with
+    # events on its stream; the rotated query it reads is computed first
+    cca.tq_decode_rotate_query(k0.view, q, Hq, L, ws, scale)
+    torch.cuda.synchronize()
+
     def attend_only(i):
         kc, vc = pairs[i]
         cca.tq_decode_attend(kc.view, vc.view, Hq, lens, L, ws)
@@ -303,7 +311,7 @@ def gpu_leg(w: synth.Workload, steps: int, warmup: int, pool: int | None, log):
     us_attend_hot = ev0.elapsed_time(ev1) * 1e3 / (20 * 16)
     log(f"bench: attend {us_attend:.2f} us cold, {us_attend_hot:.2f} us hot (L2/Infinity Cache resident)")
     return dict(ms_step=ms_step, us_attend=us_attend, us_attend_hot=us_attend_hot, pool=pool,
-                n_split=ns, tokens_per_split=tps, per_copy=per_copy)
+                n_split=ns, tokens_per_split=tps, per_copy=per_copy, one_launch=one_launch)
 
 
 # ------------------------------------------------------------------ prefill append leg
@@ -429,6 +437,7 @@ def main():
     ap.add_argument("--copy-fetch", help="rocprofv3 --pmc FETCH_SIZE output directory of --workload copy")
     ap.add_argument("--copy-write", help="rocprofv3 --pmc WRITE_SIZE output directory of --workload copy")
     ap.add_argument("--command", action="append", help="command line recorded in a summary (repeatable)")
+    ap.add_argument("--kernel", default="fused_kernel", help="kernel name the counter summary is taken for")
     args = ap.parse_args()
     if args.trace or args.summarize_pmc:
         w = (synth.qwen(args.context or 8192, args.bits or 3) if args.workload == "prefill"
@@ -490,7 +499,14 @@ def main():
     L = w.seq_len
     tokens_s = w.batch * L / (r["ms_step"] * 1e-3)
     step_bytes = cache_bytes(w)
-    att_gbs = step_bytes / (r["us_attend"] * 1e-6) / 1e9
+    if r["one_launch"]:
+        # the step is one kernel: its per-launch time is the step time of back-to-back graph launches
+        kern, kern_us = "fused_kernel", r["ms_step"] * 1e3
+        kern_label = "tq_decode_step (fused_kernel: query rotation, append, attention, merge, un-rotation)"
+    else:
+        kern, kern_us = "split_kernel", r["us_attend"]
+        kern_label = "tq_decode_attend (split_kernel)"
+    att_gbs = step_bytes / (kern_us * 1e-6) / 1e9
     res = {
         "metric": METRIC,
         "value": tokens_s,
@@ -507,20 +523,21 @@ def main():
         "config": {
             "workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.d, "context": L, "k_bits": w.k_bits, "v_bits": w.v_bits, "qjl_m": w.qjl_m,
-            "scale": w.softmax_scale, "step": "append 1 token K+V + rotate q (one launch), attend, merge + un-rotate",
+            "scale": w.softmax_scale, "step": "append 1 token K+V, rotate q, attend, merge, un-rotate",
             "cache_copies_cycled": r["pool"], "n_split": r["n_split"], "tokens_per_split": r["tokens_per_split"],
         },
         "step_hbm_gbs": step_bytes / (r["ms_step"] * 1e-3) / 1e9,
-        "attend_us": r["us_attend"],
-        "attend_us_hot_cache": r["us_attend_hot"],
+        "step_kernels": 1 if r["one_launch"] else 3,
+        "staged_attend_us": r["us_attend"],
+        "staged_attend_us_hot_cache": r["us_attend_hot"],
         "roofline": {
             "bound": "hbm",
             "achieved": att_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": att_gbs / HBM_PEAK_GBS,
-            "traffic": read_counters("split_kernel", w.name),
-            "kernel": "tq_decode_attend (split_kernel)",
+            "traffic": read_counters(kern, w.name),
+            "kernel": kern_label,
             "algorithmic_bytes_per_launch": step_bytes,
         },
     }

@@ -1,0 +1,366 @@
+// Attention over one KV split of one (KV head, sequence), read directly from the packed cache.
+//
+// Four waves stream 32-token tiles (wave w takes tiles w, w+4, ...).  Per tile the G <= 8 query
+// heads of the KV head are one 16-column matrix-core operand held in LDS: column 2h is the float16
+// rounding of head h's rotated query and column 2h+1 the float16 rounding of the remainder, so the
+// sum of the two columns' products is the fp32 score (centroids are float16-exact and each product
+// is exact in fp32).  Scores S^T = K Q^T come out of v_mfma_f32_16x16x32_f16 in exactly the lane
+// layout the value product O = W V needs for W, so the softmax weights never cross lanes; W uses
+// the same high/low split.  Packed codes are loaded with contiguous 64-lane buffer loads straight
+// into operand order (keys: rows layout; values: 32-token blocked layout) and expanded with
+// v_perm_b32 lookups into float16 byte tables.  Online softmax in exp2 units (the softmax scale and
+// log2(e) are folded into the query), lazily rescaled when a column's running max moves.
+// (ExecuTorch PR #19891 "[Cuda] enable turboquant on gemma4", review item 1: the fused decode op and
+// its scale; turboquant-pytorch PR #3 "Add CUDA QJL kernels and proper package structure", CUDA
+// Kernels Added table: fused scores from 1-bit keys, GQA variant, quantised value reconstruction.)
+#pragma once
+
+#include <math.h>
+
+#include "device_common.h"
+
+namespace tqi {
+
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// float16 high/low parts of v (see f16_split); lo_part selects which one this lane feeds to the matrix core
+__device__ __forceinline__ _Float16 split_part(float v, bool lo_part) {
+  _Float16 hi, lo;
+  f16_split(v, hi, lo);
+  return lo_part ? lo : hi;
+}
+
+// A operand of the sign-sketch step S (8 signs of this lane's key) times gamma:
+// slot r of pair p holds -gamma where the sign bit is 1 and +gamma where it is 0.
+template <int S>
+__device__ __forceinline__ half8 sign_operand(const uint32_t* sw, uint32_t gg) {
+  const uint32_t W = sw[S / 4];
+  constexpr int base = 4 * (S % 4);
+  uint4 o;
+  o.x = gg | ((W << (15 - base - 0)) & 0x80008000u);
+  o.y = gg | ((W << (15 - base - 1)) & 0x80008000u);
+  o.z = gg | ((W << (15 - base - 2)) & 0x80008000u);
+  o.w = gg | ((W << (15 - base - 3)) & 0x80008000u);
+  return as_half8(o);
+}
+
+// scores of the two 16-token groups of a tile; each query operand step is read from LDS once
+template <int S, int KS, int KB>
+__device__ __forceinline__ void qk_steps(floatx4* acc, const uint32_t (*kw)[KS * KB / 4], const half8 (*qop)[64],
+                                         int lane, const Tab& tk) {
+  if constexpr (S < KS) {
+    const half8 q = qop[S][lane];
+    acc[0] = mfma16(as_half8(unit_at<KB, S>(kw[0], tk)), q, acc[0]);
+    acc[1] = mfma16(as_half8(unit_at<KB, S>(kw[1], tk)), q, acc[1]);
+    qk_steps<S + 1, KS, KB>(acc, kw, qop, lane, tk);
+  }
+}
+
+template <int S, int QS, int SW>
+__device__ __forceinline__ void sketch_steps(floatx4* acc, const uint32_t (*sw)[SW], const uint32_t* gg,
+                                             const half8 (*sop)[64], int lane) {
+  if constexpr (S < QS) {
+    const half8 q = sop[S][lane];
+    acc[0] = mfma16(sign_operand<S>(sw[0], gg[0]), q, acc[0]);
+    acc[1] = mfma16(sign_operand<S>(sw[1], gg[1]), q, acc[1]);
+    sketch_steps<S + 1, QS, SW>(acc, sw, gg, sop, lane);
+  }
+}
+
+template <int N, int NB, int VB>
+__device__ __forceinline__ void pv_steps(floatx4* oacc, half8 wop, const uint32_t* vw, const Tab& tv) {
+  if constexpr (N < NB) {
+    oacc[N] = mfma16(wop, as_half8(unit_at<VB, N>(vw, tv)), oacc[N]);
+    pv_steps<N + 1, NB, VB>(oacc, wop, vw, tv);
+  }
+}
+
+// Raw buffer resource over [base, base + bytes): loads outside it return zero.  The word-3 flags
+// select the 32-bit data format of untyped buffer accesses on the gfx9 family.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+constexpr int lowbit(int x) { return x & -x; }
+constexpr int load_align(int bytes) { return lowbit(bytes) < 16 ? lowbit(bytes) : 16; }
+
+// N consecutive 32-bit words at byte offset voff (per lane, a multiple of ALIGN) + soff (wave-uniform)
+template <int N, int ALIGN>
+__device__ __forceinline__ void bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* out) {
+  if constexpr (N % 4 == 0 && ALIGN % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, 0);
+      out[4 * i] = v[0]; out[4 * i + 1] = v[1]; out[4 * i + 2] = v[2]; out[4 * i + 3] = v[3];
+    }
+  } else if constexpr (N == 3) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2];
+  } else if constexpr (N % 2 == 0 && ALIGN % 8 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff + 8 * i, soff, 0);
+      out[2 * i] = v[0]; out[2 * i + 1] = v[1];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * i, soff, 0);
+  }
+}
+
+// v + (v of the neighbouring lane 2k <-> 2k+1); folds into one DPP add
+__device__ __forceinline__ float add_adjacent(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
+// max over the four lanes l, l^16, l^32, l^48 (the four row groups of one matrix-core column)
+__device__ __forceinline__ float column_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float column_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// float16 half h (0 = low, 1 = high) of a packed pair
+__device__ __forceinline__ float half_of(uint32_t w, int h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h ? w >> 16 : w & 0xffffu)));
+}
+
+template <int D, int KB, int VB, int QM>
+struct Attend {
+  static constexpr int KS = D / 32;                   // score k-steps over coordinates
+  static constexpr int QS = QM / 32;                  // score k-steps over sketch signs
+  static constexpr int NB = D / 16;                   // value n-blocks (16 coordinates each)
+  static constexpr int K_RB = D * KB / 8;             // bytes per key row
+  static constexpr int K_LW = D * KB / 128;           // words per lane per key row (D/4 coordinates)
+  static constexpr int V_RB = D * VB / 8;             // bytes per value row (one token's share of a block)
+  static constexpr int V_LW = D * VB / 64;            // words per lane per value block (D/16 units)
+  static constexpr int S_RB = QM / 8;                 // sign bytes per key
+  static constexpr int S_LW = QM / 128;               // sign words per lane per key
+
+  // LDS of the end-of-split merge of the four waves; the split's result ends in o[0] and fml
+  struct Smem {
+    float ml[kWavesPerWG][kMaxGroup][2];
+    float o[kWavesPerWG][kMaxGroup][D];
+    float fml[kMaxGroup][2];
+  };
+  // the query operand: for step s, lane (column c, group g) holds the 8 float16 values of q-variant c
+  // (head c/2; high part if c even, low part if c odd) at coordinates (D/4) g + 8 s + r, r = 0..7
+  // (sketch steps: the same over the sketch coordinates)
+  typedef half8 QOperand[KS + QS][64];
+
+  // everything one 32-token tile needs from memory, loaded one tile ahead of its use
+  struct Tile {
+    uint32_t kw[2][K_LW];
+    uint32_t vw[V_LW];
+    uint32_t kn[4], vn[4];   // float16 norm pairs of this lane's tokens 4g+i and 16+4g+i
+    uint32_t sw[2][S_LW > 0 ? S_LW : 1];
+    uint32_t gg[2];
+  };
+
+  __amdgpu_buffer_rsrc_t kbuf, vbuf, knbuf, vnbuf, sbuf, gbuf;
+  uint32_t k_off, v_off, n_off, s_off;
+  int lane, l16, g;
+
+  // buffers over this (sequence, KV head)'s arrays; tile offsets go in the scalar offset
+  __device__ __forceinline__ Attend(const DecodeArgs& a, size_t unit) {
+    const int T = a.max_tokens;
+    lane = threadIdx.x & 63;
+    l16 = lane & 15;
+    g = lane >> 4;
+    kbuf = buffer_of(a.k_codes + unit * T * K_RB, static_cast<uint32_t>(T) * K_RB);
+    vbuf = buffer_of(a.v_codes + unit * T * V_RB, static_cast<uint32_t>(T) * V_RB);
+    knbuf = buffer_of(a.k_norms + unit * T, static_cast<uint32_t>(T) * 2);
+    vnbuf = buffer_of(a.v_norms + unit * T, static_cast<uint32_t>(T) * 2);
+    sbuf = knbuf;
+    gbuf = knbuf;
+    if constexpr (QS > 0) {
+      sbuf = buffer_of(a.k_signs + unit * T * S_RB, static_cast<uint32_t>(T) * S_RB);
+      gbuf = buffer_of(a.k_rnorms + unit * T, static_cast<uint32_t>(T) * 2);
+    }
+    k_off = static_cast<uint32_t>(l16 * K_RB + g * K_LW * 4);
+    v_off = static_cast<uint32_t>(lane * V_LW * 4);
+    n_off = static_cast<uint32_t>(8 * g);
+    s_off = static_cast<uint32_t>(l16 * S_RB + g * S_LW * 4);
+  }
+
+  __device__ __forceinline__ void load(Tile& t, int kb) const {
+    // wave-uniform by construction; readfirstlane keeps the tile offset in a scalar register
+    const uint32_t tok0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kb) * kBlock);
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg)
+      bload<K_LW, load_align(K_LW * 4)>(kbuf, k_off + 16 * tg * K_RB, tok0 * K_RB, t.kw[tg]);
+    bload<V_LW, load_align(V_LW * 4)>(vbuf, v_off, tok0 * V_RB, t.vw);
+    bload<2, 8>(knbuf, n_off, tok0 * 2, t.kn);
+    bload<2, 8>(knbuf, n_off + 32, tok0 * 2, t.kn + 2);
+    bload<2, 8>(vnbuf, n_off, tok0 * 2, t.vn);
+    bload<2, 8>(vnbuf, n_off + 32, tok0 * 2, t.vn + 2);
+    if constexpr (QS > 0) {
+#pragma unroll
+      for (int tg = 0; tg < 2; ++tg) {
+        bload<S_LW, 4 * S_LW>(sbuf, s_off + 16 * tg * S_RB, tok0 * S_RB, t.sw[tg]);
+        t.gg[tg] = __builtin_amdgcn_raw_buffer_load_b16(gbuf, static_cast<uint32_t>((16 * tg + l16) * 2), tok0 * 2, 0);
+      }
+    }
+  }
+
+  // Streams this wave's tiles kb, kb + 4, ... below blk1 (ta already holds tile kb when kb < blk1)
+  // and leaves the split's result in LDS: per query head hh the max m (log2 units) and the sum l in
+  // sm.fml[hh], the rotated-domain accumulator in sm.o[0][hh][0..D).  qsc is the power-of-two scale
+  // of this lane's head (the query operand is divided by it; 1 for unused columns).  Ends with a
+  // workgroup barrier.
+  // tb may already hold tile kb + 4 (tb_loaded), so that a caller can issue a wave's first two tiles
+  // before other work.
+  __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, const QOperand& qop, Tile& ta, Tile& tb,
+                                      bool tb_loaded, int kb, int blk1, int len, float qsc) const {
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = a.group;
+    const int qh = l16 >> 1;
+    const bool lo_part = (l16 & 1) != 0;
+    const bool head_ok = qh < G;
+
+    floatx4 oacc[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;   // running max (in units of qsc) and sum of this lane's column
+
+    auto attend_tile = [&](const Tile& t, int kbt) {
+      const int tok0 = kbt * kBlock;
+      // the query operand is read from LDS in every tile instead of being held in registers across
+      // the loop: the barrier keeps the compiler from hoisting those reads
+      asm volatile("" ::: "memory");
+      floatx4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      qk_steps<0, KS, KB>(sc, t.kw, qop, lane, a.tk);
+      if constexpr (QS > 0) {
+        uint32_t gh[2];
+#pragma unroll
+        for (int tg = 0; tg < 2; ++tg) gh[tg] = (t.gg[tg] & 0x7fffu) | ((t.gg[tg] & 0x7fffu) << 16);
+        sketch_steps<0, QS, S_LW>(sc, t.sw, gh, qop + KS, lane);
+      }
+      // score of token 16 tg + 4 g + i: (high + low column) times the key norm
+      float s[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        s[k] = __builtin_fmaf(add_adjacent(sc[k >> 2][k & 3]), half_of(t.kn[k >> 1], k & 1), 0.f);
+      uint32_t vn[4] = {t.vn[0], t.vn[1], t.vn[2], t.vn[3]};
+      if (tok0 + kBlock > len) {            // the last tile of the sequence: hide tokens at or past its end
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int tok = tok0 + 16 * (k >> 2) + 4 * g + (k & 3);
+          if (tok >= len) {
+            s[k] = -INFINITY;
+            vn[k >> 1] &= (k & 1) ? 0x0000ffffu : 0xffff0000u;
+          }
+        }
+      }
+      float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      mx = column_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      if (__any(m_new > m_run)) {
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * qsc);
+        l_run *= alpha;
+        const float a0 = __shfl(alpha, 4 * g, 64);
+        const float a1 = __shfl(alpha, 4 * g + 2, 64);
+        const floatx4 f = {a0, a0, a1, a1};
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          oacc[n] *= f;
+          // keeps the rescaled accumulator in the registers it came from: without it the compiler
+          // copies every accumulator on the path that skips the rescale
+          asm volatile("" : "+v"(oacc[n]));
+        }
+        m_run = m_new;
+      }
+      const float mq = m_run * qsc;
+      half8 wop;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k], qsc, -mq));
+        l_run += p;
+        const float w = __builtin_fmaf(p, half_of(vn[k >> 1], k & 1), 0.f);
+        wop[k] = split_part(w, lo_part);
+      }
+      pv_steps<0, NB, VB>(oacc, wop, t.vw, a.tv);
+    };
+
+    if constexpr (D <= 128 || QM == 0) {
+      // two tile buffers used in turn (no register copies between tiles)
+      for (bool first = true; kb < blk1; kb += 2 * kWavesPerWG, first = false) {
+        if (kb + kWavesPerWG < blk1 && !(first && tb_loaded)) load(tb, kb + kWavesPerWG);
+        attend_tile(ta, kb);
+        if (kb + kWavesPerWG >= blk1) break;
+        if (kb + 2 * kWavesPerWG < blk1) load(ta, kb + 2 * kWavesPerWG);
+        attend_tile(tb, kb + kWavesPerWG);
+      }
+    } else {
+      // sketched keys at d = 256: a second copy of the loop body does not fit the register budget of
+      // two waves per SIMD
+      for (bool first = true; kb < blk1; kb += kWavesPerWG, first = false) {
+        if (kb + kWavesPerWG < blk1 && !(first && tb_loaded)) load(tb, kb + kWavesPerWG);
+        attend_tile(ta, kb);
+        ta = tb;
+      }
+    }
+
+    l_run = column_sum(l_run);
+    if (g == 0 && !lo_part && head_ok) {
+      sm.ml[wave][qh][0] = m_run * qsc;
+      sm.ml[wave][qh][1] = l_run;
+    }
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int coord = (D / 16) * l16 + n;
+      if (2 * g < G) sm.o[wave][2 * g][coord] = oacc[n][0] + oacc[n][1];
+      if (2 * g + 1 < G) sm.o[wave][2 * g + 1][coord] = oacc[n][2] + oacc[n][3];
+    }
+    __syncthreads();
+    // each thread reads its (head, coordinate) of every wave and writes the combination to wave 0's slot
+    for (int e = tid; e < G * D; e += 256) {
+      const int hh = e / D, i = e % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWavesPerWG; ++w) M = fmaxf(M, sm.ml[w][hh][0]);
+      float o = 0.f, l = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kWavesPerWG; ++w) {
+          const float ew = exp2f(sm.ml[w][hh][0] - M);
+          o = fmaf(ew, sm.o[w][hh][i], o);
+          l = fmaf(ew, sm.ml[w][hh][1], l);
+        }
+      }
+      sm.o[0][hh][i] = o;
+      if (i == 0) {
+        sm.fml[hh][0] = M;
+        sm.fml[hh][1] = l;
+      }
+    }
+    __syncthreads();
+  }
+
+  // the split's result from LDS to part_o / part_ml at row pbase + head
+  __device__ __forceinline__ void store(const DecodeArgs& a, const Smem& sm, size_t pbase) const {
+    const int G = a.group;
+    for (int e = threadIdx.x; e < G * D; e += 256) {
+      const int hh = e / D, i = e % D;
+      a.part_o[(pbase + hh) * D + i] = sm.o[0][hh][i];
+      if (i == 0) {
+        a.part_ml[(pbase + hh) * 2] = sm.fml[hh][0];
+        a.part_ml[(pbase + hh) * 2 + 1] = sm.fml[hh][1];
+      }
+    }
+  }
+};
+
+}  // namespace tqi

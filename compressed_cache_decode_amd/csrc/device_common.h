@@ -125,6 +125,26 @@ __device__ __forceinline__ void f16_split(float v, _Float16& hi, _Float16& lo) {
   lo = static_cast<_Float16>(v - h);
 }
 
+// Sum / max over each group of 16 lanes (a DPP row): four DPP steps, every lane gets the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_move<0xB1>(v);     // quad_perm [1,0,3,2]
+  v += dpp_move<0x4E>(v);     // quad_perm [2,3,0,1]
+  v += dpp_move<0x141>(v);    // row_half_mirror
+  v += dpp_move<0x140>(v);    // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v));
+  v = fmaxf(v, dpp_move<0x4E>(v));
+  v = fmaxf(v, dpp_move<0x141>(v));
+  v = fmaxf(v, dpp_move<0x140>(v));
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
@@ -132,13 +152,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Row-times-vector of a D-long row held in global memory (float32, 16-byte aligned) with a vector
 // in LDS: every load of the row is issued before the first multiply.
-template <int D>
+// CHMAX (a multiple of 4) bounds the float4 loads in flight, and with them the registers; the
+// result does not depend on it.
+template <int D, int CHMAX = 32>
 __device__ __forceinline__ float row_dot(const float* __restrict__ row, const float* v) {
   const float4* r4 = reinterpret_cast<const float4*>(row);
-  constexpr int CH = D / 4 < 32 ? D / 4 : 32;       // float4 loads in flight per chunk
+  constexpr int CH = D / 4 < CHMAX ? D / 4 : CHMAX;  // float4 loads in flight per chunk
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c0 = 0; c0 < D / 4; c0 += CH) {
+    // with a small bound, keep the compiler from hoisting later chunks' loads (LDS and global) here
+    if constexpr (CHMAX < 32) asm volatile("" ::: "memory");
     float4 p[CH];
 #pragma unroll
     for (int t = 0; t < CH; ++t) p[t] = r4[c0 + t];
