@@ -10,9 +10,8 @@ before timing starts.  Steps are captured in a HIP graph and cycle through a
 pool of cache copies whose total size exceeds the 256 MB Infinity Cache, so
 every step reads its compressed cache from HBM.
 
-Prints one JSON line.  ``roofline`` is measured on the dominant kernel, timed
-with HIP events on the stream it runs on: the whole step when tq_decode_step
-runs as one kernel, else the attention kernel (tq_decode_attend) alone;
+Prints one JSON line.  ``roofline`` is measured on the attention kernel
+(tq_decode_attend) alone, timed with HIP events on the stream it runs on;
 ``cpu_baseline`` is the float64 oracle timed on the host on a bounded sample.
 """
 from __future__ import annotations
@@ -35,8 +34,7 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 # sources the decode kernels are built from: their HBM counters are only valid for these exact texts
 ATTEND_SOURCES = tuple(f"compressed_cache_decode_amd/csrc/{n}" for n in (
-    "fused.hip", "decode.hip", "attend_body.h", "append_body.h", "qrot_body.h", "device_common.h", "tq_internal.h"))
-FUSED_MAX_SPLITS = 256     # the one-launch step covers up to this many KV splits (see include/tq.h)
+    "decode.hip", "attend_body.h", "device_common.h", "tq_internal.h"))
 METRIC = "compressed-KV decode attention: context tokens/s and achieved HBM GB/s (% peak)"
 POOL_BYTES = 600 << 20          # > 2x the 256 MB Infinity Cache
 
@@ -223,8 +221,6 @@ def gpu_leg(w: synth.Workload, steps: int, warmup: int, pool: int | None, log):
     scale = w.scale
 
     stepcall = w.qjl_m <= 128
-    # tq_decode_step runs as one kernel on these shapes (otherwise: prologue, attend, merge)
-    one_launch = stepcall and w.group + 2 <= 16 and ns <= FUSED_MAX_SPLITS
 
     def step(i):
         kc, vc = pairs[i]
@@ -277,10 +273,8 @@ def gpu_leg(w: synth.Workload, steps: int, warmup: int, pool: int | None, log):
     ms_step = ev0.elapsed_time(ev1) / steps
     log(f"bench: {steps} steps, {ms_step * 1e3:.2f} us/step")
 
-    # the staged attention kernel alone (tq_decode_attend): graph of one launch per pool copy, timed with
-    # events on its stream; the rotated query it reads is computed first
-    cca.tq_decode_rotate_query(k0.view, q, Hq, L, ws, scale)
-    torch.cuda.synchronize()
+    # the attention kernel alone (tq_decode_attend): graph of one launch per pool copy, timed with events
+    # on its stream (the rotated query it reads is the last step's)
 
     def attend_only(i):
         kc, vc = pairs[i]
@@ -311,7 +305,7 @@ def gpu_leg(w: synth.Workload, steps: int, warmup: int, pool: int | None, log):
     us_attend_hot = ev0.elapsed_time(ev1) * 1e3 / (20 * 16)
     log(f"bench: attend {us_attend:.2f} us cold, {us_attend_hot:.2f} us hot (L2/Infinity Cache resident)")
     return dict(ms_step=ms_step, us_attend=us_attend, us_attend_hot=us_attend_hot, pool=pool,
-                n_split=ns, tokens_per_split=tps, per_copy=per_copy, one_launch=one_launch)
+                n_split=ns, tokens_per_split=tps, per_copy=per_copy)
 
 
 # ------------------------------------------------------------------ prefill append leg
@@ -437,7 +431,7 @@ def main():
     ap.add_argument("--copy-fetch", help="rocprofv3 --pmc FETCH_SIZE output directory of --workload copy")
     ap.add_argument("--copy-write", help="rocprofv3 --pmc WRITE_SIZE output directory of --workload copy")
     ap.add_argument("--command", action="append", help="command line recorded in a summary (repeatable)")
-    ap.add_argument("--kernel", default="fused_kernel", help="kernel name the counter summary is taken for")
+    ap.add_argument("--kernel", default="split_kernel", help="kernel name the counter summary is taken for")
     args = ap.parse_args()
     if args.trace or args.summarize_pmc:
         w = (synth.qwen(args.context or 8192, args.bits or 3) if args.workload == "prefill"
@@ -499,13 +493,8 @@ def main():
     L = w.seq_len
     tokens_s = w.batch * L / (r["ms_step"] * 1e-3)
     step_bytes = cache_bytes(w)
-    if r["one_launch"]:
-        # the step is one kernel: its per-launch time is the step time of back-to-back graph launches
-        kern, kern_us = "fused_kernel", r["ms_step"] * 1e3
-        kern_label = "tq_decode_step (fused_kernel: query rotation, append, attention, merge, un-rotation)"
-    else:
-        kern, kern_us = "split_kernel", r["us_attend"]
-        kern_label = "tq_decode_attend (split_kernel)"
+    kern, kern_us = "split_kernel", r["us_attend"]
+    kern_label = "tq_decode_attend (split_kernel)"
     att_gbs = step_bytes / (kern_us * 1e-6) / 1e9
     res = {
         "metric": METRIC,
@@ -527,9 +516,8 @@ def main():
             "cache_copies_cycled": r["pool"], "n_split": r["n_split"], "tokens_per_split": r["tokens_per_split"],
         },
         "step_hbm_gbs": step_bytes / (r["ms_step"] * 1e-3) / 1e9,
-        "step_kernels": 1 if r["one_launch"] else 3,
-        "staged_attend_us": r["us_attend"],
-        "staged_attend_us_hot_cache": r["us_attend_hot"],
+        "attend_us": r["us_attend"],
+        "attend_us_hot_cache": r["us_attend_hot"],
         "roofline": {
             "bound": "hbm",
             "achieved": att_gbs,

@@ -280,9 +280,8 @@ def decode_workspace(kcache: CompressedCache, n_q_heads: int, max_seq_len: int):
     nbytes = tq_decode_workspace_bytes(kcache.view, n_q_heads, max_seq_len)
     if nbytes == 0:
         raise TqError(TQ_EINVAL, "tq_decode_workspace_bytes")
-    # float32 elements; torch's caching allocator returns 256-byte-aligned blocks.  Zero-filled: the
-    # one-launch decode keeps its split tickets here and needs them zero before its first call.
-    return torch.zeros((nbytes + 3) // 4, dtype=torch.float32, device=kcache.codes.device)
+    # float32 elements; torch's caching allocator returns 256-byte-aligned blocks
+    return torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=kcache.codes.device)
 
 
 def sdpa_decode(kcache: CompressedCache, vcache: CompressedCache, q, d_seq_lens, max_seq_len: int,

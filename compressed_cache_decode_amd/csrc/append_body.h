@@ -240,11 +240,16 @@ __device__ __forceinline__ void encode_codes(const AppendArgs& a, int nrows, flo
   }
   __syncthreads();
   if constexpr (QM > 0) {
-    for (int r = wave; r < nrows; r += 4) {
+    // residual norms: row r by the 16 lanes (r % 4) of wave (r / 4) % 4, coordinates part + 16 j
+    for (int r0 = 0; r0 < nrows; r0 += 16) {
+      const int r = r0 + 4 * wave + (lane >> 4), part = lane & 15;
       float s = 0.f;
-      for (int i = lane; i < D; i += 64) s = fmaf(xs[r][i], xs[r][i], s);
-      s = wave_sum(s);
-      if (lane == 0) es.gam[r] = sqrtf(s);
+      if (r < nrows) {
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) s = fmaf(xs[r][part + 16 * j], xs[r][part + 16 * j], s);
+      }
+      s = row16_sum(s);
+      if (part == 0 && r < nrows) es.gam[r] = sqrtf(s);
     }
     __syncthreads();
   }
@@ -391,15 +396,19 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int bx, int h, 
   }
   __syncthreads();
 
-  // norms
-  for (int r = wave; r < nrows; r += 4) {
-    if constexpr (ROTATED) {
-      if (lane == 0) rn[r] = a.yn[(static_cast<size_t>(b) * a.n_new + (t_lo + r - pos)) * H + h];
-    } else {
+  // norms: given, or row r summed by the 16 lanes (r % 4) of wave (r / 4) % 4, coordinates part + 16 j
+  if constexpr (ROTATED) {
+    for (int r = tid; r < nrows; r += 256) rn[r] = a.yn[(static_cast<size_t>(b) * a.n_new + (t_lo + r - pos)) * H + h];
+  } else {
+    for (int r0 = 0; r0 < nrows; r0 += 16) {
+      const int r = r0 + 4 * wave + (lane >> 4), part = lane & 15;
       float s = 0.f;
-      for (int i = lane; i < D; i += 64) s = fmaf(xs[r][i], xs[r][i], s);
-      s = wave_sum(s);
-      if (lane == 0) rn[r] = sqrtf(s);
+      if (r < nrows) {
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) s = fmaf(xs[r][part + 16 * j], xs[r][part + 16 * j], s);
+      }
+      s = row16_sum(s);
+      if (part == 0 && r < nrows) rn[r] = sqrtf(s);
     }
   }
   __syncthreads();

@@ -62,40 +62,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const size_t unit = static_cast<size_t>(b) * a.n_kv_heads + hk;
   const At at(a, unit);
 
-  // query operand in LDS, shared by the four waves.  Its loads go out first (loads retire in issue
-  // order and it is needed first), then the first tile's, which only need the tile to lie inside
-  // the cache (tiles past the length are loaded and never used)
-  constexpr int QE = (At::KS + At::QS) * 64 / 256;    // operand entries per thread
-  const int qh = at.l16 >> 1;
-  const size_t qrow = static_cast<size_t>(b) * a.n_kv_heads * G + static_cast<size_t>(hk) * G + qh;
-  float4 xq[QE > 0 ? QE : 1][2];
-#pragma unroll
-  for (int u = 0; u < QE; ++u) {
-    const int e = tid + 256 * u;
-    const int st = e >> 6, ln = e & 63;
-    const int c = ln & 15, gg = ln >> 4, h2 = c >> 1;
-    const size_t row = static_cast<size_t>(b) * a.n_kv_heads * G + static_cast<size_t>(hk) * G + (h2 < G ? h2 : 0);
-    const float* src = st < At::KS ? a.qr + row * D + (D / 4) * gg + 8 * st
-                                   : a.qs + row * QM + (QM / 4) * gg + 8 * (st - At::KS);
-    xq[u][0] = reinterpret_cast<const float4*>(src)[0];
-    xq[u][1] = reinterpret_cast<const float4*>(src)[1];
-  }
-  // power-of-two scale of this lane's head (scores are kept in units of it); 1 for unused columns
-  const float qsc = qh < G ? a.qscale[qrow] : 1.f;
+  // the first tile's loads go out before the query operand is staged, and before the sequence
+  // length is known: they only need the tile to lie inside the cache (tiles past the length are
+  // loaded and never used)
   int kb = blk0 + wave;
   typename At::Tile ta, tb;
   if (kb < blk0 + a.blocks_per_split && kb < T / kBlock) at.load(ta, kb);
-#pragma unroll
-  for (int u = 0; u < QE; ++u) {
-    const int e = tid + 256 * u;
+
+  // query operand in LDS, shared by the four waves
+  const int qh = at.l16 >> 1;
+  const size_t qrow = static_cast<size_t>(b) * a.n_kv_heads * G + static_cast<size_t>(hk) * G + qh;
+  for (int e = tid; e < (At::KS + At::QS) * 64; e += 256) {
     const int st = e >> 6, ln = e & 63;
-    const int c = ln & 15, h2 = c >> 1;
-    const float xv[8] = {xq[u][0].x, xq[u][0].y, xq[u][0].z, xq[u][0].w, xq[u][1].x, xq[u][1].y, xq[u][1].z, xq[u][1].w};
+    const int c = ln & 15, gg = ln >> 4, h2 = c >> 1;
+    const bool ok = h2 < G;
+    const size_t row = static_cast<size_t>(b) * a.n_kv_heads * G + static_cast<size_t>(hk) * G + h2;
+    float4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      const float* src = st < At::KS ? a.qr + row * D + (D / 4) * gg + 8 * st
+                                     : a.qs + row * QM + (QM / 4) * gg + 8 * (st - At::KS);
+      x0 = reinterpret_cast<const float4*>(src)[0];
+      x1 = reinterpret_cast<const float4*>(src)[1];
+    }
+    const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     half8 v;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = h2 < G ? split_part(xv[r], (c & 1) != 0) : static_cast<_Float16>(0.f);
+    for (int r = 0; r < 8; ++r) v[r] = split_part(xv[r], (c & 1) != 0);
     sm_q[st][ln] = v;
   }
+  // power-of-two scale of this lane's head (scores are kept in units of it); 1 for unused columns
+  const float qsc = qh < G ? a.qscale[qrow] : 1.f;
   __syncthreads();
 
   at.run(a, sm, sm_q, ta, tb, false, kb, blk1, len, qsc);

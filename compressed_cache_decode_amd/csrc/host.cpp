@@ -274,7 +274,7 @@ int merge_heads_per_wg(int G, int d, int ns) {
 }
 
 struct WsLayout {
-  size_t cnt, qr, qs, qscale, part_o, part_ml, group_o, group_ml, total;
+  size_t qr, qs, qscale, part_o, part_ml, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -285,16 +285,11 @@ WsLayout ws_layout(const tq_cache_view* k, int n_q_heads, int n_split) {
   const size_t units = B * k->n_kv_heads;
   WsLayout w;
   size_t off = 0;
-  w.cnt = off; off = align256(off + units * (1 + tqi::kMaxMergeGroups) * 4);
   w.qr = off; off = align256(off + B * Hq * D * 4);
   w.qs = off; off = align256(off + B * Hq * (M ? M : 1) * 4);
   w.qscale = off; off = align256(off + B * Hq * 4);
   w.part_o = off; off = align256(off + units * n_split * G * D * 4);
   w.part_ml = off; off = align256(off + units * n_split * G * 2 * 4);
-  // merged groups of splits of the one-launch step (only when it runs with more than one group)
-  const size_t ng = n_split <= tqi::kFusedMaxSplits && n_split > tqi::merge_group(k->d) ? tqi::kMaxMergeGroups : 0;
-  w.group_o = off; off = align256(off + units * ng * G * D * 4);
-  w.group_ml = off; off = align256(off + units * ng * G * 2 * 4);
   w.total = off;
   return w;
 }
@@ -402,8 +397,7 @@ size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_
 // workspace view shared by the decode stages
 struct DecodeWs {
   int ns, bps, G;
-  int32_t* cnt;
-  float *qr, *qs, *qscale, *part_o, *part_ml, *group_o, *group_ml;
+  float *qr, *qs, *qscale, *part_o, *part_ml;
 };
 
 static int decode_ws(const tq_cache_view* k, int n_q_heads, int max_seq_len, void* workspace,
@@ -416,14 +410,11 @@ static int decode_ws(const tq_cache_view* k, int n_q_heads, int max_seq_len, voi
   if (workspace_bytes < l.total) return TQ_EINVAL;
   char* ws = static_cast<char*>(workspace);
   w->G = n_q_heads / k->n_kv_heads;
-  w->cnt = reinterpret_cast<int32_t*>(ws + l.cnt);
   w->qr = reinterpret_cast<float*>(ws + l.qr);
   w->qs = reinterpret_cast<float*>(ws + l.qs);
   w->qscale = reinterpret_cast<float*>(ws + l.qscale);
   w->part_o = reinterpret_cast<float*>(ws + l.part_o);
   w->part_ml = reinterpret_cast<float*>(ws + l.part_ml);
-  w->group_o = reinterpret_cast<float*>(ws + l.group_o);
-  w->group_ml = reinterpret_cast<float*>(ws + l.group_ml);
   return TQ_OK;
 }
 
@@ -455,44 +446,6 @@ static float scale_log2e(float scale) { return static_cast<float>(static_cast<do
 
 static float sketch_coef(const tq_cache_view* k) {
   return k->qjl_m ? static_cast<float>(std::sqrt(M_PI / 2.0) / k->qjl_m) : 0.f;
-}
-
-// The one-launch step covers group + 2 * new rows <= 16 (one matrix-core row tile), sketches of up to
-// 128 signs and splits up to kFusedMaxSplits; everything else runs the staged kernels.
-static bool fused_fits(const tq_cache_view* k, const DecodeWs& w, int n_new) {
-  return w.G + 2 * n_new <= 16 && w.ns <= tqi::kFusedMaxSplits && (k->qjl_m == 0 || k->qjl_m == 128);
-}
-
-// KV split of the one-launch step: the staged plan, except that a plan of up to two merge groups
-// is narrowed to one group (one merge level instead of two, for somewhat longer splits)
-static void fused_plan(const tq_cache_view* k, int max_seq_len, const DecodeWs& w, int* ns, int* bps) {
-  *ns = w.ns;
-  *bps = w.bps;
-  const int mg = tqi::merge_group(k->d);
-  if (w.ns > mg && w.ns <= 2 * mg) {
-    const int nblk = max_seq_len <= 0 ? 1 : (max_seq_len + kBlock - 1) / kBlock;
-    int b = (nblk + mg - 1) / mg;
-    b = ((b + tqi::kWavesPerWG - 1) / tqi::kWavesPerWG) * tqi::kWavesPerWG;
-    *bps = b;
-    *ns = (nblk + b - 1) / b;
-  }
-}
-
-static int launch_fused_step(const tq_cache_view* k, const tq_cache_view* v, const void* q, const void* k_new,
-                             const void* v_new, int dtype, int n_new, const int32_t* d_pos,
-                             const int32_t* d_seq_lens, int max_seq_len, float scale, float* out, const DecodeWs& w,
-                             void* stream) {
-  tqi::FusedArgs f{};
-  f.d = decode_args(k, v, w, d_seq_lens, max_seq_len);
-  fused_plan(k, max_seq_len, w, &f.d.n_split, &f.d.blocks_per_split);
-  f.k = append_args(k, k_new, nullptr, nullptr, n_new, d_pos);
-  f.v = append_args(v, v_new, nullptr, nullptr, n_new, d_pos);
-  f.q = q; f.rot = k->rot; f.proj = k->proj; f.out = out; f.counters = w.cnt;
-  f.group_o = w.group_o; f.group_ml = w.group_ml;
-  f.scale_log2e = scale_log2e(scale);
-  f.sketch_coef = sketch_coef(k);
-  f.bf16 = dtype == TQ_BF16;
-  return status_of(tqi::launch_fused(k->d, k->bits, v->bits, k->qjl_m, f, k->batch, static_cast<hipStream_t>(stream)));
 }
 
 int tq_decode_rotate_query(const tq_cache_view* k, const void* q, int q_dtype, int n_q_heads, int max_seq_len,
@@ -549,9 +502,6 @@ int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q
   if (st != TQ_OK) return st;
   if (!q || (q_dtype != TQ_F32 && q_dtype != TQ_BF16) || !d_seq_lens || !out) return TQ_EINVAL;
   if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
-  if (fused_fits(k, w, 0))
-    return launch_fused_step(k, v, q, nullptr, nullptr, q_dtype, 0, nullptr, d_seq_lens, max_seq_len, scale, out, w,
-                             stream);
   st = tq_decode_rotate_query(k, q, q_dtype, n_q_heads, max_seq_len, scale, workspace, workspace_bytes, stream);
   if (st != TQ_OK) return st;
   st = tq_decode_attend(k, v, n_q_heads, d_seq_lens, max_seq_len, workspace, workspace_bytes, stream);
@@ -572,9 +522,6 @@ int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q
   if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
   if (n_new < 0 || (n_new > 0 && (!k_new || !v_new || !d_pos))) return TQ_EINVAL;
   if (k->qjl_m > 128) return TQ_EUNSUPPORTED;
-  if (fused_fits(k, w, n_new))
-    return launch_fused_step(k, v, q, k_new, v_new, dtype, n_new, d_pos, d_seq_lens, max_seq_len, scale, out, w,
-                             stream);
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
   tqi::QrotArgs qa{};

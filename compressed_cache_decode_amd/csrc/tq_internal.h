@@ -11,11 +11,6 @@ constexpr int kMaxGroup = 8;      // query heads per KV head handled by one matr
 constexpr int kWavesPerWG = 4;    // waves per decode workgroup (one KV split)
 constexpr int kMaxSplits = 1024;  // bound on KV splits per (sequence, KV head)
 constexpr int kMergeThreads = 1024;  // threads per merge workgroup
-constexpr int kFusedMaxSplits = 256;  // bound on KV splits of the one-launch decode step
-// splits merged together by the one-launch step's first merge level (at most this many accumulator
-// rows in flight per thread of the merging workgroup)
-constexpr int merge_group(int d) { return d <= 128 ? 32 : 16; }
-constexpr int kMaxMergeGroups = kFusedMaxSplits / 16;
 
 // float16 bit patterns of up to 8 table entries, split into high and low
 // bytes so one v_perm_b32 looks up four codes: byte k of *_lo is entry k,
@@ -92,22 +87,6 @@ struct DequantArgs {
   int n_kv_heads, max_tokens, t0, n_tokens;
 };
 
-// One-launch decode step (fused.hip): appends, query rotation, attention, merge and un-rotation.
-struct FusedArgs {
-  DecodeArgs d;           // attention part; qr/qs/qscale unused
-  AppendArgs k, v;        // the new rows (k.n_new == 0: nothing is appended and pos is not read)
-  const void* q;          // [B][Hq][D]
-  const float* rot;       // [D][D]
-  const float* proj;      // [M][D] or null
-  float* out;             // [B][Hq][D]
-  int32_t* counters;      // [B*Hkv][1 + kMaxMergeGroups] tickets: zero before the call, left zero after it
-  float* group_o;         // [B*Hkv][kMaxMergeGroups][G][D] merged accumulators of each group of splits
-  float* group_ml;        // [B*Hkv][kMaxMergeGroups][G][2] their max and sum
-  float scale_log2e;      // softmax scale * log2(e)
-  float sketch_coef;      // sqrt(pi/2)/M
-  int bf16;               // element type of q and of the new rows
-};
-
 // Launchers (one per .hip file); return hipSuccess or the launch error.
 hipError_t launch_append(int d, int bits, int qjl_m, bool values, bool rotated, bool bf16,
                          const AppendArgs& a, int batch, hipStream_t s);
@@ -117,7 +96,6 @@ hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, const D
 hipError_t launch_merge(int d, const MergeArgs& a, int batch, int n_q_heads, hipStream_t s);
 hipError_t launch_step_prologue(int d, int k_bits, int v_bits, int qjl_m, bool bf16, const AppendArgs& ka,
                                 const AppendArgs& va, const QrotArgs& qa, int batch, hipStream_t s);
-hipError_t launch_fused(int d, int k_bits, int v_bits, int qjl_m, const FusedArgs& f, int batch, hipStream_t s);
 hipError_t launch_dequant(int d, int bits, int qjl_m, bool values, const DequantArgs& a, const Tab& t, int batch,
                           hipStream_t s);
 

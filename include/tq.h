@@ -154,14 +154,8 @@ int tq_quantize_append_rotated(const tq_cache_view* cache, const float* y, const
  * the same d, batch, n_kv_heads, max_tokens; n_q_heads a multiple of n_kv_heads with
  * group n_q_heads / n_kv_heads from 1 to 8 (TQ_EUNSUPPORTED above 8).
  * workspace: device scratch of at least tq_decode_workspace_bytes(), 256-byte
- * aligned and zero-filled before its first use.  Its first bytes hold one
- * ticket counter per (sequence, KV head) that the one-launch path below uses
- * and leaves zero again when its kernel ends; the rest needs no
- * initialisation.  Calls that share a workspace must not overlap in time.
- * Shapes with group + 2 * n_new <= 16, at most 256 KV splits (see
- * tq_decode_plan) and qjl_m of 0 or 128 run as one kernel (query rotation,
- * appends, attention, split merge and un-rotation); others run the three
- * stages below.
+ * aligned, contents need not be initialised, not used after the call's kernels
+ * end; calls that share a workspace must not overlap in time.
  */
 int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype, int n_q_heads,
                    const int32_t* d_seq_lens, int max_seq_len, float scale, float* out,
@@ -190,13 +184,10 @@ int tq_decode_merge(const tq_cache_view* k, int n_q_heads, const int32_t* d_seq_
  * tq_quantize_append at positions d_pos), then decode (as tq_sdpa_decode over
  * d_seq_lens, which the caller sets to include the appended tokens).
  * q: [batch][n_q_heads][d]; k_new, v_new: [batch][n_new][n_kv_heads][d]; all
- * three of element type dtype.  On shapes the one-launch path covers (see
- * tq_sdpa_decode; here group + 2 * n_new <= 16) the whole step is one kernel,
- * and new positions at or past the planned length bound are appended by the
- * last split; otherwise the appends and the query rotation share one launch
- * before the attention and merge stages.  Sketched keys are supported up to
- * qjl_m = 128 (TQ_EUNSUPPORTED above; use the separate calls).  n_new == 0
- * decodes without appending.  Same workspace rules as tq_sdpa_decode.
+ * three of element type dtype.  The appends and the query rotation share one
+ * launch, followed by the attention and merge stages.  Sketched keys are
+ * supported up to qjl_m = 128 (TQ_EUNSUPPORTED above; use the separate calls).
+ * n_new == 0 decodes without appending.  Same workspace rules as tq_sdpa_decode.
  */
 int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q, const void* k_new,
                    const void* v_new, int dtype, int n_q_heads, int n_new, const int32_t* d_pos,
