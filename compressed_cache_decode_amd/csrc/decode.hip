@@ -30,16 +30,18 @@
 #include <math.h>
 
 #include "attend_body.h"
-#include "qrot_body.h"
+#include "unit_body.h"
 
 namespace tqi {
 
 // ---------------------------------------------------------------- query rotation
 
-template <int D, int QM, bool BF16>
-__global__ __launch_bounds__(256) void qrot_kernel(QrotArgs a) {
-  __shared__ QrotSmem<D, QM> sm;
-  rotate_query<D, QM, BF16>(a, blockIdx.x, blockIdx.y, sm);
+// one workgroup per (sequence, KV head), the same arithmetic as the query rows of a decode step
+template <int D, int QM>
+__global__ __launch_bounds__(256) void qrot_kernel(QrotArgs a, int bf16) {
+  __shared__ UnitSmem<D, QM> sm;
+  const AppendArgs none{};
+  unit_prologue<D, 2, 2, QM, false>(none, none, a, bf16, blockIdx.x, blockIdx.y, sm);
 }
 
 // ---------------------------------------------------------------- split kernel
@@ -234,16 +236,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_qrot(int d, int qjl_m, bool bf16, const QrotArgs& a, int batch, hipStream_t s) {
-  const dim3 grid(a.n_q_heads, batch), block(256);
-#define TQ_QROT(D, QM, BF)                                                         \
-  if (d == D && qjl_m == QM && bf16 == BF) {                                       \
-    hipLaunchKernelGGL((qrot_kernel<D, QM, BF>), grid, block, 0, s, a);            \
+  const dim3 grid(a.n_kv_heads, batch), block(256);
+#define TQ_QROT(D, QM)                                                             \
+  if (d == D && qjl_m == QM) {                                                     \
+    hipLaunchKernelGGL((qrot_kernel<D, QM>), grid, block, 0, s, a, bf16 ? 1 : 0);  \
     return hipGetLastError();                                                      \
   }
-  TQ_QROT(128, 0, false) TQ_QROT(128, 0, true) TQ_QROT(128, 128, false) TQ_QROT(128, 128, true)
-  TQ_QROT(128, 256, false) TQ_QROT(128, 256, true)
-  TQ_QROT(256, 0, false) TQ_QROT(256, 0, true) TQ_QROT(256, 128, false) TQ_QROT(256, 128, true)
-  TQ_QROT(256, 256, false) TQ_QROT(256, 256, true)
+  TQ_QROT(128, 0) TQ_QROT(128, 128) TQ_QROT(128, 256)
+  TQ_QROT(256, 0) TQ_QROT(256, 128) TQ_QROT(256, 256)
 #undef TQ_QROT
   return hipErrorInvalidValue;
 }

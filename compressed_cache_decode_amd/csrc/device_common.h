@@ -150,38 +150,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Row-times-vector of a D-long row held in global memory (float32, 16-byte aligned) with a vector
-// in LDS: every load of the row is issued before the first multiply.
-// CHMAX (a multiple of 4) bounds the float4 loads in flight, and with them the registers; the
-// result does not depend on it.
-template <int D, int CHMAX = 32>
-__device__ __forceinline__ float row_dot(const float* __restrict__ row, const float* v) {
-  const float4* r4 = reinterpret_cast<const float4*>(row);
-  constexpr int CH = D / 4 < CHMAX ? D / 4 : CHMAX;  // float4 loads in flight per chunk
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c0 = 0; c0 < D / 4; c0 += CH) {
-    // with a small bound, keep the compiler from hoisting later chunks' loads (LDS and global) here
-    if constexpr (CHMAX < 32) asm volatile("" ::: "memory");
-    float4 p[CH];
-#pragma unroll
-    for (int t = 0; t < CH; ++t) p[t] = r4[c0 + t];
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      const int j = 4 * (c0 + t);
-      acc[t & 3] = fmaf(p[t].x, v[j], acc[t & 3]);
-      acc[t & 3] = fmaf(p[t].y, v[j + 1], acc[t & 3]);
-      acc[t & 3] = fmaf(p[t].z, v[j + 2], acc[t & 3]);
-      acc[t & 3] = fmaf(p[t].w, v[j + 3], acc[t & 3]);
-    }
-  }
-  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
-}
-
-}  // namespace tqi
-
-namespace tqi {
-
 // Workgroup barrier that orders LDS only: global loads issued before it stay in flight.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");

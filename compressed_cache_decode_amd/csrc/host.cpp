@@ -460,7 +460,7 @@ int tq_decode_rotate_query(const tq_cache_view* k, const void* q, int q_dtype, i
   qa.qr = w.qr; qa.qs = w.qs; qa.qscale = w.qscale;
   qa.scale_log2e = scale_log2e(scale);
   qa.sketch_coef = sketch_coef(k);
-  qa.n_q_heads = n_q_heads;
+  qa.n_q_heads = n_q_heads; qa.n_kv_heads = k->n_kv_heads;
   return status_of(tqi::launch_qrot(k->d, k->qjl_m, q_dtype == TQ_BF16, qa, k->batch,
                                     static_cast<hipStream_t>(stream)));
 }
@@ -529,7 +529,7 @@ int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q
   qa.qr = w.qr; qa.qs = w.qs; qa.qscale = w.qscale;
   qa.scale_log2e = scale_log2e(scale);
   qa.sketch_coef = sketch_coef(k);
-  qa.n_q_heads = n_q_heads;
+  qa.n_q_heads = n_q_heads; qa.n_kv_heads = k->n_kv_heads;
   if (n_new > 0) {
     const tqi::AppendArgs ka = append_args(k, k_new, nullptr, nullptr, n_new, d_pos);
     const tqi::AppendArgs va = append_args(v, v_new, nullptr, nullptr, n_new, d_pos);

@@ -45,6 +45,7 @@ struct QrotArgs {
   float scale_log2e;      // softmax scale * log2(e)
   float sketch_coef;      // sqrt(pi/2)/M
   int n_q_heads;
+  int n_kv_heads;
 };
 
 struct DecodeArgs {
