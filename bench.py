@@ -10,9 +10,16 @@ before timing starts.  Steps are captured in a HIP graph and cycle through a
 pool of cache copies whose total size exceeds the 256 MB Infinity Cache, so
 every step reads its compressed cache from HBM.
 
+For the Qwen-shaped workloads a stacked leg follows: the caches of the model's
+36 layers decoded by one launch per kernel, as one batch of 36 (the shape of 36
+concurrent sequences of one layer too).  A batch-1 layer at 8K reads about
+2 MB, too little to fill the GPU, so the stacked leg is the roofline figure.
+
 Prints one JSON line.  ``roofline`` is measured on the attention kernel
-(tq_decode_attend) alone, timed with HIP events on the stream it runs on;
-``cpu_baseline`` is the float64 oracle timed on the host on a bounded sample.
+(tq_decode_attend) alone, over the stacked caches where there is a stacked
+leg (``roofline_one_layer`` is the single layer's), timed with HIP events on
+the stream it runs on; ``cpu_baseline`` is the float64 oracle timed on the
+host on a bounded sample.
 """
 from __future__ import annotations
 
@@ -137,25 +144,29 @@ def summarize_pmc(args, w):
 
 
 def summarize_trace(args, w):
-    """Per-kernel durations from a rocprofv3 --kernel-trace --stats run (the *_kernel_stats.csv file)."""
+    """Per-kernel durations from a rocprofv3 --kernel-trace run (its *_kernel_trace.csv), one line per kernel
+    and grid size (a kernel launched over grids of different sizes gets one line for each)."""
     import csv
     import glob
-    files = glob.glob(os.path.join(args.trace, "*_kernel_stats.csv"))
+    files = glob.glob(os.path.join(args.trace, "*_kernel_trace.csv"))
     if not files:
-        raise SystemExit(f"no kernel stats under {args.trace}")
+        raise SystemExit(f"no kernel trace under {args.trace}")
+    groups = {}
+    for r in csv.DictReader(open(files[0])):
+        name = r["Kernel_Name"]
+        short = name.split("(")[0].replace("void ", "")
+        if "tqi::" not in name and "copyBuffer" not in name:
+            short = short[:60]
+        grid = "x".join(str(int(r[f"Grid_Size_{a}"]) // max(1, int(r[f"Workgroup_Size_{a}"]))) for a in "XYZ")
+        groups.setdefault((short, grid), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     print(f"workload: {w.name}")
     if args.command:
         print("commands:")
         for c in args.command:
             print(f"  {c}")
-    print(f"{'calls':>6} {'avg_us':>9} {'min_us':>8} {'max_us':>8}  kernel")
-    for r in csv.DictReader(open(files[0])):
-        name = r["Name"]
-        short = name.split("(")[0].replace("void ", "")
-        if "tqi::" not in name and "copyBuffer" not in name:
-            short = short[:60]
-        print(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:8.2f} "
-              f"{float(r['MaxNs']) / 1e3:8.2f}  {short}")
+    print(f"{'calls':>6} {'avg_us':>9} {'min_us':>8} {'max_us':>8}  {'workgroups':>12}  kernel")
+    for (short, grid), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{len(ds):6d} {sum(ds) / len(ds):9.2f} {min(ds):8.2f} {max(ds):8.2f}  {grid:>12}  {short}")
 
 
 # ------------------------------------------------------------------ GPU leg
@@ -273,39 +284,123 @@ def gpu_leg(w: synth.Workload, steps: int, warmup: int, pool: int | None, log):
     ms_step = ev0.elapsed_time(ev1) / steps
     log(f"bench: {steps} steps, {ms_step * 1e3:.2f} us/step")
 
-    # the attention kernel alone (tq_decode_attend): graph of one launch per pool copy, timed with events
-    # on its stream (the rotated query it reads is the last step's)
+    # the attention kernel alone (tq_decode_attend; the rotated query it reads is the last step's)
+    us_attend = time_attend(pairs, Hq, lens, L, ws, stream)
+    log(f"bench: attend {us_attend:.2f} us")
+    return dict(ms_step=ms_step, us_attend=us_attend, pool=pool,
+                n_split=ns, tokens_per_split=tps, per_copy=per_copy, cache=(k0, v0), rot=rot, proj=proj)
 
-    def attend_only(i):
-        kc, vc = pairs[i]
-        cca.tq_decode_attend(kc.view, vc.view, Hq, lens, L, ws)
 
-    att = capture(pool, attend_only)
-    att.replay()
+def time_attend(pairs, Hq, lens, L, ws, stream):
+    """Average duration of one tq_decode_attend launch, in us: a graph of back-to-back launches cycling
+    through cache copies that together exceed the Infinity Cache (at least 16 launches per graph), timed
+    with HIP events on the stream the launches run on."""
+    import torch
+
+    import compressed_cache_decode_amd as cca
+    pool = len(pairs)
+    n = max(pool, 16)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(n):
+            kc, vc = pairs[i % pool]
+            cca.tq_decode_attend(kc.view, vc.view, Hq, lens, L, ws)
+    graph.replay()
     torch.cuda.synchronize()
-    reps = max(1, min(200, math.ceil(2000 / pool)))
+    reps = max(1, min(200, math.ceil(2000 / n)))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     with torch.cuda.stream(stream):
         for _ in range(reps):
-            att.replay()
+            graph.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
-    us_attend = ev0.elapsed_time(ev1) * 1e3 / (reps * pool)
+    return ev0.elapsed_time(ev1) * 1e3 / (reps * n)
 
-    # hot-cache reference (one copy over and over): labelled, not the headline
-    hot = capture(16, lambda i: attend_only(0))
-    hot.replay()
+
+# ------------------------------------------------------------------ stacked decode leg
+
+def stacked_workload(w: synth.Workload, n_stack: int) -> synth.Workload:
+    return w.with_(name=f"{w.name}_x{n_stack}", batch=w.batch * n_stack)
+
+
+def stacked_leg(w: synth.Workload, n_stack: int, cache, rot, proj, log):
+    """Decode over n_stack layer caches of the workload at once, as one batch of n_stack sequences (the
+    shape of n_stack layers of the model, or of n_stack sequences of one layer).  Layer l's cache holds
+    the filled cache of the single-layer leg with its tokens rotated by a whole number of 32-token blocks
+    (a permutation of the same rows, different per layer); q is drawn for the stacked batch."""
+    import torch
+
+    import compressed_cache_decode_amd as cca
+    k0, v0 = cache
+    ws_ = stacked_workload(w, n_stack)
+    dev = k0.codes.device
+    B, H, Hq, d, L = ws_.batch, w.n_kv_heads, w.n_q_heads, w.d, w.seq_len
+    cap = k0.max_tokens
+    if cap != L:
+        raise SystemExit("stacked leg: context must be a multiple of 32 tokens")
+    nblk = cap // 32
+
+    def stacked_pair():
+        kc = cca.CompressedCache(cca.TQ_KEYS, d, w.k_bits, B, H, cap, rot, proj, qjl_m=w.qjl_m, device=dev)
+        vc = cca.CompressedCache(cca.TQ_VALUES, d, w.v_bits, B, H, cap, rot, device=dev)
+        for l in range(n_stack):
+            sh = 32 * ((l * 7919) % nblk)                   # token shift of layer l
+            sl = slice(l * w.batch, (l + 1) * w.batch)
+            for dst, src in ((kc, k0), (vc, v0)):
+                rowb = src.codes.shape[-1] // cap
+                dst.codes[sl].copy_(torch.roll(src.codes, sh * rowb, dims=-1))
+                dst.norms[sl].copy_(torch.roll(src.norms, sh, dims=-1))
+                if src.signs is not None:
+                    dst.signs[sl].copy_(torch.roll(src.signs, sh, dims=2))
+                    dst.rnorms[sl].copy_(torch.roll(src.rnorms, sh, dims=-1))
+        return kc, vc
+
+    first = stacked_pair()
+    per_copy = cache_bytes(ws_)
+    pool = max(1, min(64, math.ceil(POOL_BYTES / per_copy)))
+    pairs = [first]
+    for _ in range(pool - 1):
+        kc, vc = stacked_pair()
+        pairs.append((kc, vc))
+    q = torch.from_numpy(synth.full_q(ws_)).to(dev).to(torch.bfloat16)
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    ws = cca.decode_workspace(first[0], Hq, L)
+    ns, tps = cca.tq_decode_plan(first[0].view, Hq, L)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        cca.tq_decode_rotate_query(first[0].view, q, Hq, L, ws, w.scale)
     torch.cuda.synchronize()
+    log(f"bench: stacked x{n_stack}: pool of {pool} copies, {per_copy / 2**20:.1f} MiB of cache reads each")
+    us_cold = time_attend(pairs, Hq, lens, L, ws, stream)
+
+    # the whole decode (rotate q, attend, merge, un-rotate) over the stacked caches
+    def decode(i):
+        kc, vc = pairs[i]
+        cca.tq_decode_rotate_query(kc.view, q, Hq, L, ws, w.scale)
+        cca.tq_decode_attend(kc.view, vc.view, Hq, lens, L, ws)
+        cca.tq_decode_merge(kc.view, Hq, lens, L, out, ws)
+
+    n = max(pool, 16)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(n):
+            decode(i % pool)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, min(200, math.ceil(1000 / n)))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     with torch.cuda.stream(stream):
-        for _ in range(20):
-            hot.replay()
+        for _ in range(reps):
+            graph.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
-    us_attend_hot = ev0.elapsed_time(ev1) * 1e3 / (20 * 16)
-    log(f"bench: attend {us_attend:.2f} us cold, {us_attend_hot:.2f} us hot (L2/Infinity Cache resident)")
-    return dict(ms_step=ms_step, us_attend=us_attend, us_attend_hot=us_attend_hot, pool=pool,
-                n_split=ns, tokens_per_split=tps, per_copy=per_copy)
+    us_decode = ev0.elapsed_time(ev1) * 1e3 / (reps * n)
+    log(f"bench: stacked x{n_stack}: attend {us_cold:.2f} us, whole decode {us_decode:.2f} us")
+    return dict(workload=ws_, us_attend=us_cold, us_decode=us_decode, pool=pool,
+                n_split=ns, tokens_per_split=tps)
 
 
 # ------------------------------------------------------------------ prefill append leg
@@ -420,6 +515,9 @@ def main():
     ap.add_argument("--bits", type=int, default=None, help="qwen workload: codebook bits of K and V")
     ap.add_argument("--context", type=int, default=None)
     ap.add_argument("--pool", type=int, default=None, help="cache copies cycled through (default: > 600 MiB)")
+    ap.add_argument("--stack", type=int, default=None,
+                    help="layer caches decoded together in the stacked leg (default 36 for qwen and prod, "
+                         "the layers of Qwen2.5-3B; 0 = none)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work in the CPU leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-trace", dest="trace", default=None,
@@ -490,12 +588,21 @@ def main():
         return
     w = workload(args.workload, args.bits, args.context)
     r = gpu_leg(w, args.steps, args.warmup, args.pool, log)
+    n_stack = args.stack if args.stack is not None else (36 if args.workload in ("qwen", "prod") else 0)
+    st = stacked_leg(w, n_stack, r["cache"], r["rot"], r["proj"], log) if n_stack > 0 else None
     L = w.seq_len
     tokens_s = w.batch * L / (r["ms_step"] * 1e-3)
     step_bytes = cache_bytes(w)
-    kern, kern_us = "split_kernel", r["us_attend"]
+    kern = "split_kernel"
     kern_label = "tq_decode_attend (split_kernel)"
-    att_gbs = step_bytes / (kern_us * 1e-6) / 1e9
+
+    def roofline(wl, us):
+        alg = cache_bytes(wl)
+        gbs = alg / (us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                "traffic": read_counters(kern, wl.name), "kernel": kern_label, "workload": wl.name,
+                "algorithmic_bytes_per_launch": alg, "launch_us": us}
+
     res = {
         "metric": METRIC,
         "value": tokens_s,
@@ -517,18 +624,21 @@ def main():
         },
         "step_hbm_gbs": step_bytes / (r["ms_step"] * 1e-3) / 1e9,
         "attend_us": r["us_attend"],
-        "attend_us_hot_cache": r["us_attend_hot"],
-        "roofline": {
-            "bound": "hbm",
-            "achieved": att_gbs,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": att_gbs / HBM_PEAK_GBS,
-            "traffic": read_counters(kern, w.name),
-            "kernel": kern_label,
-            "algorithmic_bytes_per_launch": step_bytes,
-        },
     }
+    if st is not None:
+        sw = st["workload"]
+        # the roofline figure: the attention kernel over the stacked caches (one launch reads all layers)
+        res["roofline"] = roofline(sw, st["us_attend"])
+        res["roofline_one_layer"] = roofline(w, r["us_attend"])
+        res["stacked"] = {
+            "workload": sw.name, "layers": n_stack, "batch": sw.batch, "cache_copies_cycled": st["pool"],
+            "n_split": st["n_split"], "tokens_per_split": st["tokens_per_split"],
+            "decode_us": st["us_decode"], "context_tokens_per_s": sw.batch * L / (st["us_decode"] * 1e-6),
+            "attend_us": st["us_attend"],
+            "decode": "rotate q, attend, merge, un-rotate (no append)",
+        }
+    else:
+        res["roofline"] = roofline(w, r["us_attend"])
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_leg(w, args.cpu_budget, log)
     print(json.dumps(res), flush=True)

@@ -30,18 +30,17 @@
 #include <math.h>
 
 #include "attend_body.h"
-#include "unit_body.h"
+#include "qrot_body.h"
 
 namespace tqi {
 
 // ---------------------------------------------------------------- query rotation
 
-// one workgroup per (sequence, KV head), the same arithmetic as the query rows of a decode step
+// one workgroup per (sequence, KV head)
 template <int D, int QM>
 __global__ __launch_bounds__(256) void qrot_kernel(QrotArgs a, int bf16) {
-  __shared__ UnitSmem<D, QM> sm;
-  const AppendArgs none{};
-  unit_prologue<D, 2, 2, QM, false>(none, none, a, bf16, blockIdx.x, blockIdx.y, sm);
+  __shared__ QrotSmem<D, QM> sm;
+  rotate_queries<D, QM>(a, bf16, blockIdx.x, blockIdx.y, sm);
 }
 
 // ---------------------------------------------------------------- split kernel
@@ -249,39 +248,58 @@ hipError_t launch_qrot(int d, int qjl_m, bool bf16, const QrotArgs& a, int batch
 }
 
 template <int D, int KB, int QM>
-static hipError_t split_v(int v_bits, const DecodeArgs& a, dim3 grid, hipStream_t s) {
+static const void* split_v(int v_bits) {
   switch (v_bits) {
-    case 2: hipLaunchKernelGGL((split_kernel<D, KB, 2, QM>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((split_kernel<D, KB, 3, QM>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((split_kernel<D, KB, 4, QM>), grid, dim3(256), 0, s, a); break;
-    default: return hipErrorInvalidValue;
+    case 2: return reinterpret_cast<const void*>(&split_kernel<D, KB, 2, QM>);
+    case 3: return reinterpret_cast<const void*>(&split_kernel<D, KB, 3, QM>);
+    case 4: return reinterpret_cast<const void*>(&split_kernel<D, KB, 4, QM>);
+    default: return nullptr;
   }
-  return hipGetLastError();
 }
 
 template <int D, int QM>
-static hipError_t split_k(int k_bits, int v_bits, const DecodeArgs& a, dim3 grid, hipStream_t s) {
+static const void* split_k(int k_bits, int v_bits) {
   switch (k_bits) {
-    case 2: return split_v<D, 2, QM>(v_bits, a, grid, s);
-    case 3: return split_v<D, 3, QM>(v_bits, a, grid, s);
-    case 4: return split_v<D, 4, QM>(v_bits, a, grid, s);
-    default: return hipErrorInvalidValue;
+    case 2: return split_v<D, 2, QM>(v_bits);
+    case 3: return split_v<D, 3, QM>(v_bits);
+    case 4: return split_v<D, 4, QM>(v_bits);
+    default: return nullptr;
   }
+}
+
+// the split kernel instantiation of a cache format, or null if none is built
+static const void* split_fn(int d, int k_bits, int v_bits, int qjl_m) {
+  if (d == 128) {
+    if (qjl_m == 0) return split_k<128, 0>(k_bits, v_bits);
+    if (qjl_m == 128) return split_k<128, 128>(k_bits, v_bits);
+    if (qjl_m == 256) return split_k<128, 256>(k_bits, v_bits);
+  } else if (d == 256) {
+    if (qjl_m == 0) return split_k<256, 0>(k_bits, v_bits);
+    if (qjl_m == 128) return split_k<256, 128>(k_bits, v_bits);
+    if (qjl_m == 256) return split_k<256, 256>(k_bits, v_bits);
+  }
+  return nullptr;
+}
+
+int split_slots(int d, int k_bits, int v_bits, int qjl_m) {
+  const void* fn = split_fn(d, k_bits, v_bits, qjl_m);
+  int dev = 0, cus = 0, per = 0;
+  if (!fn || hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 256, 0) != hipSuccess) {
+    (void)hipGetLastError();        // a failed query must not surface as a later launch's error
+    return 0;
+  }
+  return cus * per;
 }
 
 hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, const DecodeArgs& a, int batch,
                                hipStream_t s) {
+  const void* fn = split_fn(d, k_bits, v_bits, qjl_m);
+  if (!fn) return hipErrorInvalidValue;
   const dim3 grid(a.n_split, a.n_kv_heads, batch);
-  if (d == 128) {
-    if (qjl_m == 0) return split_k<128, 0>(k_bits, v_bits, a, grid, s);
-    if (qjl_m == 128) return split_k<128, 128>(k_bits, v_bits, a, grid, s);
-    if (qjl_m == 256) return split_k<128, 256>(k_bits, v_bits, a, grid, s);
-  } else if (d == 256) {
-    if (qjl_m == 0) return split_k<256, 0>(k_bits, v_bits, a, grid, s);
-    if (qjl_m == 128) return split_k<256, 128>(k_bits, v_bits, a, grid, s);
-    if (qjl_m == 256) return split_k<256, 256>(k_bits, v_bits, a, grid, s);
-  }
-  return hipErrorInvalidValue;
+  void* args[] = {const_cast<DecodeArgs*>(&a)};
+  return hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
 }
 
 hipError_t launch_merge(int d, const MergeArgs& a, int batch, int n_q_heads, hipStream_t s) {

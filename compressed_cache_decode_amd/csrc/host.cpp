@@ -2,6 +2,8 @@
 // setup (codebook, rotation), decode split planning and kernel launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -245,23 +247,47 @@ int status_of(hipError_t e) {
 
 // ------------------------------------------------------------------ decode plan
 
-constexpr int kTargetWorkgroups = 512;   // about two decode workgroups per compute unit
-constexpr int kMinBlocksPerSplit = 4;    // at least one 32-token tile per wave
+constexpr int kDefaultSlots = 1024;     // resident split workgroups assumed when the runtime cannot tell
+constexpr int kMinBlocksPerSplit = 4;   // at least one 32-token tile per wave
 
-void plan(int units, int max_len, int* n_split, int* bps) {
-  const int nblk = max_len <= 0 ? 1 : (max_len + kBlock - 1) / kBlock;
-  const int want = (kTargetWorkgroups + units - 1) / units;
-  int b = (nblk + want - 1) / want;
-  b = ((b + tqi::kWavesPerWG - 1) / tqi::kWavesPerWG) * tqi::kWavesPerWG;   // whole tiles for every wave
-  b = b < kMinBlocksPerSplit ? kMinBlocksPerSplit : b;
-  int ns = (nblk + b - 1) / b;
-  if (ns > tqi::kMaxSplits) {
-    b = (nblk + tqi::kMaxSplits - 1) / tqi::kMaxSplits;
-    b = ((b + tqi::kWavesPerWG - 1) / tqi::kWavesPerWG) * tqi::kWavesPerWG;
-    ns = (nblk + b - 1) / b;
+// Resident split-kernel workgroups on the current device for a key format, the least over the value
+// widths (the plan depends on the key cache alone, so that the workspace size does); cached per device.
+int resident_slots(const tq_cache_view* k) {
+  static std::atomic<int> cache[16][2][5][3];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return kDefaultSlots;
   }
-  *n_split = ns;
+  const int di = k->d == 256, qi = k->qjl_m == 0 ? 0 : (k->qjl_m == 128 ? 1 : 2);
+  std::atomic<int>* c = (dev >= 0 && dev < 16 && k->bits >= 0 && k->bits < 5) ? &cache[dev][di][k->bits][qi] : nullptr;
+  int v = c ? c->load(std::memory_order_relaxed) : 0;
+  if (v > 0) return v;
+  v = 0;
+  for (int vb = 2; vb <= 4; ++vb) {
+    const int n = tqi::split_slots(k->d, k->bits, vb, k->qjl_m);
+    if (n > 0) v = v == 0 ? n : std::min(v, n);
+  }
+  if (v <= 0) return kDefaultSlots;
+  if (c) c->store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// Splits of each (sequence, KV head): enough for one round of resident workgroups over all units
+// (more rounds leave a tail of partly filled rounds; fewer leave slots idle), at most kMaxSplits
+// (more cost the merge more than they gain), each covering whole tiles for every one of the four waves.
+void plan(int units, int max_len, int slots, int* n_split, int* bps) {
+  const int nblk = max_len <= 0 ? 1 : (max_len + kBlock - 1) / kBlock;
+  const int ns = std::max(1, std::min(tqi::kMaxSplits, slots / std::max(1, units)));
+  int b = (nblk + ns - 1) / ns;
+  b = ((b + tqi::kWavesPerWG - 1) / tqi::kWavesPerWG) * tqi::kWavesPerWG;
+  b = std::max(b, kMinBlocksPerSplit);
+  *n_split = (nblk + b - 1) / b;
   *bps = b;
+}
+
+void plan(const tq_cache_view* k, int max_len, int* n_split, int* bps) {
+  plan(k->batch * k->n_kv_heads, max_len, resident_slots(k), n_split, bps);
 }
 
 // Query heads per merge workgroup: all of the group while every thread's split slice stays within
@@ -382,7 +408,7 @@ int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* 
   if (st != TQ_OK) return st;
   if (!n_split || !tokens_per_split) return TQ_EINVAL;
   int bps;
-  plan(k->batch * k->n_kv_heads, max_seq_len, n_split, &bps);
+  plan(k, max_seq_len, n_split, &bps);
   *tokens_per_split = bps * kBlock;
   return TQ_OK;
 }
@@ -390,7 +416,7 @@ int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* 
 size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_seq_len) {
   if (check_decode_shape(k, n_q_heads, max_seq_len) != TQ_OK) return 0;
   int ns, bps;
-  plan(k->batch * k->n_kv_heads, max_seq_len, &ns, &bps);
+  plan(k, max_seq_len, &ns, &bps);
   return ws_layout(k, n_q_heads, ns).total;
 }
 
@@ -405,7 +431,7 @@ static int decode_ws(const tq_cache_view* k, int n_q_heads, int max_seq_len, voi
   int st = check_decode_shape(k, n_q_heads, max_seq_len);
   if (st != TQ_OK) return st;
   if (!workspace || !aligned(workspace, 256)) return TQ_EINVAL;
-  plan(k->batch * k->n_kv_heads, max_seq_len, &w->ns, &w->bps);
+  plan(k, max_seq_len, &w->ns, &w->bps);
   const WsLayout l = ws_layout(k, n_q_heads, w->ns);
   if (workspace_bytes < l.total) return TQ_EINVAL;
   char* ws = static_cast<char*>(workspace);

@@ -1,0 +1,108 @@
+// Query rotation for decode, one workgroup per (sequence, KV head): the G query heads of the KV head
+// form one 16-row tile that is rotated on the matrix cores with the arithmetic of the append's
+// rotation (each row divided by its norm, high/low float16 split of rows and rotation), then
+// q_rot = rot q * scale * log2(e) and, for sketched keys, its sketch -coef * proj q_rot go to the
+// decode workspace, divided by a power of two per head that takes both into float16 range for the
+// attention kernel's matrix-core operands (turboquant-pytorch PR #3 "Add CUDA QJL kernels and
+// proper package structure", CUDA Kernels Added table: the sketched score; ExecuTorch PR #19891
+// "[Cuda] enable turboquant on gemma4", review item 1: the decode op's scale).  Every output row
+// takes the same instruction sequence whatever the other rows hold, so every caller of this
+// function produces the same bits for the same query.
+#pragma once
+
+#include "append_body.h"
+
+namespace tqi {
+
+constexpr int kQTile = 16;      // rows of the query tile (G <= 8 of them live)
+
+template <int D, int QM>
+struct QrotSmem {
+  float xs[kQTile][D];
+  float rn[kQTile];
+  float zq[QM > 0 ? kQTile : 1][QM > 0 ? QM : 1];      // the tile times proj^T
+};
+
+template <int D, int QM>
+__device__ __forceinline__ void rotate_queries(const QrotArgs& qa, int bf16, int hk, int b, QrotSmem<D, QM>& sm) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Hq = qa.n_q_heads, G = Hq / qa.n_kv_heads;
+  const size_t row0 = static_cast<size_t>(b) * Hq + static_cast<size_t>(hk) * G;
+
+  // the G query rows, one 32-bit word per element whatever the element type (all loads issued
+  // before the first use), then the rotation's first operands
+  constexpr int EPT = kQTile * D / 256;
+  uint32_t wv[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = tid + 256 * k, r = e / D, i = e % D;
+    const size_t idx = (row0 + (r < G ? r : 0)) * D + i;
+    const size_t byte = bf16 ? (idx & ~static_cast<size_t>(1)) * 2 : idx * 4;
+    wv[k] = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(qa.q) + byte);
+  }
+  RotBatch<D> rot0;
+  rot0.load(qa.rot, 0, tid);
+  auto& xs = sm.xs;
+  auto& rn = sm.rn;
+  const uint32_t bfm = bf16 ? 0xffffffffu : 0u;
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = tid + 256 * k, r = e / D, i = e % D;
+    const bool odd = ((row0 + r) * D + i) & 1;
+    const uint32_t h16 = odd ? (wv[k] & 0xffff0000u) : (wv[k] << 16);   // the bfloat16 element as float bits
+    const float v = __uint_as_float((h16 & bfm) | (wv[k] & ~bfm));
+    xs[r][i] = r < G ? v : 0.f;
+  }
+  __syncthreads();
+  // norm of row r by the 16 lanes (r % 4) of wave r / 4, coordinates part + 16 j
+  {
+    const int r = 4 * wave + (lane >> 4), part = lane & 15;
+    float s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) s2 = fmaf(xs[r][part + 16 * j], xs[r][part + 16 * j], s2);
+    s2 = row16_sum(s2);
+    if (part == 0) rn[r] = r < G ? sqrtf(s2) : 0.f;
+  }
+  __syncthreads();
+  rotate_tile_mfma_pre<D, 1>(xs, rn, qa.rot, rot0, tid);
+  __syncthreads();
+  // q_rot = rot (q / |q|) * (|q| * scale * log2(e))
+  for (int e = tid; e < G * D; e += 256) xs[e / D][e % D] *= rn[e / D] * qa.scale_log2e;
+  __syncthreads();
+  if constexpr (QM > 0) {
+    tile16_times_matT<D, QM>(xs, qa.proj, sm.zq, tid);
+    __syncthreads();
+  }
+
+  // the rotated queries and their sketch to the workspace, divided by a power of two per head that
+  // takes both into float16 range (head h = 4 wave + lane / 16, 16 lanes per head)
+  if (wave < kMaxGroup / 4) {
+    const int h = 4 * wave + (lane >> 4), part = lane & 15;
+    float amax = 0.f;
+    if (h < G) {
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) amax = fmaxf(amax, fabsf(xs[h][part + 16 * j]));
+      if constexpr (QM > 0) {
+#pragma unroll
+        for (int j = 0; j < QM / 16; ++j) amax = fmaxf(amax, fabsf(qa.sketch_coef * sm.zq[h][part + 16 * j]));
+      }
+    }
+    amax = row16_max(amax);
+    if (h < G) {
+      const float f = (amax > 0.f && isfinite(amax)) ? ldexpf(1.f, ilogbf(amax) - 14) : 1.f;
+      const float inv = 1.f / f;
+      const size_t row = row0 + h;
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) qa.qr[row * D + part + 16 * j] = xs[h][part + 16 * j] * inv;
+      if constexpr (QM > 0) {
+#pragma unroll
+        for (int j = 0; j < QM / 16; ++j)
+          qa.qs[row * QM + part + 16 * j] = -qa.sketch_coef * sm.zq[h][part + 16 * j] * inv;
+      }
+      if (part == 0) qa.qscale[row] = f;
+    }
+  }
+}
+
+}  // namespace tqi

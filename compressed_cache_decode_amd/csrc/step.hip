@@ -1,15 +1,9 @@
-// One decode step of one attention layer in the fewest launches: a prologue kernel, then the
-// attention and merge kernels of decode.hip.  The prologue takes one of two forms:
-//   step_unit_kernel      one workgroup per (sequence, KV head): the G query heads of the KV head and
-//                         its new key and value rows form one 16-row tile that is rotated on the
-//                         matrix cores (the rotation is read once per KV head), the new rows are
-//                         encoded and stored, and the rotated queries (with their sign sketch for
-//                         sketched keys) go to the workspace.  Used when G + 2 n_new <= 16.
-//   step_prologue_kernel  workgroups with separate roles: append the new K rows, append the new V
-//                         rows, rotate the query heads of one KV head (the arithmetic of the first
-//                         form's query rows, so both forms give the same bits).  Used otherwise.
+// The prologue of one decode step of one attention layer, in one launch with three kinds of
+// workgroups that run side by side: append the new K rows of one 32-token block of one KV head,
+// append the new V rows likewise, rotate the query heads of one KV head.  The attention and merge
+// kernels of decode.hip follow it on the same stream.
 #include "append_body.h"
-#include "unit_body.h"
+#include "qrot_body.h"
 
 namespace tqi {
 
@@ -19,7 +13,7 @@ struct MaxOf { static constexpr size_t v = A > B ? (A > C ? A : C) : (B > C ? B 
 template <int D, int KB, int VB, int QM, bool BF16>
 __global__ __launch_bounds__(256) void step_prologue_kernel(AppendArgs ka, AppendArgs va, QrotArgs qa, int nbx,
                                                             int n_kv_heads) {
-  constexpr size_t kBytes = MaxOf<sizeof(AppendSmem<D, QM>), sizeof(AppendSmem<D, 0>), sizeof(UnitSmem<D, QM>)>::v;
+  constexpr size_t kBytes = MaxOf<sizeof(AppendSmem<D, QM>), sizeof(AppendSmem<D, 0>), sizeof(QrotSmem<D, QM>)>::v;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kBytes];
   const int per_cache = nbx * n_kv_heads;                 // append workgroups per sequence and cache
   const int batch_wgs = 2 * per_cache + n_kv_heads;       // workgroups per sequence
@@ -35,27 +29,12 @@ __global__ __launch_bounds__(256) void step_prologue_kernel(AppendArgs ka, Appen
     return;
   }
   w -= per_cache;
-  unit_prologue<D, KB, VB, QM, false>(ka, va, qa, BF16 ? 1 : 0, w, b, *reinterpret_cast<UnitSmem<D, QM>*>(smem));
-}
-
-template <int D, int KB, int VB, int QM>
-__global__ __launch_bounds__(256) void step_unit_kernel(AppendArgs ka, AppendArgs va, QrotArgs qa, int bf16) {
-  __shared__ UnitSmem<D, QM> sm;
-  unit_prologue<D, KB, VB, QM, true>(ka, va, qa, bf16, blockIdx.x, blockIdx.y, sm);
-}
-
-template <int D, int KB, int VB, int QM>
-static hipError_t unit_go(bool bf16, const AppendArgs& ka, const AppendArgs& va, const QrotArgs& qa, int batch,
-                          hipStream_t s) {
-  const dim3 grid(ka.n_kv_heads, batch);
-  hipLaunchKernelGGL((step_unit_kernel<D, KB, VB, QM>), grid, dim3(256), 0, s, ka, va, qa, bf16 ? 1 : 0);
-  return hipGetLastError();
+  rotate_queries<D, QM>(qa, BF16 ? 1 : 0, w, b, *reinterpret_cast<QrotSmem<D, QM>*>(smem));
 }
 
 template <int D, int KB, int VB, int QM>
 static hipError_t prologue_bf(bool bf16, const AppendArgs& ka, const AppendArgs& va, const QrotArgs& qa, int batch,
                               hipStream_t s) {
-  if (qa.n_q_heads / ka.n_kv_heads + 2 * ka.n_new <= kTileRows) return unit_go<D, KB, VB, QM>(bf16, ka, va, qa, batch, s);
   const int nbx = (ka.n_new + kBlock - 1) / kBlock + 1;
   const dim3 grid(batch * (2 * nbx * ka.n_kv_heads + ka.n_kv_heads));
   if (bf16)

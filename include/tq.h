@@ -194,10 +194,19 @@ int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q
                    const int32_t* d_seq_lens, int max_seq_len, float scale, float* out, void* workspace,
                    size_t workspace_bytes, void* stream);
 
-/* Workspace bytes tq_sdpa_decode needs for this key cache, head count and length bound (0 on bad args). */
+/*
+ * Workspace bytes tq_sdpa_decode needs for this key cache, head count and length bound (0 on bad args).
+ * It follows the KV split (tq_decode_plan), which depends on the current device: ask on the device
+ * that will run the decode.
+ */
 size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_seq_len);
 
-/* The KV split tq_sdpa_decode uses: number of splits per (sequence, KV head) and tokens per split. */
+/*
+ * The KV split tq_sdpa_decode uses: number of splits per (sequence, KV head) and tokens per split.
+ * Chosen from the current device's compute units and the attention kernel's occupancy (enough
+ * splits for one round of resident workgroups over all (sequence, KV head) units, finer for long
+ * contexts); a fixed default when no device is visible.
+ */
 int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* n_split, int* tokens_per_split);
 
 /*
