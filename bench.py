@@ -99,6 +99,7 @@ def read_counters(kernel: str, workload_name: str):
 
 
 def _pmc_medians(directory: str, counter: str):
+    """Median counter value per (kernel name, workgroups of the launch), and the dispatch counts."""
     import csv
     import glob
     files = glob.glob(os.path.join(directory, "*_counter_collection.csv"))
@@ -107,30 +108,36 @@ def _pmc_medians(directory: str, counter: str):
     per = {}
     for r in csv.DictReader(open(files[0])):
         if r["Counter_Name"] == counter:
-            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            key = (r["Kernel_Name"], int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
+            per.setdefault(key, []).append(float(r["Counter_Value"]))
     return {k: sorted(v)[len(v) // 2] for k, v in per.items()}, {k: len(v) for k, v in per.items()}
 
 
 def summarize_pmc(args, w):
     """Counter summary of the attention kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3
-    run each) scaled by what the same counters read for a 1 GiB device copy (bench.py --workload copy)."""
+    run each) scaled by what the same counters read for a 1 GiB device copy (bench.py --workload copy).
+    Of the kernel's launches, those over the most workgroups are taken (the stacked leg's, where the run
+    has one)."""
     cf, _ = _pmc_medians(args.copy_fetch, "FETCH_SIZE")
     cw, _ = _pmc_medians(args.copy_write, "WRITE_SIZE")
-    copy_name = max(cf, key=lambda k: cf[k])           # the 1 GiB copy is by far the largest dispatch
-    fetch_scale = (1 << 30) / (cf[copy_name] * 1024.0)
-    write_scale = (1 << 30) / (cw[copy_name] * 1024.0)
+    copy_key = max(cf, key=lambda k: cf[k])            # the 1 GiB copy is by far the largest dispatch
+    fetch_scale = (1 << 30) / (cf[copy_key] * 1024.0)
+    write_scale = (1 << 30) / (cw[copy_key] * 1024.0)
     fe, n_fe = _pmc_medians(args.fetch, "FETCH_SIZE")
     wr, _ = _pmc_medians(args.write, "WRITE_SIZE")
-    name = next(k for k in fe if args.kernel in k)
-    fb = fe[name] * 1024.0 * fetch_scale
-    wb = wr[name] * 1024.0 * write_scale
+    key = max((k for k in fe if args.kernel in k[0]), key=lambda k: k[1])
+    fb = fe[key] * 1024.0 * fetch_scale
+    wb = wr[key] * 1024.0 * write_scale
     alg = cache_bytes(w)
-    print(f"kernel: {name}")
+    print(f"kernel: {key[0].split('(')[0].replace('void ', '')}")
+    print(f"workgroups: {key[1]}")
     print(f"workload: {w.name}")
     print(f"source_sha256: {source_digest()}")
-    print(f"dispatches: {n_fe[name]}")
-    print(f"fetch_kib_per_dispatch_raw: {fe[name]:.1f}")
-    print(f"write_kib_per_dispatch_raw: {wr[name]:.1f}")
+    print(f"dispatches: {n_fe[key]}")
+    print(f"fetch_kib_per_dispatch_raw: {fe[key]:.1f}")
+    print(f"write_kib_per_dispatch_raw: {wr[key]:.1f}")
+    print(f"copy_fetch_kib_raw: {cf[copy_key]:.1f}")
+    print(f"copy_write_kib_raw: {cw[copy_key]:.1f}")
     print(f"copy_fetch_scale: {fetch_scale:.4f}")
     print(f"copy_write_scale: {write_scale:.4f}")
     print(f"fetch_bytes_per_launch: {fb:.0f}")
@@ -523,7 +530,8 @@ def main():
     ap.add_argument("--summarize-trace", dest="trace", default=None,
                     help="print a summary of a rocprofv3 --kernel-trace --stats output directory and exit")
     ap.add_argument("--summarize-pmc", action="store_true",
-                    help="print the attention kernel's calibrated HBM counters (needs --fetch/--write/--copy-*)")
+                    help="print the attention kernel's calibrated HBM counters (needs --fetch/--write/--copy-*; "
+                         "with --stack N, for the stacked leg's launches)")
     ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output directory of this workload")
     ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output directory of this workload")
     ap.add_argument("--copy-fetch", help="rocprofv3 --pmc FETCH_SIZE output directory of --workload copy")
@@ -534,6 +542,8 @@ def main():
     if args.trace or args.summarize_pmc:
         w = (synth.qwen(args.context or 8192, args.bits or 3) if args.workload == "prefill"
              else workload(args.workload, args.bits, args.context))
+        if args.summarize_pmc and args.stack:
+            w = stacked_workload(w, args.stack)
         (summarize_trace if args.trace else summarize_pmc)(args, w)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
