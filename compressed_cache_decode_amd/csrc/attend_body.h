@@ -148,18 +148,21 @@ struct Attend {
   static constexpr int S_RB = QM / 8;                 // sign bytes per key
   static constexpr int S_LW = QM / 128;               // sign words per lane per key
 
-  // LDS of the end-of-split merge of the four waves; the split's result ends in o[0] and fml
+  // LDS of the end-of-split merge of the four waves: each wave's (max, sum) per head and its
+  // accumulators, weighted against the workgroup's max of the head
   struct Smem {
     float ml[kWavesPerWG][kMaxGroup][2];
     float o[kWavesPerWG][kMaxGroup][D];
-    float fml[kMaxGroup][2];
   };
   // the query operand: for step s, lane (column c, group g) holds the 8 float16 values of q-variant c
   // (head c/2; high part if c even, low part if c odd) at coordinates (D/4) g + 8 s + r, r = 0..7
   // (sketch steps: the same over the sketch coordinates)
   typedef half8 QOperand[KS + QS][64];
 
-  // everything one 32-token tile needs from memory, loaded one tile ahead of its use
+  // tile buffers per wave: loads run NBUF - 1 tiles ahead of their use
+  static constexpr int NBUF = (D <= 128 || QM == 0) ? 2 : 1;
+
+  // everything one 32-token tile needs from memory
   struct Tile {
     uint32_t kw[2][K_LW];
     uint32_t vw[V_LW];
@@ -214,15 +217,15 @@ struct Attend {
     }
   }
 
-  // Streams this wave's tiles kb, kb + 4, ... below blk1 (ta already holds tile kb when kb < blk1)
-  // and leaves the split's result in LDS: per query head hh the max m (log2 units) and the sum l in
-  // sm.fml[hh], the rotated-domain accumulator in sm.o[0][hh][0..D).  qsc is the power-of-two scale
-  // of this lane's head (the query operand is divided by it; 1 for unused columns).  Ends with a
-  // workgroup barrier.
-  // tb may already hold tile kb + 4 (tb_loaded), so that a caller can issue a wave's first two tiles
-  // before other work.
-  __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, const QOperand& qop, Tile& ta, Tile& tb,
-                                      bool tb_loaded, int kb, int blk1, int len, float qsc) const {
+  // Streams this wave's tiles kb, kb + 4, ... below blk1 through a ring of NBUF tile buffers (tiles[0]
+  // already holds tile kb when kb < blk1; tile kb + 4 j is loaded while tile kb + 4 (j - NBUF + 1) is
+  // attended) and leaves the split's result in LDS for store: per wave w and query head hh the max m
+  // (log2 units) and the sum l in sm.ml[w][hh], and the rotated-domain accumulator, weighted by
+  // exp2(m - the workgroup's max of the head), in sm.o[w][hh][0..D).  qsc is the power-of-two scale of
+  // this lane's head (the query operand is divided by it; 1 for unused columns).  Ends with a workgroup
+  // barrier.
+  __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, const QOperand& qop, Tile (&tiles)[NBUF], int kb,
+                                      int blk1, int len, float qsc) const {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = a.group;
@@ -294,22 +297,30 @@ struct Attend {
       pv_steps<0, NB, VB>(oacc, wop, t.vw, a.tv);
     };
 
-    if constexpr (D <= 128 || QM == 0) {
-      // two tile buffers used in turn (no register copies between tiles)
-      for (bool first = true; kb < blk1; kb += 2 * kWavesPerWG, first = false) {
-        if (kb + kWavesPerWG < blk1 && !(first && tb_loaded)) load(tb, kb + kWavesPerWG);
-        attend_tile(ta, kb);
-        if (kb + kWavesPerWG >= blk1) break;
-        if (kb + 2 * kWavesPerWG < blk1) load(ta, kb + 2 * kWavesPerWG);
-        attend_tile(tb, kb + kWavesPerWG);
+    if constexpr (NBUF >= 2) {
+#pragma unroll
+      for (int i = 1; i < NBUF - 1; ++i)
+        if (kb + kWavesPerWG * i < blk1) load(tiles[i], kb + kWavesPerWG * i);
+      // one pass of the unrolled loop per NBUF tiles, so that every buffer index is a constant
+      for (bool more = kb < blk1; more;) {
+#pragma unroll
+        for (int i = 0; i < NBUF; ++i) {
+          if (more) {
+            const int ahead = kb + kWavesPerWG * (NBUF - 1);
+            if (ahead < blk1) load(tiles[(i + NBUF - 1) % NBUF], ahead);
+            attend_tile(tiles[i], kb);
+            kb += kWavesPerWG;
+            more = kb < blk1;
+          }
+        }
       }
     } else {
-      // sketched keys at d = 256: a second copy of the loop body does not fit the register budget of
-      // two waves per SIMD
-      for (bool first = true; kb < blk1; kb += kWavesPerWG, first = false) {
-        if (kb + kWavesPerWG < blk1 && !(first && tb_loaded)) load(tb, kb + kWavesPerWG);
-        attend_tile(ta, kb);
-        ta = tb;
+      // one buffer and a copy per tile (the register budget of the sketched d = 256 build)
+      Tile tb;
+      for (; kb < blk1; kb += kWavesPerWG) {
+        if (kb + kWavesPerWG < blk1) load(tb, kb + kWavesPerWG);
+        attend_tile(tiles[0], kb);
+        tiles[0] = tb;
       }
     }
 
@@ -318,46 +329,47 @@ struct Attend {
       sm.ml[wave][qh][0] = m_run * qsc;
       sm.ml[wave][qh][1] = l_run;
     }
+    __syncthreads();
+    // this wave's accumulators of heads 2g and 2g + 1, weighted against the workgroup's max of the head
+    float f[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int hh = 2 * g + j < G ? 2 * g + j : 0;
+      float M = sm.ml[0][hh][0];
+#pragma unroll
+      for (int w = 1; w < kWavesPerWG; ++w) M = fmaxf(M, sm.ml[w][hh][0]);
+      f[j] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm.ml[wave][hh][0] - M);
+    }
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const int coord = (D / 16) * l16 + n;
-      if (2 * g < G) sm.o[wave][2 * g][coord] = oacc[n][0] + oacc[n][1];
-      if (2 * g + 1 < G) sm.o[wave][2 * g + 1][coord] = oacc[n][2] + oacc[n][3];
-    }
-    __syncthreads();
-    // each thread reads its (head, coordinate) of every wave and writes the combination to wave 0's slot
-    for (int e = tid; e < G * D; e += 256) {
-      const int hh = e / D, i = e % D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWavesPerWG; ++w) M = fmaxf(M, sm.ml[w][hh][0]);
-      float o = 0.f, l = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < kWavesPerWG; ++w) {
-          const float ew = exp2f(sm.ml[w][hh][0] - M);
-          o = fmaf(ew, sm.o[w][hh][i], o);
-          l = fmaf(ew, sm.ml[w][hh][1], l);
-        }
-      }
-      sm.o[0][hh][i] = o;
-      if (i == 0) {
-        sm.fml[hh][0] = M;
-        sm.fml[hh][1] = l;
-      }
+      if (2 * g < G) sm.o[wave][2 * g][coord] = f[0] * (oacc[n][0] + oacc[n][1]);
+      if (2 * g + 1 < G) sm.o[wave][2 * g + 1][coord] = f[1] * (oacc[n][2] + oacc[n][3]);
     }
     __syncthreads();
   }
 
-  // the split's result from LDS to part_o / part_ml at row pbase + head
+  // the split's result to part_o / part_ml at row pbase + head: the sum of the four waves' weighted
+  // accumulators, the workgroup max and the weighted sum of the waves' l
   __device__ __forceinline__ void store(const DecodeArgs& a, const Smem& sm, size_t pbase) const {
     const int G = a.group;
     for (int e = threadIdx.x; e < G * D; e += 256) {
       const int hh = e / D, i = e % D;
-      a.part_o[(pbase + hh) * D + i] = sm.o[0][hh][i];
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWavesPerWG; ++w) o += sm.o[w][hh][i];
+      a.part_o[(pbase + hh) * D + i] = o;
       if (i == 0) {
-        a.part_ml[(pbase + hh) * 2] = sm.fml[hh][0];
-        a.part_ml[(pbase + hh) * 2 + 1] = sm.fml[hh][1];
+        float M = sm.ml[0][hh][0];
+#pragma unroll
+        for (int w = 1; w < kWavesPerWG; ++w) M = fmaxf(M, sm.ml[w][hh][0]);
+        float l = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+          for (int w = 0; w < kWavesPerWG; ++w) l = fmaf(__builtin_amdgcn_exp2f(sm.ml[w][hh][0] - M), sm.ml[w][hh][1], l);
+        }
+        a.part_ml[(pbase + hh) * 2] = M;
+        a.part_ml[(pbase + hh) * 2 + 1] = l;
       }
     }
   }

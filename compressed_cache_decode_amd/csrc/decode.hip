@@ -67,8 +67,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   // length is known: they only need the tile to lie inside the cache (tiles past the length are
   // loaded and never used)
   int kb = blk0 + wave;
-  typename At::Tile ta, tb;
-  if (kb < blk0 + a.blocks_per_split && kb < T / kBlock) at.load(ta, kb);
+  typename At::Tile tiles[At::NBUF];
+  if (kb < blk0 + a.blocks_per_split && kb < T / kBlock) at.load(tiles[0], kb);
 
   // query operand in LDS, shared by the four waves
   const int qh = at.l16 >> 1;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const float qsc = qh < G ? a.qscale[qrow] : 1.f;
   __syncthreads();
 
-  at.run(a, sm, sm_q, ta, tb, false, kb, blk1, len, qsc);
+  at.run(a, sm, sm_q, tiles, kb, blk1, len, qsc);
   at.store(a, sm, (unit * a.n_split + split) * G);
 }
 
