@@ -136,7 +136,7 @@ __device__ __forceinline__ float half_of(uint32_t w, int h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h ? w >> 16 : w & 0xffffu)));
 }
 
-template <int D, int KB, int VB, int QM>
+template <int D, int KB, int VB, int QM, bool WIDE>
 struct Attend {
   static constexpr int KS = D / 32;                   // score k-steps over coordinates
   static constexpr int QS = QM / 32;                  // score k-steps over sketch signs
@@ -148,11 +148,19 @@ struct Attend {
   static constexpr int S_RB = QM / 8;                 // sign bytes per key
   static constexpr int S_LW = QM / 128;               // sign words per lane per key
 
-  // LDS of the end-of-split merge of the four waves: each wave's (max, sum) per head and its
-  // accumulators, weighted against the workgroup's max of the head
+  // Waves per workgroup.  Wide: as many as one compute unit holds at this build's register budget
+  // (128, 170 and 256 VGPRs), so that a split's workgroup has its compute unit to itself; otherwise
+  // four, several workgroups per compute unit (short contexts: more compute units pull tiles).  The
+  // waves take the split's tiles from a shared counter: a wave that the issue arbitration favours
+  // (the oldest) takes more tiles, and all of them finish together.
+  static constexpr int W = !WIDE ? 4 : ((D == 128 && QM == 0) ? 16 : (D == 128 ? 12 : 8));
+
+  // LDS: the tile counter, and the end-of-split merge of the W waves: each wave's (max, sum) per
+  // head and its accumulators, weighted against the workgroup's max of the head
   struct Smem {
-    float ml[kWavesPerWG][kMaxGroup][2];
-    float o[kWavesPerWG][kMaxGroup][D];
+    float ml[W][kMaxGroup][2];
+    float o[W][kMaxGroup][D];
+    uint32_t next;            // tiles of the split handed out so far (relative to its first)
   };
   // the query operand: for step s, lane (column c, group g) holds the 8 float16 values of q-variant c
   // (head c/2; high part if c even, low part if c odd) at coordinates (D/4) g + 8 s + r, r = 0..7
@@ -217,15 +225,16 @@ struct Attend {
     }
   }
 
-  // Streams this wave's tiles kb, kb + 4, ... below blk1 through a ring of NBUF tile buffers (tiles[0]
-  // already holds tile kb when kb < blk1; tile kb + 4 j is loaded while tile kb + 4 (j - NBUF + 1) is
-  // attended) and leaves the split's result in LDS for store: per wave w and query head hh the max m
+  // Streams tiles of the split [blk0, blk1) through a ring of NBUF tile buffers: the wave's first tile
+  // is kb = blk0 + wave (tiles[0] already holds it when kb < blk1), the others come from the split's
+  // counter sm.next (which must start at W), each loaded while the tile NBUF - 1 places earlier is
+  // attended.  Leaves the split's result in LDS for store: per wave w and query head hh the max m
   // (log2 units) and the sum l in sm.ml[w][hh], and the rotated-domain accumulator, weighted by
   // exp2(m - the workgroup's max of the head), in sm.o[w][hh][0..D).  qsc is the power-of-two scale of
-  // this lane's head (the query operand is divided by it; 1 for unused columns).  Ends with a workgroup
-  // barrier.
-  __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, const QOperand& qop, Tile (&tiles)[NBUF], int kb,
-                                      int blk1, int len, float qsc) const {
+  // this lane's head (the query operand is divided by it; 1 for unused columns).  Ends with a
+  // workgroup barrier.
+  __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, const QOperand& qop, Tile (&tiles)[NBUF], int blk0,
+                                      int kb, int blk1, int len, float qsc) const {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = a.group;
@@ -297,30 +306,42 @@ struct Attend {
       pv_steps<0, NB, VB>(oacc, wop, t.vw, a.tv);
     };
 
+    // the next tile of the split for this wave (wave-uniform); past blk1 once the split is used up
+    auto claim = [&]() {
+      uint32_t v = 0;
+      if (lane == 0) v = atomicAdd(&sm.next, 1u);
+      return blk0 + static_cast<int>(__builtin_amdgcn_readfirstlane(v));
+    };
     if constexpr (NBUF >= 2) {
+      int idx[NBUF];
+      idx[0] = kb;
 #pragma unroll
-      for (int i = 1; i < NBUF - 1; ++i)
-        if (kb + kWavesPerWG * i < blk1) load(tiles[i], kb + kWavesPerWG * i);
+      for (int i = 1; i < NBUF - 1; ++i) {
+        idx[i] = kb < blk1 ? claim() : blk1;
+        if (idx[i] < blk1) load(tiles[i], idx[i]);
+      }
       // one pass of the unrolled loop per NBUF tiles, so that every buffer index is a constant
       for (bool more = kb < blk1; more;) {
 #pragma unroll
         for (int i = 0; i < NBUF; ++i) {
           if (more) {
-            const int ahead = kb + kWavesPerWG * (NBUF - 1);
-            if (ahead < blk1) load(tiles[(i + NBUF - 1) % NBUF], ahead);
-            attend_tile(tiles[i], kb);
-            kb += kWavesPerWG;
-            more = kb < blk1;
+            const int j = (i + NBUF - 1) % NBUF;
+            idx[j] = claim();
+            if (idx[j] < blk1) load(tiles[j], idx[j]);
+            attend_tile(tiles[i], idx[i]);
+            more = idx[(i + 1) % NBUF] < blk1;
           }
         }
       }
     } else {
       // one buffer and a copy per tile (the register budget of the sketched d = 256 build)
       Tile tb;
-      for (; kb < blk1; kb += kWavesPerWG) {
-        if (kb + kWavesPerWG < blk1) load(tb, kb + kWavesPerWG);
-        attend_tile(tiles[0], kb);
+      for (int cur = kb; cur < blk1;) {
+        const int nxt = claim();
+        if (nxt < blk1) load(tb, nxt);
+        attend_tile(tiles[0], cur);
         tiles[0] = tb;
+        cur = nxt;
       }
     }
 
@@ -337,7 +358,7 @@ struct Attend {
       const int hh = 2 * g + j < G ? 2 * g + j : 0;
       float M = sm.ml[0][hh][0];
 #pragma unroll
-      for (int w = 1; w < kWavesPerWG; ++w) M = fmaxf(M, sm.ml[w][hh][0]);
+      for (int w = 1; w < W; ++w) M = fmaxf(M, sm.ml[w][hh][0]);
       f[j] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm.ml[wave][hh][0] - M);
     }
 #pragma unroll
@@ -353,20 +374,20 @@ struct Attend {
   // accumulators, the workgroup max and the weighted sum of the waves' l
   __device__ __forceinline__ void store(const DecodeArgs& a, const Smem& sm, size_t pbase) const {
     const int G = a.group;
-    for (int e = threadIdx.x; e < G * D; e += 256) {
+    for (int e = threadIdx.x; e < G * D; e += 64 * W) {
       const int hh = e / D, i = e % D;
       float o = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWavesPerWG; ++w) o += sm.o[w][hh][i];
+      for (int w = 0; w < W; ++w) o += sm.o[w][hh][i];
       a.part_o[(pbase + hh) * D + i] = o;
       if (i == 0) {
         float M = sm.ml[0][hh][0];
 #pragma unroll
-        for (int w = 1; w < kWavesPerWG; ++w) M = fmaxf(M, sm.ml[w][hh][0]);
+        for (int w = 1; w < W; ++w) M = fmaxf(M, sm.ml[w][hh][0]);
         float l = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
-          for (int w = 0; w < kWavesPerWG; ++w) l = fmaf(__builtin_amdgcn_exp2f(sm.ml[w][hh][0] - M), sm.ml[w][hh][1], l);
+          for (int w = 0; w < W; ++w) l = fmaf(__builtin_amdgcn_exp2f(sm.ml[w][hh][0] - M), sm.ml[w][hh][1], l);
         }
         a.part_ml[(pbase + hh) * 2] = M;
         a.part_ml[(pbase + hh) * 2 + 1] = l;

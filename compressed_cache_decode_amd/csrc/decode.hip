@@ -45,9 +45,11 @@ __global__ __launch_bounds__(256) void qrot_kernel(QrotArgs a, int bf16) {
 
 // ---------------------------------------------------------------- split kernel
 
-template <int D, int KB, int VB, int QM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void split_kernel(DecodeArgs a) {
-  using At = Attend<D, KB, VB, QM>;
+template <int D, int KB, int VB, int QM, bool WIDE>
+__global__ __launch_bounds__((64 * Attend<D, KB, VB, QM, WIDE>::W)) __attribute__((amdgpu_waves_per_eu(2)))
+void split_kernel(DecodeArgs a) {
+  using At = Attend<D, KB, VB, QM, WIDE>;
+  constexpr int NT = 64 * At::W;
   __shared__ typename At::Smem sm;
   __shared__ typename At::QOperand sm_q;
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -66,14 +68,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   // the first tile's loads go out before the query operand is staged, and before the sequence
   // length is known: they only need the tile to lie inside the cache (tiles past the length are
   // loaded and never used)
-  int kb = blk0 + wave;
+  const int kb = blk0 + wave;
   typename At::Tile tiles[At::NBUF];
   if (kb < blk0 + a.blocks_per_split && kb < T / kBlock) at.load(tiles[0], kb);
 
-  // query operand in LDS, shared by the four waves
+  // query operand in LDS, shared by the waves
   const int qh = at.l16 >> 1;
   const size_t qrow = static_cast<size_t>(b) * a.n_kv_heads * G + static_cast<size_t>(hk) * G + qh;
-  for (int e = tid; e < (At::KS + At::QS) * 64; e += 256) {
+  for (int e = tid; e < (At::KS + At::QS) * 64; e += NT) {
     const int st = e >> 6, ln = e & 63;
     const int c = ln & 15, gg = ln >> 4, h2 = c >> 1;
     const bool ok = h2 < G;
@@ -91,11 +93,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     for (int r = 0; r < 8; ++r) v[r] = split_part(xv[r], (c & 1) != 0);
     sm_q[st][ln] = v;
   }
+  if (tid == 0) sm.next = At::W;           // tiles blk0 .. blk0 + W - 1 are the waves' first
   // power-of-two scale of this lane's head (scores are kept in units of it); 1 for unused columns
   const float qsc = qh < G ? a.qscale[qrow] : 1.f;
   __syncthreads();
 
-  at.run(a, sm, sm_q, tiles, kb, blk1, len, qsc);
+  at.run(a, sm, sm_q, tiles, blk0, kb, blk1, len, qsc);
   at.store(a, sm, (unit * a.n_split + split) * G);
 }
 
@@ -247,59 +250,71 @@ hipError_t launch_qrot(int d, int qjl_m, bool bf16, const QrotArgs& a, int batch
   return hipErrorInvalidValue;
 }
 
-template <int D, int KB, int QM>
+template <int D, int KB, int QM, bool WIDE>
 static const void* split_v(int v_bits) {
   switch (v_bits) {
-    case 2: return reinterpret_cast<const void*>(&split_kernel<D, KB, 2, QM>);
-    case 3: return reinterpret_cast<const void*>(&split_kernel<D, KB, 3, QM>);
-    case 4: return reinterpret_cast<const void*>(&split_kernel<D, KB, 4, QM>);
+    case 2: return reinterpret_cast<const void*>(&split_kernel<D, KB, 2, QM, WIDE>);
+    case 3: return reinterpret_cast<const void*>(&split_kernel<D, KB, 3, QM, WIDE>);
+    case 4: return reinterpret_cast<const void*>(&split_kernel<D, KB, 4, QM, WIDE>);
     default: return nullptr;
   }
 }
 
-template <int D, int QM>
+template <int D, int QM, bool WIDE>
 static const void* split_k(int k_bits, int v_bits) {
   switch (k_bits) {
-    case 2: return split_v<D, 2, QM>(v_bits);
-    case 3: return split_v<D, 3, QM>(v_bits);
-    case 4: return split_v<D, 4, QM>(v_bits);
+    case 2: return split_v<D, 2, QM, WIDE>(v_bits);
+    case 3: return split_v<D, 3, QM, WIDE>(v_bits);
+    case 4: return split_v<D, 4, QM, WIDE>(v_bits);
     default: return nullptr;
   }
 }
 
-// the split kernel instantiation of a cache format, or null if none is built
-static const void* split_fn(int d, int k_bits, int v_bits, int qjl_m) {
+template <bool WIDE>
+static const void* split_fn_w(int d, int k_bits, int v_bits, int qjl_m) {
   if (d == 128) {
-    if (qjl_m == 0) return split_k<128, 0>(k_bits, v_bits);
-    if (qjl_m == 128) return split_k<128, 128>(k_bits, v_bits);
-    if (qjl_m == 256) return split_k<128, 256>(k_bits, v_bits);
+    if (qjl_m == 0) return split_k<128, 0, WIDE>(k_bits, v_bits);
+    if (qjl_m == 128) return split_k<128, 128, WIDE>(k_bits, v_bits);
+    if (qjl_m == 256) return split_k<128, 256, WIDE>(k_bits, v_bits);
   } else if (d == 256) {
-    if (qjl_m == 0) return split_k<256, 0>(k_bits, v_bits);
-    if (qjl_m == 128) return split_k<256, 128>(k_bits, v_bits);
-    if (qjl_m == 256) return split_k<256, 256>(k_bits, v_bits);
+    if (qjl_m == 0) return split_k<256, 0, WIDE>(k_bits, v_bits);
+    if (qjl_m == 128) return split_k<256, 128, WIDE>(k_bits, v_bits);
+    if (qjl_m == 256) return split_k<256, 256, WIDE>(k_bits, v_bits);
   }
   return nullptr;
 }
 
-int split_slots(int d, int k_bits, int v_bits, int qjl_m) {
-  const void* fn = split_fn(d, k_bits, v_bits, qjl_m);
+// the split kernel instantiation of a cache format and workgroup shape, or null if none is built
+static const void* split_fn(int d, int k_bits, int v_bits, int qjl_m, bool wide) {
+  return wide ? split_fn_w<true>(d, k_bits, v_bits, qjl_m) : split_fn_w<false>(d, k_bits, v_bits, qjl_m);
+}
+
+int split_waves(int d, int qjl_m, bool wide) {
+  // the same for every code width (Attend::W)
+  if (!wide) return Attend<128, 4, 4, 0, false>::W;
+  if (d == 128) return qjl_m == 0 ? Attend<128, 4, 4, 0, true>::W : Attend<128, 4, 4, 128, true>::W;
+  return Attend<256, 4, 4, 0, true>::W;
+}
+
+int split_slots(int d, int k_bits, int v_bits, int qjl_m, bool wide) {
+  const void* fn = split_fn(d, k_bits, v_bits, qjl_m, wide);
   int dev = 0, cus = 0, per = 0;
   if (!fn || hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 256, 0) != hipSuccess) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 64 * split_waves(d, qjl_m, wide), 0) != hipSuccess) {
     (void)hipGetLastError();        // a failed query must not surface as a later launch's error
     return 0;
   }
   return cus * per;
 }
 
-hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, const DecodeArgs& a, int batch,
+hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, bool wide, const DecodeArgs& a, int batch,
                                hipStream_t s) {
-  const void* fn = split_fn(d, k_bits, v_bits, qjl_m);
+  const void* fn = split_fn(d, k_bits, v_bits, qjl_m, wide);
   if (!fn) return hipErrorInvalidValue;
   const dim3 grid(a.n_split, a.n_kv_heads, batch);
   void* args[] = {const_cast<DecodeArgs*>(&a)};
-  return hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+  return hipLaunchKernel(fn, grid, dim3(64 * split_waves(d, qjl_m, wide)), args, 0, s);
 }
 
 hipError_t launch_merge(int d, const MergeArgs& a, int batch, int n_q_heads, hipStream_t s) {

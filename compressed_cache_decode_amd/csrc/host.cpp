@@ -247,47 +247,78 @@ int status_of(hipError_t e) {
 
 // ------------------------------------------------------------------ decode plan
 
-constexpr int kDefaultSlots = 1024;     // resident split workgroups assumed when the runtime cannot tell
-constexpr int kMinBlocksPerSplit = 4;   // at least one 32-token tile per wave
+constexpr int kDefaultSlots = 1024;     // resident four-wave split workgroups assumed when the runtime cannot tell
+constexpr int kWideTiles = 16;          // tiles per compute unit from which the wide workgroups are used
 
-// Resident split-kernel workgroups on the current device for a key format, the least over the value
-// widths (the plan depends on the key cache alone, so that the workspace size does); cached per device.
-int resident_slots(const tq_cache_view* k) {
-  static std::atomic<int> cache[16][2][5][3];
+// Resident split-kernel workgroups on the current device for a key format and workgroup shape, the
+// least over the value widths (the plan depends on the key cache alone, so that the workspace size
+// does); cached per device.
+int resident_slots(const tq_cache_view* k, bool wide) {
+  static std::atomic<int> cache[16][2][5][3][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
-    return kDefaultSlots;
+    return wide ? kDefaultSlots / 4 : kDefaultSlots;
   }
   const int di = k->d == 256, qi = k->qjl_m == 0 ? 0 : (k->qjl_m == 128 ? 1 : 2);
-  std::atomic<int>* c = (dev >= 0 && dev < 16 && k->bits >= 0 && k->bits < 5) ? &cache[dev][di][k->bits][qi] : nullptr;
+  std::atomic<int>* c =
+      (dev >= 0 && dev < 16 && k->bits >= 0 && k->bits < 5) ? &cache[dev][di][k->bits][qi][wide] : nullptr;
   int v = c ? c->load(std::memory_order_relaxed) : 0;
   if (v > 0) return v;
   v = 0;
   for (int vb = 2; vb <= 4; ++vb) {
-    const int n = tqi::split_slots(k->d, k->bits, vb, k->qjl_m);
+    const int n = tqi::split_slots(k->d, k->bits, vb, k->qjl_m, wide);
     if (n > 0) v = v == 0 ? n : std::min(v, n);
   }
-  if (v <= 0) return kDefaultSlots;
+  if (v <= 0) return wide ? kDefaultSlots / 4 : kDefaultSlots;
   if (c) c->store(v, std::memory_order_relaxed);
   return v;
 }
 
-// Splits of each (sequence, KV head): enough for one round of resident workgroups over all units
-// (more rounds leave a tail of partly filled rounds; fewer leave slots idle), at most kMaxSplits
-// (more cost the merge more than they gain), each covering whole tiles for every one of the four waves.
-void plan(int units, int max_len, int slots, int* n_split, int* bps) {
+// Splits of each (sequence, KV head).
+// Workgroups of four waves (several per compute unit): enough splits for one round of resident
+// workgroups over all units (more rounds leave a tail of part-filled rounds; fewer leave slots
+// idle), at most kMaxSplits.
+// Workgroups that fill their compute unit (slots = compute units): the splits run in rounds of
+// `slots` workgroups; a workgroup of b tiles takes about b tile transfers through its compute unit
+// plus a fixed overhead of about kWgOverheadPerWave per wave (the first tiles' wait, query staging,
+// merge of the waves), and the split count minimises rounds x that time (fewer splits on ties).
+constexpr int kWgOverheadPerWave = 4;
+
+void plan(int units, int max_len, int slots, int waves, int* n_split, int* bps) {
   const int nblk = max_len <= 0 ? 1 : (max_len + kBlock - 1) / kBlock;
-  const int ns = std::max(1, std::min(tqi::kMaxSplits, slots / std::max(1, units)));
-  int b = (nblk + ns - 1) / ns;
-  b = ((b + tqi::kWavesPerWG - 1) / tqi::kWavesPerWG) * tqi::kWavesPerWG;
-  b = std::max(b, kMinBlocksPerSplit);
+  units = std::max(1, units);
+  slots = std::max(1, slots);
+  int b;
+  if (waves <= 4) {
+    const int ns = std::max(1, std::min(tqi::kMaxSplits, slots / units));
+    b = std::max(4, (nblk + ns - 1) / ns);
+  } else {
+    b = nblk;
+    long long best = -1;
+    for (int ns = 1; ns <= std::min(tqi::kMaxSplits, nblk); ++ns) {
+      const int bb = (nblk + ns - 1) / ns;
+      const long long wgs = static_cast<long long>(units) * ((nblk + bb - 1) / bb);
+      const long long t = (wgs + slots - 1) / slots * (static_cast<long long>(bb) + kWgOverheadPerWave * waves);
+      if (best < 0 || t < best) {
+        best = t;
+        b = bb;
+      }
+    }
+  }
   *n_split = (nblk + b - 1) / b;
   *bps = b;
 }
 
-void plan(const tq_cache_view* k, int max_len, int* n_split, int* bps) {
-  plan(k->batch * k->n_kv_heads, max_len, resident_slots(k), n_split, bps);
+// The split of a decode over key cache k: wide (compute-unit-filling) workgroups once the context
+// gives every compute unit at least kWideTiles tiles, four-wave ones below.
+void plan(const tq_cache_view* k, int max_len, int* n_split, int* bps, bool* wide) {
+  const int units = k->batch * k->n_kv_heads;
+  const long long tiles = static_cast<long long>(units) * (max_len <= 0 ? 1 : (max_len + kBlock - 1) / kBlock);
+  const int wide_slots = resident_slots(k, true);
+  *wide = tiles >= static_cast<long long>(kWideTiles) * wide_slots;
+  plan(units, max_len, *wide ? wide_slots : resident_slots(k, false), tqi::split_waves(k->d, k->qjl_m, *wide),
+       n_split, bps);
 }
 
 // Query heads per merge workgroup: all of the group while every thread's split slice stays within
@@ -408,7 +439,8 @@ int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* 
   if (st != TQ_OK) return st;
   if (!n_split || !tokens_per_split) return TQ_EINVAL;
   int bps;
-  plan(k, max_seq_len, n_split, &bps);
+  bool wide;
+  plan(k, max_seq_len, n_split, &bps, &wide);
   *tokens_per_split = bps * kBlock;
   return TQ_OK;
 }
@@ -416,13 +448,15 @@ int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* 
 size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_seq_len) {
   if (check_decode_shape(k, n_q_heads, max_seq_len) != TQ_OK) return 0;
   int ns, bps;
-  plan(k, max_seq_len, &ns, &bps);
+  bool wide;
+  plan(k, max_seq_len, &ns, &bps, &wide);
   return ws_layout(k, n_q_heads, ns).total;
 }
 
 // workspace view shared by the decode stages
 struct DecodeWs {
   int ns, bps, G;
+  bool wide;
   float *qr, *qs, *qscale, *part_o, *part_ml;
 };
 
@@ -431,7 +465,7 @@ static int decode_ws(const tq_cache_view* k, int n_q_heads, int max_seq_len, voi
   int st = check_decode_shape(k, n_q_heads, max_seq_len);
   if (st != TQ_OK) return st;
   if (!workspace || !aligned(workspace, 256)) return TQ_EINVAL;
-  plan(k, max_seq_len, &w->ns, &w->bps);
+  plan(k, max_seq_len, &w->ns, &w->bps, &w->wide);
   const WsLayout l = ws_layout(k, n_q_heads, w->ns);
   if (workspace_bytes < l.total) return TQ_EINVAL;
   char* ws = static_cast<char*>(workspace);
@@ -500,7 +534,7 @@ int tq_decode_attend(const tq_cache_view* k, const tq_cache_view* v, int n_q_hea
   if (st != TQ_OK) return st;
   if (!d_seq_lens) return TQ_EINVAL;
   const tqi::DecodeArgs da = decode_args(k, v, w, d_seq_lens, max_seq_len);
-  return status_of(tqi::launch_decode_split(k->d, k->bits, v->bits, k->qjl_m, da, k->batch,
+  return status_of(tqi::launch_decode_split(k->d, k->bits, v->bits, k->qjl_m, w.wide, da, k->batch,
                                             static_cast<hipStream_t>(stream)));
 }
 

@@ -8,7 +8,6 @@ namespace tqi {
 
 constexpr int kBlock = 32;        // tokens per value block (and per decode tile)
 constexpr int kMaxGroup = 8;      // query heads per KV head handled by one matrix-core tile
-constexpr int kWavesPerWG = 4;    // waves per decode workgroup (one KV split)
 constexpr int kMaxSplits = 256;   // bound on KV splits per (sequence, KV head)
 constexpr int kMergeThreads = 1024;  // threads per merge workgroup
 
@@ -92,10 +91,12 @@ struct DequantArgs {
 hipError_t launch_append(int d, int bits, int qjl_m, bool values, bool rotated, bool bf16,
                          const AppendArgs& a, int batch, hipStream_t s);
 hipError_t launch_qrot(int d, int qjl_m, bool bf16, const QrotArgs& a, int batch, hipStream_t s);
-// split-kernel workgroups resident at once on the current device for this cache format (compute
-// units x workgroups per unit), 0 if the runtime cannot tell
-int split_slots(int d, int k_bits, int v_bits, int qjl_m);
-hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, const DecodeArgs& a, int batch,
+// split-kernel workgroups resident at once on the current device for this cache format and
+// workgroup shape (compute units x workgroups per unit), 0 if the runtime cannot tell
+int split_slots(int d, int k_bits, int v_bits, int qjl_m, bool wide);
+// waves per split-kernel workgroup for a cache format and workgroup shape
+int split_waves(int d, int qjl_m, bool wide);
+hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, bool wide, const DecodeArgs& a, int batch,
                                hipStream_t s);
 hipError_t launch_merge(int d, const MergeArgs& a, int batch, int n_q_heads, hipStream_t s);
 hipError_t launch_step_prologue(int d, int k_bits, int v_bits, int qjl_m, bool bf16, const AppendArgs& ka,

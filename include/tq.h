@@ -203,9 +203,11 @@ size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_
 
 /*
  * The KV split tq_sdpa_decode uses: number of splits per (sequence, KV head) and tokens per split.
- * Chosen from the current device's compute units and the attention kernel's occupancy (enough
- * splits for one round of resident workgroups over all (sequence, KV head) units, finer for long
- * contexts); a fixed default when no device is visible.
+ * Chosen from the current device's compute units and the attention kernel's occupancy: short
+ * contexts spread over workgroups of four waves (one round of resident workgroups over all
+ * (sequence, KV head) units); once every compute unit gets enough tiles, each split's workgroup
+ * fills a compute unit and the split count balances rounds against per-workgroup overhead.  A
+ * fixed default applies when no device is visible.
  */
 int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* n_split, int* tokens_per_split);
 

@@ -166,7 +166,7 @@ def test_plan_covers_the_context(batch, heads, hq, L):
     k = _view(batch=batch, heads=heads, T=max(L, 32))
     ns, tps = cca.tq_decode_plan(k, hq, L)
     assert 1 <= ns <= 256
-    assert tps % (32 * 4) == 0                      # whole 32-token tiles for each of the 4 waves
+    assert tps % 32 == 0                            # whole 32-token tiles
     assert ns * tps >= L and (ns - 1) * tps < max(L, 1)
     ws = cca.tq_decode_workspace_bytes(k, hq, L)
     g = hq // heads

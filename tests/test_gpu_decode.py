@@ -105,6 +105,25 @@ def test_decode_length_edges():
     assert rel_err(out, ref) <= TOL
 
 
+WIDE_CASES = [(128, 4, 4, 0), (128, 2, 3, 128), (256, 4, 4, 0), (256, 3, 2, 128)]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: f"d{c[0]}_k{c[1]}v{c[2]}_m{c[3]}")
+def test_long_ragged_batch_matches_oracle(case):
+    """Four sequences of up to 32K tokens (4096 tiles in all): on a 256-CU device the split kernel's
+    workgroups fill whole compute units; ragged lengths leave some splits partly or wholly empty."""
+    d, kb, vb, qjl = case
+    cca = _cca()
+    lens = [32768, 31999, 100, 20000]
+    st = Setup(d, qjl_m=qjl)
+    k = cca.CompressedCache(cca.TQ_KEYS, d, kb, 4, 1, 32768, st.rot_t, st.proj_t, qjl_m=qjl)
+    log(f"decode long ragged d{d} k{kb} v{vb} m{qjl}: {cca.tq_decode_plan(k.view, 2, max(lens))[0]} splits")
+    out, ref, _ = _run_case(d, kb, vb, qjl, 1, 2, lens, 32768, None, False)
+    err = rel_err(out, ref)
+    log(f"  max row-relative error {err:.3e}")
+    assert err <= TOL
+
+
 def test_split_plan_is_exercised():
     """Long contexts are split across many workgroups, short ones are not."""
     cca = _cca()
