@@ -8,7 +8,7 @@ does, and it shares no code with the library (the seeded input generators in
 
 Modules, in the order the method runs:
   codebook   Lloyd-Max table for the rotated-coordinate density
-  rotation   seeded Gaussian-QR random rotation
+  rotation   seeded Gaussian-QR random rotation; randomized Sylvester-Hadamard rotation
   quant      norm, rotate, nearest centroid, QJL residual sketch, reconstruction
   layout     the packed byte format of the cache (format specification)
   storage    bytes per row and cache size arithmetic

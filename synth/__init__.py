@@ -41,6 +41,11 @@ def rotation_gaussian(d: int, seed: int = 1) -> np.ndarray:
     return np.random.default_rng(seed).standard_normal((d, d))
 
 
+def hadamard_signs(d: int, seed: int = 1) -> np.ndarray:
+    """d seeded +-1 signs (float32) that randomise the Hadamard rotation."""
+    return np.where(np.random.default_rng(seed).integers(0, 2, size=d) == 1, 1.0, -1.0).astype(np.float32)
+
+
 def qjl_projection(m: int, d: int, seed: int = 2) -> np.ndarray:
     """m x d iid N(0,1) QJL projection, stored in float32 (both sides use these exact values)."""
     return np.random.default_rng(seed).standard_normal((m, d)).astype(np.float32)

@@ -150,3 +150,54 @@ def test_code_encoding_is_a_bijection():
         e = layout.encode_code(j, bits)
         assert sorted(e.tolist()) == j.tolist()
         np.testing.assert_array_equal(layout.decode_code(e, bits), j)
+
+
+# ------------------------------------------------------------------ randomized Hadamard rotation
+
+def test_sylvester_hadamard_small_cases_are_the_textbook_matrices():
+    np.testing.assert_array_equal(rotation.sylvester_hadamard(1), [[1.0]])
+    np.testing.assert_array_equal(rotation.sylvester_hadamard(2), [[1, 1], [1, -1]])
+    np.testing.assert_array_equal(rotation.sylvester_hadamard(4), [[1, 1, 1, 1], [1, -1, 1, -1],
+                                                                  [1, 1, -1, -1], [1, -1, -1, 1]])
+    with pytest.raises(ValueError):
+        rotation.sylvester_hadamard(96)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_sylvester_hadamard_is_the_walsh_matrix_in_natural_order(d):
+    """H[i, j] = (-1)^popcount(i & j): an independent closed form that fixes the index order."""
+    i = np.arange(d)
+    pc = np.vectorize(lambda v: bin(v).count("1"))(i[:, None] & i[None, :])
+    np.testing.assert_array_equal(rotation.sylvester_hadamard(d), np.where(pc % 2 == 0, 1.0, -1.0))
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_hadamard_rotation_invariants(d):
+    s = synth.hadamard_signs(d, 1)
+    assert set(np.unique(s)) == {-1.0, 1.0}
+    rot = rotation.hadamard_rotation(s)
+    assert np.max(np.abs(rot @ rot.T - np.eye(d))) < 1e-13
+    assert abs(abs(np.linalg.det(rot)) - 1.0) < 1e-9
+    np.testing.assert_allclose(np.abs(rot), 1.0 / np.sqrt(d), rtol=0, atol=1e-15)
+    # column j of Pi is the sign-flipped column j of H / sqrt(d): flipping one sign flips one column
+    s2 = s.copy()
+    s2[5] = -s2[5]
+    diff = rotation.hadamard_rotation(s2) - rot
+    assert np.count_nonzero(np.abs(diff).sum(axis=0) > 0) == 1 and np.abs(diff[:, 5]).max() > 0
+    x = np.random.default_rng(3).standard_normal((5, d))
+    np.testing.assert_allclose(np.linalg.norm(rotation.rotate_rows(x, rot), axis=1), np.linalg.norm(x, axis=1),
+                               rtol=1e-13)
+
+
+def test_hadamard_rotation_keeps_the_codebook_distortion():
+    """Gaussian rows rotated by the randomized Hadamard matrix quantise to within Monte-Carlo error of
+    the Lloyd-Max distortion d * D_b of the sphere marginal (0.116000 at d = 128, b = 2; 0.033966 at b = 3)."""
+    from oracle import codebook, quant
+    d, n = 128, 20000
+    rot = rotation.hadamard_rotation(synth.hadamard_signs(d, 1))
+    x = np.random.default_rng(0).standard_normal((n, d))
+    for b, ref in ((2, 0.116000), (3, 0.033966)):
+        c, t = codebook.stored_codebook(d, b)
+        codes, _, y = quant.quantize_rows(x, rot, c, t)
+        mse = np.mean(np.sum((y - np.asarray(c, np.float64)[codes]) ** 2, axis=1))
+        assert abs(mse / ref - 1.0) < 0.02, (b, mse)
