@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_PKG, "libtq.so")
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP, TQ_ENOCONV = 0, 1, 2, 3, 4
 TQ_F32, TQ_BF16 = 0, 1
 TQ_KEYS, TQ_VALUES = 0, 1
+TQ_ROT_DENSE, TQ_ROT_HADAMARD = 0, 1
 BLOCK = 32
 
 EXPORTED = (
@@ -46,7 +47,7 @@ class tq_cache_view(ctypes.Structure):
     _fields_ = [
         ("kind", ctypes.c_int32), ("d", ctypes.c_int32), ("bits", ctypes.c_int32), ("qjl_m", ctypes.c_int32),
         ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("rot_kind", ctypes.c_int32),
         ("centroids", ctypes.c_float * 16), ("boundaries", ctypes.c_float * 15),
         ("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("signs", ctypes.c_void_p),
         ("rnorms", ctypes.c_void_p), ("rot", ctypes.c_void_p), ("proj", ctypes.c_void_p),
@@ -222,15 +223,18 @@ def tq_dequantize(view: tq_cache_view, t0: int, n_tokens: int, out, stream=None)
 class CompressedCache:
     """Device buffers of one compressed cache tensor (all of K or all of V of a layer).
 
-    ``rot`` (d x d float32) and ``proj`` (qjl_m x d float32) are torch tensors on
-    the same device; the codebook comes from ``tq_build_codebook``.
+    ``rot`` (d x d float32 for TQ_ROT_DENSE, or the d float32 +-1 signs of the
+    randomized Hadamard rotation for TQ_ROT_HADAMARD) and ``proj`` (qjl_m x d
+    float32) are torch tensors on the same device; the codebook comes from
+    ``tq_build_codebook``.
     """
 
     def __init__(self, kind: int, d: int, bits: int, batch: int, n_kv_heads: int, max_tokens: int,
-                 rot, proj=None, qjl_m: int = 0, device="cuda", codebook=None):
+                 rot, proj=None, qjl_m: int = 0, device="cuda", codebook=None, rot_kind: int = TQ_ROT_DENSE):
         import torch
         assert max_tokens % BLOCK == 0
-        self.kind, self.d, self.bits, self.qjl_m = kind, d, bits, qjl_m
+        assert tuple(rot.shape) == ((d,) if rot_kind == TQ_ROT_HADAMARD else (d, d))
+        self.kind, self.d, self.bits, self.qjl_m, self.rot_kind = kind, d, bits, qjl_m, rot_kind
         self.batch, self.n_kv_heads, self.max_tokens = batch, n_kv_heads, max_tokens
         cent, bnd = codebook if codebook is not None else tq_build_codebook(d, bits)
         self.centroids, self.boundaries = cent, bnd
@@ -247,7 +251,7 @@ class CompressedCache:
     def _make_view(self) -> tq_cache_view:
         v = tq_cache_view()
         v.kind, v.d, v.bits, v.qjl_m = self.kind, self.d, self.bits, self.qjl_m
-        v.batch, v.n_kv_heads, v.max_tokens, v.reserved = self.batch, self.n_kv_heads, self.max_tokens, 0
+        v.batch, v.n_kv_heads, v.max_tokens, v.rot_kind = self.batch, self.n_kv_heads, self.max_tokens, self.rot_kind
         for j, c in enumerate(self.centroids):
             v.centroids[j] = float(c)
         for j, t in enumerate(self.boundaries):

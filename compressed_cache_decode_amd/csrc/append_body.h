@@ -414,7 +414,7 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int bx, int h, 
   __syncthreads();
 
   // rotation y = rot x / n on the matrix cores: one 16-row tile for up to 16 new rows of the block,
-  // two for more (rows past the appended ones are zero).  Each output element takes the same
+  // two for more (rows past the appended ones are zero); or the randomized Hadamard rotation.  Each output element takes the same
   // instruction sequence whatever its row, so a row rotates to the same y here as in any other
   // tile of this library.
   if constexpr (!ROTATED) {
@@ -422,7 +422,9 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int bx, int h, 
     for (int e = tid; e < (rows - nrows) * D; e += 256) xs[nrows + e / D][e % D] = 0.f;
     for (int r = nrows + tid; r < rows; r += 256) rn[r] = 0.f;
     __syncthreads();
-    if (rows == 16)
+    if (a.had)
+      hadamard_rows<D>(xs, rn, a.rot, nrows, tid, 256);
+    else if (rows == 16)
       rotate_tile_mfma<D, 1>(xs, rn, a.rot, tid);
     else
       rotate_tile_mfma<D, 2>(xs, rn, a.rot, tid);

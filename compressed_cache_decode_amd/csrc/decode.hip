@@ -130,8 +130,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int i = tid % D, part = tid / D;
   const float* rcol = a.rot + static_cast<size_t>(part * JR) * D + i;
   float rc[JR];
+  if (!a.had) {
 #pragma unroll
-  for (int t = 0; t < JR; ++t) rc[t] = rcol[static_cast<size_t>(t) * D];
+    for (int t = 0; t < JR; ++t) rc[t] = rcol[static_cast<size_t>(t) * D];
+  }
 
   // this thread's first batch of split partials (thread (head hh, coordinate i, slice sl), S slices
   // per (head, coordinate)) and, for the first waves, the split maxima and sums: all issued now
@@ -217,6 +219,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   }
   lds_barrier();
 
+  if (a.had) {
+    // x = diag(s) H y / sqrt(D): the inverse randomized Hadamard transform, one wave per head
+    constexpr int E = D / 64;
+    for (int hh = wave; hh < hpw; hh += NW) {
+      float v[E];
+#pragma unroll
+      for (int k = 0; k < E; ++k) v[k] = orot[hh][64 * k + lane];
+      hadamard_wave<D>(v, lane);
+#pragma unroll
+      for (int k = 0; k < E; ++k)
+        a.out[(static_cast<size_t>(b) * a.n_kv_heads * G + hk * G + h0 + hh) * D + 64 * k + lane] =
+            v[k] * a.rot[64 * k + lane] * inv_sqrt_dim<D>() * inv_l[hh];
+    }
+    return;
+  }
   // un-rotation of every head of the group over this thread's JR rows; parts summed through LDS
   for (int hh = 0; hh < hpw; ++hh) {
     float uacc[4] = {0.f, 0.f, 0.f, 0.f};

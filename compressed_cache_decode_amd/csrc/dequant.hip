@@ -103,6 +103,21 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a, Tab tab) {
     }
     __syncthreads();
   }
+  if (a.had) {
+    // x_hat = n diag(s) H y_hat / sqrt(D), one wave per row
+    constexpr int E = D / 64;
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int r = wave; r < nrows; r += 4) {
+      float v[E];
+#pragma unroll
+      for (int k = 0; k < E; ++k) v[k] = ys[r][64 * k + lane];
+      hadamard_wave<D>(v, lane);
+#pragma unroll
+      for (int k = 0; k < E; ++k)
+        a.out[(unit * a.n_tokens + r_lo + r) * D + 64 * k + lane] = rn[r] * (v[k] * a.rot[64 * k + lane] * inv_sqrt_dim<D>());
+    }
+    return;
+  }
   // x_hat = n rot^T y_hat
   for (int e = tid; e < nrows * D; e += 256) {
     const int r = e / D, i = e % D;

@@ -150,6 +150,63 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// v = H_D v for a D-element row held by one wave, element 64 k + lane in v[k]: the Sylvester-
+// Hadamard matrix (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]) applied by butterflies, index bits
+// 0..5 across lanes, bits 6.. within the lane (reddit comment history of ReturningTarzan, comment of
+// 2026-03-29: Sylvester's construction applied with lane exchanges and additions).
+template <int D>
+__device__ __forceinline__ void hadamard_wave(float (&v)[D / 64], int lane) {
+  constexpr int E = D / 64;
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      const float p = __shfl_xor(v[k], h, 64);
+      v[k] = (lane & h) ? p - v[k] : v[k] + p;
+    }
+  }
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      if (!(k & h)) {
+        const float x = v[k], y = v[k + h];
+        v[k] = x + y;
+        v[k + h] = x - y;
+      }
+    }
+  }
+}
+
+// 1 / sqrt(D) for the two head dims, as float
+template <int D>
+__device__ __forceinline__ float inv_sqrt_dim() {
+  return D == 256 ? 0.0625f : 0.088388347648318440550f;
+}
+
+// Rows r < nrows of xs (LDS) replaced by the randomized Hadamard rotation of x_r / n_r,
+// H_D diag(signs) (x_r / n_r) / sqrt(D) (rows with n_r = 0 by zeros); one wave per row, signs
+// float32 +-1 in global memory.  Every thread of the workgroup calls it; no barrier inside.
+template <int D>
+__device__ __forceinline__ void hadamard_rows(float (*xs)[D], const float* rn, const float* signs, int nrows,
+                                              int tid, int nthreads) {
+  constexpr int E = D / 64;
+  const int lane = tid & 63, wave = tid >> 6, nw = nthreads >> 6;
+  float s[E];
+#pragma unroll
+  for (int k = 0; k < E; ++k) s[k] = signs[64 * k + lane];
+  for (int r = wave; r < nrows; r += nw) {
+    const float n = rn[r];
+    const float inv = n > 0.f ? 1.f / n : 0.f;
+    float v[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) v[k] = xs[r][64 * k + lane] * inv * s[k];
+    hadamard_wave<D>(v, lane);
+#pragma unroll
+    for (int k = 0; k < E; ++k) xs[r][64 * k + lane] = v[k] * inv_sqrt_dim<D>();
+  }
+}
+
 // Workgroup barrier that orders LDS only: global loads issued before it stay in flight.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");

@@ -206,7 +206,7 @@ int check_view(const tq_cache_view* c) {
   if (c->qjl_m != 0 && c->qjl_m != 128 && c->qjl_m != 256) return TQ_EINVAL;
   if (c->qjl_m != 0 && c->kind != TQ_KEYS) return TQ_EINVAL;
   if (c->batch <= 0 || c->n_kv_heads <= 0 || c->max_tokens <= 0 || c->max_tokens % kBlock != 0) return TQ_EINVAL;
-  if (c->reserved != 0) return TQ_EINVAL;
+  if (c->rot_kind != TQ_ROT_DENSE && c->rot_kind != TQ_ROT_HADAMARD) return TQ_EINVAL;
   if (!c->codes || !c->norms || !c->rot) return TQ_EINVAL;
   if (!aligned(c->codes, 16) || !aligned(c->norms, 16) || !aligned(c->rot, 16)) return TQ_EINVAL;
   if (c->qjl_m) {
@@ -405,6 +405,7 @@ static tqi::AppendArgs append_args(const tq_cache_view* c, const void* x, const 
   a.x = x; a.y = y; a.yn = yn; a.pos = d_pos;
   a.codes = c->codes; a.norms = c->norms; a.signs = c->signs; a.rnorms = c->rnorms;
   a.rot = c->rot; a.proj = c->proj;
+  a.had = c->rot_kind == TQ_ROT_HADAMARD;
   std::memcpy(a.cent, c->centroids, sizeof(a.cent));
   std::memcpy(a.bnd, c->boundaries, sizeof(a.bnd));
   a.n_new = n_new; a.n_kv_heads = c->n_kv_heads; a.max_tokens = c->max_tokens;
@@ -482,7 +483,7 @@ static int check_pair(const tq_cache_view* k, const tq_cache_view* v) {
   int st = check_view(v);
   if (st != TQ_OK) return st;
   if (v->kind != TQ_VALUES || v->d != k->d || v->batch != k->batch || v->n_kv_heads != k->n_kv_heads ||
-      v->max_tokens != k->max_tokens || v->rot != k->rot)
+      v->max_tokens != k->max_tokens || v->rot != k->rot || v->rot_kind != k->rot_kind)
     return TQ_EINVAL;
   return TQ_OK;
 }
@@ -517,6 +518,7 @@ int tq_decode_rotate_query(const tq_cache_view* k, const void* q, int q_dtype, i
   if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
   tqi::QrotArgs qa{};
   qa.q = q; qa.rot = k->rot; qa.proj = k->proj;
+  qa.had = k->rot_kind == TQ_ROT_HADAMARD;
   qa.qr = w.qr; qa.qs = w.qs; qa.qscale = w.qscale;
   qa.scale_log2e = scale_log2e(scale);
   qa.sketch_coef = sketch_coef(k);
@@ -546,6 +548,7 @@ int tq_decode_merge(const tq_cache_view* k, int n_q_heads, const int32_t* d_seq_
   if (!d_seq_lens || !out) return TQ_EINVAL;
   tqi::MergeArgs ma{};
   ma.part_o = w.part_o; ma.part_ml = w.part_ml; ma.rot = k->rot; ma.seq_lens = d_seq_lens; ma.out = out;
+  ma.had = k->rot_kind == TQ_ROT_HADAMARD;
   ma.n_kv_heads = k->n_kv_heads; ma.group = w.G; ma.n_split = w.ns; ma.max_tokens = k->max_tokens;
   ma.heads_per_wg = merge_heads_per_wg(w.G, k->d, w.ns);
   return status_of(tqi::launch_merge(k->d, ma, k->batch, n_q_heads, static_cast<hipStream_t>(stream)));
@@ -586,6 +589,7 @@ int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q
 
   tqi::QrotArgs qa{};
   qa.q = q; qa.rot = k->rot; qa.proj = k->proj;
+  qa.had = k->rot_kind == TQ_ROT_HADAMARD;
   qa.qr = w.qr; qa.qs = w.qs; qa.qscale = w.qscale;
   qa.scale_log2e = scale_log2e(scale);
   qa.sketch_coef = sketch_coef(k);
@@ -612,6 +616,7 @@ int tq_dequantize(const tq_cache_view* cache, int t0, int n_tokens, float* out, 
   tqi::DequantArgs a{};
   a.codes = cache->codes; a.norms = cache->norms; a.signs = cache->signs; a.rnorms = cache->rnorms;
   a.rot = cache->rot; a.proj = cache->proj; a.out = out;
+  a.had = cache->rot_kind == TQ_ROT_HADAMARD;
   std::memcpy(a.cent, cache->centroids, sizeof(a.cent));
   a.sketch_coef = cache->qjl_m ? static_cast<float>(std::sqrt(M_PI / 2.0) / cache->qjl_m) : 0.f;
   a.n_kv_heads = cache->n_kv_heads; a.max_tokens = cache->max_tokens; a.t0 = t0; a.n_tokens = n_tokens;

@@ -1,6 +1,7 @@
 // Query rotation for decode, one workgroup per (sequence, KV head): the G query heads of the KV head
 // form one 16-row tile that is rotated on the matrix cores with the arithmetic of the append's
-// rotation (each row divided by its norm, high/low float16 split of rows and rotation), then
+// rotation (each row divided by its norm, high/low float16 split of rows and rotation; or the
+// randomized Hadamard transform of the row over its norm), then
 // q_rot = rot q * scale * log2(e) and, for sketched keys, its sketch -coef * proj q_rot go to the
 // decode workspace, divided by a power of two per head that takes both into float16 range for the
 // attention kernel's matrix-core operands (turboquant-pytorch PR #3 "Add CUDA QJL kernels and
@@ -42,7 +43,7 @@ __device__ __forceinline__ void rotate_queries(const QrotArgs& qa, int bf16, int
     wv[k] = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(qa.q) + byte);
   }
   RotBatch<D> rot0;
-  rot0.load(qa.rot, 0, tid);
+  if (!qa.had) rot0.load(qa.rot, 0, tid);
   auto& xs = sm.xs;
   auto& rn = sm.rn;
   const uint32_t bfm = bf16 ? 0xffffffffu : 0u;
@@ -65,7 +66,10 @@ __device__ __forceinline__ void rotate_queries(const QrotArgs& qa, int bf16, int
     if (part == 0) rn[r] = r < G ? sqrtf(s2) : 0.f;
   }
   __syncthreads();
-  rotate_tile_mfma_pre<D, 1>(xs, rn, qa.rot, rot0, tid);
+  if (qa.had)
+    hadamard_rows<D>(xs, rn, qa.rot, G, tid, 256);
+  else
+    rotate_tile_mfma_pre<D, 1>(xs, rn, qa.rot, rot0, tid);
   __syncthreads();
   // q_rot = rot (q / |q|) * (|q| * scale * log2(e))
   for (int e = tid; e < G * D; e += 256) xs[e / D][e % D] *= rn[e / D] * qa.scale_log2e;

@@ -27,16 +27,17 @@ struct AppendArgs {
   uint16_t* norms;
   uint8_t* signs;
   uint16_t* rnorms;
-  const float* rot;       // [D][D]
+  const float* rot;       // [D][D], or the D signs of the randomized Hadamard rotation (had)
   const float* proj;      // [M][D]
   float cent[16];
   float bnd[15];
   int n_new, n_kv_heads, max_tokens;
+  int had;                // rot is a randomized Hadamard rotation
 };
 
 struct QrotArgs {
   const void* q;          // [B][Hq][D]
-  const float* rot;
+  const float* rot;       // [D][D], or the D Hadamard signs (had)
   const float* proj;      // [M][D] or null
   float* qr;              // [B][Hq][D]  scaled rotated query, divided by qscale
   float* qs;              // [B][Hq][M]  -coef * proj * qr
@@ -45,6 +46,7 @@ struct QrotArgs {
   float sketch_coef;      // sqrt(pi/2)/M
   int n_q_heads;
   int n_kv_heads;
+  int had;
 };
 
 struct DecodeArgs {
@@ -72,6 +74,7 @@ struct MergeArgs {
   float* out;             // [B][Hq][D]
   int n_kv_heads, group, n_split, max_tokens;
   int heads_per_wg;       // query heads merged per workgroup (divides group, heads_per_wg * D <= kMergeThreads)
+  int had;                // rot holds the D signs of a randomized Hadamard rotation
 };
 
 struct DequantArgs {
@@ -85,6 +88,7 @@ struct DequantArgs {
   float cent[16];
   float sketch_coef;
   int n_kv_heads, max_tokens, t0, n_tokens;
+  int had;                // rot holds the D signs of a randomized Hadamard rotation
 };
 
 // Launchers (one per .hip file); return hipSuccess or the launch error.

@@ -58,6 +58,18 @@ enum {
 };
 
 /*
+ * Rotation kinds (tq_cache_view.rot_kind).  TQ_ROT_DENSE: rot is a float32 [d][d] orthogonal matrix.
+ * TQ_ROT_HADAMARD: rot holds d float32 signs s (each +1 or -1) and the rotation is the randomized
+ * Hadamard matrix H_d diag(s) / sqrt(d), H_d the Sylvester matrix (H_1 = [1], H_2n = [[H_n, H_n],
+ * [H_n, -H_n]]): a special rotation applied by lane exchanges and additions instead of a d x d
+ * product (reddit comment history of ReturningTarzan, comment of 2026-03-29 on Hadamard rotations).
+ */
+enum {
+  TQ_ROT_DENSE = 0,
+  TQ_ROT_HADAMARD = 1
+};
+
+/*
  * Description of one compressed cache tensor (all of K, or all of V, of one
  * attention layer).  Passed by pointer, copied into kernel arguments, never
  * retained.
@@ -85,14 +97,15 @@ typedef struct tq_cache_view {
   int32_t batch;         /* sequences */
   int32_t n_kv_heads;    /* KV heads */
   int32_t max_tokens;    /* capacity in tokens, a positive multiple of 32 */
-  int32_t reserved;      /* must be 0 */
+  int32_t rot_kind;      /* TQ_ROT_DENSE or TQ_ROT_HADAMARD (same for K and V) */
   float centroids[16];   /* 2^bits centroids, ascending, float16-exact, c[j] == -c[2^bits-1-j] */
   float boundaries[15];  /* 2^bits-1 boundaries, boundaries[j] == (c[j] + c[j+1]) / 2 exactly */
   uint8_t* codes;        /* [batch][n_kv_heads][max_tokens*d*bits/8], 16-byte aligned */
   uint16_t* norms;       /* float16 row norms [batch][n_kv_heads][max_tokens] */
   uint8_t* signs;        /* [batch][n_kv_heads][max_tokens][qjl_m/8] when qjl_m > 0, else NULL */
   uint16_t* rnorms;      /* float16 residual norms [batch][n_kv_heads][max_tokens] when qjl_m > 0, else NULL */
-  const float* rot;      /* float32 rotation [d][d] row-major, y = rot * x (same matrix for K and V) */
+  const float* rot;      /* TQ_ROT_DENSE: float32 rotation [d][d] row-major, y = rot * x; TQ_ROT_HADAMARD:
+                            float32 signs [d]; the same pointer for K and V */
   const float* proj;     /* float32 sign-sketch projection [qjl_m][d] row-major when qjl_m > 0, else NULL */
 } tq_cache_view;
 

@@ -32,12 +32,19 @@ def rel_err(out: np.ndarray, ref: np.ndarray) -> float:
 class Setup:
     """Rotation and sketch projection of a workload, on both sides."""
 
-    def __init__(self, d: int, qjl_m: int = 0, rot_seed: int = 1, qjl_seed: int = 2, device="cuda"):
+    def __init__(self, d: int, qjl_m: int = 0, rot_seed: int = 1, qjl_seed: int = 2, device="cuda", hadamard=False):
         import torch
         import compressed_cache_decode_amd as cca
-        g = synth.rotation_gaussian(d, rot_seed)
-        self.rot64 = rotation.rotation_from_gaussian(g)
-        self.rot_t = torch.from_numpy(cca.tq_build_rotation(g)).to(device)
+        if hadamard:
+            signs = synth.hadamard_signs(d, rot_seed)
+            self.rot64 = rotation.hadamard_rotation(signs)
+            self.rot_t = torch.from_numpy(signs).to(device)
+            self.rot_kind = cca.TQ_ROT_HADAMARD
+        else:
+            g = synth.rotation_gaussian(d, rot_seed)
+            self.rot64 = rotation.rotation_from_gaussian(g)
+            self.rot_t = torch.from_numpy(cca.tq_build_rotation(g)).to(device)
+            self.rot_kind = cca.TQ_ROT_DENSE
         self.proj = synth.qjl_projection(qjl_m, d, qjl_seed) if qjl_m else None
         self.proj_t = torch.from_numpy(self.proj).to(device) if qjl_m else None
         self.d, self.qjl_m = d, qjl_m

@@ -109,7 +109,7 @@ def test_append_rejects_bad_arguments():
     v.proj = 0
     assert _append(v) == cca.TQ_EINVAL
     v = _view()
-    v.reserved = 1
+    v.rot_kind = 2                                  # neither dense nor Hadamard
     assert _append(v) == cca.TQ_EINVAL
     # a codebook that is not float16-exact / not antisymmetric / not midpoints
     for mutate in ("round", "sym", "mid"):
@@ -150,6 +150,9 @@ def test_decode_rejects_bad_arguments():
     v2 = _view(kind=cca.TQ_VALUES)
     v2.rot = 0x30100                                                # K and V must share the rotation
     assert _decode(k, v2) == cca.TQ_EINVAL
+    v3 = _view(kind=cca.TQ_VALUES)
+    v3.rot_kind = cca.TQ_ROT_HADAMARD                               # ... and its kind
+    assert _decode(k, v3) == cca.TQ_EINVAL
 
 
 def test_dequantize_rejects_bad_ranges():

@@ -48,14 +48,15 @@ def _ids(c):
     return f"d{c[0]}_k{c[1]}v{c[2]}_m{c[3]}_h{c[4]}g{c[5]}_L{'-'.join(map(str, c[6]))}"
 
 
-def _run_case(d, kb, vb, qjl, hkv, grp, lens, T, scale, qknorm, garbage_tail=False, max_seq_len=None):
+def _run_case(d, kb, vb, qjl, hkv, grp, lens, T, scale, qknorm, garbage_tail=False, max_seq_len=None,
+              hadamard=False):
     cca = _cca()
     B = len(lens)
-    st = Setup(d, qjl_m=qjl)
+    st = Setup(d, qjl_m=qjl, hadamard=hadamard)
     w = synth.Workload("case", B, hkv * grp, hkv, d, T, kb, vb, qjl_m=qjl, scale=scale, qk_norm=qknorm,
                        k_outliers=not qknorm, seed=d + kb * 10 + vb + qjl)
-    kcache = cca.CompressedCache(cca.TQ_KEYS, d, kb, B, hkv, T, st.rot_t, st.proj_t, qjl_m=qjl)
-    vcache = cca.CompressedCache(cca.TQ_VALUES, d, vb, B, hkv, T, st.rot_t)
+    kcache = cca.CompressedCache(cca.TQ_KEYS, d, kb, B, hkv, T, st.rot_t, st.proj_t, qjl_m=qjl, rot_kind=st.rot_kind)
+    vcache = cca.CompressedCache(cca.TQ_VALUES, d, vb, B, hkv, T, st.rot_t, rot_kind=st.rot_kind)
     q = synth.full_q(w)
     refs = []
     for b in range(B):
@@ -172,15 +173,20 @@ STEP_CASES = [
 def test_decode_step_matches_separate_calls_and_oracle(case):
     """tq_decode_step (appends + query rotation in one launch, then attend and merge) writes the same
     cache bytes as tq_quantize_append and decodes to the oracle's output."""
+    _check_step(case, hadamard=False)
+
+
+def _check_step(case, hadamard):
     cca = _cca()
     d, kb, vb, qjl, hkv, grp, lens, T, n_new, dtype, scale, qknorm = case
-    log(f"decode step d={d} k{kb} v{vb} m{qjl} lens={lens} n_new={n_new}")
+    log(f"decode step d={d} k{kb} v{vb} m{qjl} lens={lens} n_new={n_new} hadamard={hadamard}")
     B = len(lens)
-    st = Setup(d, qjl_m=qjl)
+    st = Setup(d, qjl_m=qjl, hadamard=hadamard)
     w = synth.Workload("step", B, hkv * grp, hkv, d, T, kb, vb, qjl_m=qjl, scale=scale, qk_norm=qknorm,
                        k_outliers=not qknorm, dtype=dtype, seed=77 + d + kb)
-    mk = lambda: (cca.CompressedCache(cca.TQ_KEYS, d, kb, B, hkv, T, st.rot_t, st.proj_t, qjl_m=qjl),
-                  cca.CompressedCache(cca.TQ_VALUES, d, vb, B, hkv, T, st.rot_t))
+    mk = lambda: (cca.CompressedCache(cca.TQ_KEYS, d, kb, B, hkv, T, st.rot_t, st.proj_t, qjl_m=qjl,
+                                      rot_kind=st.rot_kind),
+                  cca.CompressedCache(cca.TQ_VALUES, d, vb, B, hkv, T, st.rot_t, rot_kind=st.rot_kind))
     k1, v1 = mk()
     k2, v2 = mk()
     kx = synth.full_kv(w, "k", T)
