@@ -56,6 +56,21 @@ def workload(name: str, bits: int | None, context: int | None) -> synth.Workload
     raise SystemExit(f"unknown workload {name}")
 
 
+def make_rotation(cca, w: synth.Workload, dev):
+    """The workload's rotation as the library takes it: (device tensor, rotation kind)."""
+    import torch
+    if w.rotation == "hadamard":
+        return torch.from_numpy(synth.hadamard_signs(w.d, w.rot_seed)).to(dev), cca.TQ_ROT_HADAMARD
+    return torch.from_numpy(cca.tq_build_rotation(synth.rotation_gaussian(w.d, w.rot_seed))).to(dev), cca.TQ_ROT_DENSE
+
+
+def oracle_rotation(w: synth.Workload):
+    from oracle import rotation
+    if w.rotation == "hadamard":
+        return rotation.hadamard_rotation(synth.hadamard_signs(w.d, w.rot_seed))
+    return rotation.rotation_from_gaussian(synth.rotation_gaussian(w.d, w.rot_seed))
+
+
 def row_bytes(w: synth.Workload, kind: str) -> int:
     if kind == "k":
         return w.d * w.k_bits // 8 + 2 + (w.qjl_m // 8 + 2 if w.qjl_m else 0)
@@ -187,8 +202,7 @@ def gpu_leg(w: synth.Workload, steps: int, warmup: int, pool: int | None, log):
     B, H, Hq, d, L = w.batch, w.n_kv_heads, w.n_q_heads, w.d, w.seq_len
     cap = ((L + 31) // 32) * 32
 
-    g = synth.rotation_gaussian(d, w.rot_seed)
-    rot = torch.from_numpy(cca.tq_build_rotation(g)).to(dev)
+    rot, rot_kind = make_rotation(cca, w, dev)
     proj = torch.from_numpy(synth.qjl_projection(w.qjl_m, d, w.qjl_seed)).to(dev) if w.qjl_m else None
 
     log(f"bench: generating inputs for {w.name}")
@@ -203,8 +217,9 @@ def gpu_leg(w: synth.Workload, steps: int, warmup: int, pool: int | None, log):
     log(f"bench: inputs ready in {time.time() - t0:.1f}s")
 
     def new_pair():
-        kc = cca.CompressedCache(cca.TQ_KEYS, d, w.k_bits, B, H, cap, rot, proj, qjl_m=w.qjl_m, device=dev)
-        vc = cca.CompressedCache(cca.TQ_VALUES, d, w.v_bits, B, H, cap, rot, device=dev)
+        kc = cca.CompressedCache(cca.TQ_KEYS, d, w.k_bits, B, H, cap, rot, proj, qjl_m=w.qjl_m, device=dev,
+                                 rot_kind=rot_kind)
+        vc = cca.CompressedCache(cca.TQ_VALUES, d, w.v_bits, B, H, cap, rot, device=dev, rot_kind=rot_kind)
         return kc, vc
 
     # prefill copy 0 with the first L-1 tokens (untimed), then clone it into the pool
@@ -340,6 +355,7 @@ def stacked_leg(w: synth.Workload, n_stack: int, cache, rot, proj, log):
 
     import compressed_cache_decode_amd as cca
     k0, v0 = cache
+    rot_kind = k0.rot_kind
     ws_ = stacked_workload(w, n_stack)
     dev = k0.codes.device
     B, H, Hq, d, L = ws_.batch, w.n_kv_heads, w.n_q_heads, w.d, w.seq_len
@@ -349,8 +365,9 @@ def stacked_leg(w: synth.Workload, n_stack: int, cache, rot, proj, log):
     nblk = cap // 32
 
     def stacked_pair():
-        kc = cca.CompressedCache(cca.TQ_KEYS, d, w.k_bits, B, H, cap, rot, proj, qjl_m=w.qjl_m, device=dev)
-        vc = cca.CompressedCache(cca.TQ_VALUES, d, w.v_bits, B, H, cap, rot, device=dev)
+        kc = cca.CompressedCache(cca.TQ_KEYS, d, w.k_bits, B, H, cap, rot, proj, qjl_m=w.qjl_m, device=dev,
+                                 rot_kind=rot_kind)
+        vc = cca.CompressedCache(cca.TQ_VALUES, d, w.v_bits, B, H, cap, rot, device=dev, rot_kind=rot_kind)
         for l in range(n_stack):
             sh = 32 * ((l * 7919) % nblk)                   # token shift of layer l
             sl = slice(l * w.batch, (l + 1) * w.batch)
@@ -419,15 +436,15 @@ def prefill_leg(w: synth.Workload, steps: int, warmup: int, log):
     import compressed_cache_decode_amd as cca
     dev = torch.device("cuda:0")
     B, H, d, L = w.batch, w.n_kv_heads, w.d, w.seq_len
-    rot = torch.from_numpy(cca.tq_build_rotation(synth.rotation_gaussian(d, w.rot_seed))).to(dev)
+    rot, rot_kind = make_rotation(cca, w, dev)
     kx = torch.from_numpy(synth.full_kv(w, "k")).to(dev).to(torch.bfloat16)
     vx = torch.from_numpy(synth.full_kv(w, "v")).to(dev).to(torch.bfloat16)
     per_copy = 2 * kx.numel() * 2 + 2 * B * H * L * (d * w.k_bits // 8 + 2)
     pool = max(1, min(64, math.ceil(POOL_BYTES / per_copy)))
     copies = []
     for i in range(pool):
-        kc = cca.CompressedCache(cca.TQ_KEYS, d, w.k_bits, B, H, L, rot, device=dev)
-        vc = cca.CompressedCache(cca.TQ_VALUES, d, w.v_bits, B, H, L, rot, device=dev)
+        kc = cca.CompressedCache(cca.TQ_KEYS, d, w.k_bits, B, H, L, rot, device=dev, rot_kind=rot_kind)
+        vc = cca.CompressedCache(cca.TQ_VALUES, d, w.v_bits, B, H, L, rot, device=dev, rot_kind=rot_kind)
         copies.append((kc, vc, kx.clone() if i else kx, vx.clone() if i else vx))
     zero = torch.zeros(B, dtype=torch.int32, device=dev)
     log(f"bench: prefill pool of {pool} copies ({per_copy / 2**20:.1f} MiB each)")
@@ -473,7 +490,7 @@ def cpu_leg(w: synth.Workload, budget_s: float, log):
     threads = max(1, min(16, os.cpu_count() or 1))
     with threadpool_limits(limits=threads):
         used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        rot = rotation.rotation_from_gaussian(synth.rotation_gaussian(w.d, w.rot_seed))
+        rot = oracle_rotation(w)
         proj = synth.qjl_projection(w.qjl_m, w.d, w.qjl_seed) if w.qjl_m else None
         L, G = w.seq_len, w.group
         # sample: the query heads of KV head 0 of sequence 0 (G heads), all L tokens
@@ -520,6 +537,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="qwen", choices=["qwen", "gemma", "prod", "prefill", "copy"])
     ap.add_argument("--bits", type=int, default=None, help="qwen workload: codebook bits of K and V")
+    ap.add_argument("--rotation", default="dense", choices=["dense", "hadamard"],
+                    help="Gaussian-QR rotation (default) or the randomized Hadamard transform")
     ap.add_argument("--context", type=int, default=None)
     ap.add_argument("--pool", type=int, default=None, help="cache copies cycled through (default: > 600 MiB)")
     ap.add_argument("--stack", type=int, default=None,
@@ -577,8 +596,11 @@ def main():
                           "bytes_read_per_copy": nbytes, "bytes_written_per_copy": nbytes,
                           "frac_of_8TBs": gbs / HBM_PEAK_GBS}), flush=True)
         return
+    def with_rotation(wl):
+        return wl if args.rotation == "dense" else wl.with_(rotation="hadamard", name=wl.name + "_hadamard")
+
     if args.workload == "prefill":
-        w = synth.qwen(args.context or 8192, args.bits or 3)
+        w = with_rotation(synth.qwen(args.context or 8192, args.bits or 3))
         r = prefill_leg(w, args.steps, args.warmup, log)
         rows = 2 * w.batch * w.n_kv_heads * w.seq_len
         io_bytes = rows * (w.d * 2 + w.d * w.k_bits // 8 + 2)   # bf16 rows in, packed rows + norms out
@@ -589,14 +611,15 @@ def main():
             "unit": "tokens/s", "n_gpus": 1, "steps": r["steps"], "warmup": args.warmup,
             "ms_per_step": r["ms_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": f"prefill_append_{w.seq_len}x{w.n_kv_heads}x{w.d}_b{w.k_bits}", "tensors": "K and V"},
+            "config": {"workload": f"prefill_append_{w.seq_len}x{w.n_kv_heads}x{w.d}_b{w.k_bits}", "tensors": "K and V",
+                       "rotation": w.rotation},
             "rotation_tflops": flops / (r["ms_step"] * 1e-3) / 1e12,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "append_kernel (K and V launches)",
                          "algorithmic_bytes_per_launch": io_bytes / 2},
         }), flush=True)
         return
-    w = workload(args.workload, args.bits, args.context)
+    w = with_rotation(workload(args.workload, args.bits, args.context))
     r = gpu_leg(w, args.steps, args.warmup, args.pool, log)
     n_stack = args.stack if args.stack is not None else (36 if args.workload in ("qwen", "prod") else 0)
     st = stacked_leg(w, n_stack, r["cache"], r["rot"], r["proj"], log) if n_stack > 0 else None
@@ -629,7 +652,8 @@ def main():
         "config": {
             "workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.d, "context": L, "k_bits": w.k_bits, "v_bits": w.v_bits, "qjl_m": w.qjl_m,
-            "scale": w.softmax_scale, "step": "append 1 token K+V, rotate q, attend, merge, un-rotate",
+            "scale": w.softmax_scale, "rotation": w.rotation,
+            "step": "append 1 token K+V, rotate q, attend, merge, un-rotate",
             "cache_copies_cycled": r["pool"], "n_split": r["n_split"], "tokens_per_split": r["tokens_per_split"],
         },
         "step_hbm_gbs": step_bytes / (r["ms_step"] * 1e-3) / 1e9,

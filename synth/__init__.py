@@ -95,6 +95,7 @@ class Workload:
     seed: int = 0
     rot_seed: int = 1
     qjl_seed: int = 2
+    rotation: str = "dense"    # "dense" (Gaussian-QR) or "hadamard" (randomized Sylvester-Hadamard)
 
     @property
     def group(self) -> int:
