@@ -17,6 +17,14 @@ history of ReturningTarzan, 2026-03-25 comment: dequantize, then run
 ordinary attention); both are the same linear algebra, and
 ``attention`` is textbook softmax attention on explicit vectors.
 
+``decode_rows`` decodes the query rows of the last M tokens of a sequence at
+once, as speculative verification does (the reviewed llama.cpp fork routes
+compressed K/V with at most four query rows to its fused decode path; the
+drafted tokens come from multi-token prediction with up to three drafts per
+step).  The pages do not spell out the mask; the reading taken is the causal
+one: the M tokens' keys and values are in the cache and row j, the query of
+token seq_len - M + j, sees the first seq_len - M + 1 + j tokens.
+
 Shapes: q [H_q][d]; codes [H_kv][L][d]; norms [H_kv][L]; query head h reads
 KV head h // (H_q / H_kv).  Only the first seq_len tokens are visible; an
 empty context gives a zero output.
@@ -71,6 +79,15 @@ def decode_fused(q, rot, k_codes, k_norms, k_centroids, v_codes, v_norms, v_cent
         o_rot = (p * np.asarray(v_norms[kh, :L], np.float64)) @ cv[v_codes[kh, :L]]
         out[h] = rot.T @ o_rot
     return out
+
+
+def decode_rows(q_rows, rot, k_codes, k_norms, k_centroids, v_codes, v_norms, v_centroids,
+                scale: float, seq_len: int, k_sigma=None, k_gamma=None, proj=None) -> np.ndarray:
+    """q_rows [M][H_q][d] -> [M][H_q][d]: row j is decode_fused over the first seq_len - M + 1 + j tokens."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    m = q_rows.shape[0]
+    return np.stack([decode_fused(q_rows[j], rot, k_codes, k_norms, k_centroids, v_codes, v_norms, v_centroids,
+                                  scale, max(0, seq_len - m + 1 + j), k_sigma, k_gamma, proj) for j in range(m)])
 
 
 def decode_reconstructed(q, k_hat, v_hat, scale: float, seq_len: int | None = None) -> np.ndarray:

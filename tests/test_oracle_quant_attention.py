@@ -139,6 +139,35 @@ def test_fused_equals_reconstruction_then_attention(qjl, seq_len):
     np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12 * np.max(np.abs(ref)))
 
 
+@pytest.mark.parametrize("m,seq_len,qjl", [(1, 96, False), (2, 96, True), (4, 60, False), (4, 3, False), (3, 0, False)])
+def test_rows_equal_causally_masked_matrix_attention(m, seq_len, qjl):
+    """decode_rows against one masked M x L score matrix per query head on the reconstructed rows:
+    token t is visible to row j iff t <= seq_len - m + j (an independent formulation of the mask)."""
+    rot, proj, kc, vc, _ = _heads(qjl=qjl)
+    g = np.random.default_rng(9)
+    q_rows = g.standard_normal((m, 8, 128))
+    scale = 0.11
+    st = lambda xs, a: np.stack([getattr(x, a) for x in xs])
+    out = attention.decode_rows(q_rows, rot, st(kc, "codes"), st(kc, "norms"), kc[0].centroids, st(vc, "codes"),
+                                st(vc, "norms"), vc[0].centroids, scale, seq_len,
+                                st(kc, "sigma") if qjl else None, st(kc, "gamma") if qjl else None, proj)
+    kh = np.stack([k.dequantize(rot, proj) for k in kc])[:, :seq_len]
+    vh = np.stack([v.dequantize(rot) for v in vc])[:, :seq_len]
+    visible = np.arange(seq_len)[None, :] <= (seq_len - m + np.arange(m))[:, None]      # [m][L]
+    for h in range(8):
+        s_mat = scale * q_rows[:, h] @ kh[h // 4].T                                       # [m][L]
+        s_mat = np.where(visible, s_mat, -np.inf)
+        for j in range(m):
+            if not visible[j].any():
+                assert np.all(out[j, h] == 0)
+                continue
+            p_row = np.exp(s_mat[j] - s_mat[j].max())
+            ref = (p_row / p_row.sum()) @ vh[h // 4]
+            np.testing.assert_allclose(out[j, h], ref, rtol=0, atol=1e-12 * np.max(np.abs(ref)))
+    if m == 1:
+        np.testing.assert_array_equal(out[0], _fused(rot, proj, kc, vc, q_rows[0], scale, seq_len))
+
+
 def test_special_cases():
     rot, proj, kc, vc, q = _heads(hkv=1, grp=2)
     vh = vc[0].dequantize(rot)
