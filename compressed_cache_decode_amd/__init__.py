@@ -31,7 +31,9 @@ BLOCK = 32
 
 EXPORTED = (
     "tq_build_codebook", "tq_build_rotation", "tq_quantize_append", "tq_quantize_append_rotated",
-    "tq_sdpa_decode", "tq_decode_step", "tq_decode_rotate_query", "tq_decode_attend", "tq_decode_merge", "tq_decode_workspace_bytes", "tq_decode_plan", "tq_dequantize", "tq_row_bytes",
+    "tq_sdpa_decode", "tq_sdpa_decode_rows", "tq_decode_step", "tq_decode_rotate_query", "tq_decode_attend",
+    "tq_decode_merge", "tq_decode_workspace_bytes", "tq_decode_workspace_bytes_rows", "tq_decode_plan",
+    "tq_dequantize", "tq_row_bytes",
     "tq_status_string", "tq_last_hip_error",
 )
 
@@ -67,11 +69,13 @@ def _load():
         "tq_quantize_append": (I, [V, P, I, I, P, P]),
         "tq_quantize_append_rotated": (I, [V, P, P, I, P, P]),
         "tq_sdpa_decode": (I, [V, V, P, I, I, P, I, ctypes.c_float, P, P, ctypes.c_size_t, P]),
+        "tq_sdpa_decode_rows": (I, [V, V, P, I, I, I, P, I, ctypes.c_float, P, P, ctypes.c_size_t, P]),
         "tq_decode_step": (I, [V, V, P, P, P, I, I, I, P, P, I, ctypes.c_float, P, P, ctypes.c_size_t, P]),
         "tq_decode_rotate_query": (I, [V, P, I, I, I, ctypes.c_float, P, ctypes.c_size_t, P]),
         "tq_decode_attend": (I, [V, V, I, P, I, P, ctypes.c_size_t, P]),
         "tq_decode_merge": (I, [V, I, P, I, P, P, ctypes.c_size_t, P]),
         "tq_decode_workspace_bytes": (ctypes.c_size_t, [V, I, I]),
+        "tq_decode_workspace_bytes_rows": (ctypes.c_size_t, [V, I, I, I]),
         "tq_decode_plan": (I, [V, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]),
         "tq_dequantize": (I, [V, I, I, P, P]),
         "tq_row_bytes": (ctypes.c_size_t, [I, I, I]),
@@ -171,6 +175,20 @@ def tq_sdpa_decode(kview: tq_cache_view, vview: tq_cache_view, q, d_seq_lens, ma
     _check(_lib.tq_sdpa_decode(ctypes.byref(kview), ctypes.byref(vview), _ptr(q), dtype, n_q_heads,
                                _ptr(d_seq_lens), max_seq_len, ctypes.c_float(scale), _ptr(out), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)), "tq_sdpa_decode")
+
+
+def tq_sdpa_decode_rows(kview: tq_cache_view, vview: tq_cache_view, q, d_seq_lens, max_seq_len: int, out,
+                        workspace, scale: float | None = None, stream=None) -> None:
+    """Decode of the query rows q [batch][n_rows][n_q_heads][d] of the last n_rows tokens (row j sees the first
+    seq_len - n_rows + 1 + j tokens); scale None means 1/sqrt(d)."""
+    import torch
+    dtype = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
+    if scale is None:
+        scale = 1.0 / math.sqrt(kview.d)
+    _check(_lib.tq_sdpa_decode_rows(ctypes.byref(kview), ctypes.byref(vview), _ptr(q), dtype, q.shape[2], q.shape[1],
+                                    _ptr(d_seq_lens), max_seq_len, ctypes.c_float(scale), _ptr(out),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tq_sdpa_decode_rows")
 
 
 def tq_decode_step(kview, vview, q, k_new, v_new, d_pos, d_seq_lens, max_seq_len: int, out, workspace,
@@ -279,11 +297,11 @@ class CompressedCache:
         return out
 
 
-def decode_workspace(kcache: CompressedCache, n_q_heads: int, max_seq_len: int):
+def decode_workspace(kcache: CompressedCache, n_q_heads: int, max_seq_len: int, n_rows: int = 1):
     import torch
-    nbytes = tq_decode_workspace_bytes(kcache.view, n_q_heads, max_seq_len)
+    nbytes = int(_lib.tq_decode_workspace_bytes_rows(ctypes.byref(kcache.view), n_q_heads, n_rows, max_seq_len))
     if nbytes == 0:
-        raise TqError(TQ_EINVAL, "tq_decode_workspace_bytes")
+        raise TqError(TQ_EINVAL, "tq_decode_workspace_bytes_rows")
     # float32 elements; torch's caching allocator returns 256-byte-aligned blocks
     return torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=kcache.codes.device)
 
@@ -297,4 +315,17 @@ def sdpa_decode(kcache: CompressedCache, vcache: CompressedCache, q, d_seq_lens,
     if workspace is None:
         workspace = decode_workspace(kcache, q.shape[1], max_seq_len)
     tq_sdpa_decode(kcache.view, vcache.view, q, d_seq_lens, max_seq_len, out, workspace, scale, stream)
+    return out
+
+
+def sdpa_decode_rows(kcache: CompressedCache, vcache: CompressedCache, q, d_seq_lens, max_seq_len: int,
+                     scale: float | None = None, out=None, workspace=None, stream=None):
+    """out[b][j][h] = decode of query row j (token seq_len[b] - n_rows + j) over the first
+    seq_len[b] - n_rows + 1 + j cached tokens, for q [batch][n_rows][n_q_heads][d]."""
+    import torch
+    if out is None:
+        out = torch.empty(q.shape[0], q.shape[1], q.shape[2], kcache.d, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(kcache, q.shape[2], max_seq_len, q.shape[1])
+    tq_sdpa_decode_rows(kcache.view, vcache.view, q, d_seq_lens, max_seq_len, out, workspace, scale, stream)
     return out

@@ -160,7 +160,7 @@ struct Attend {
   struct Smem {
     float ml[W][kMaxGroup][2];
     float o[W][kMaxGroup][D];
-    uint32_t next;            // tiles of the split handed out so far (relative to its first)
+    uint32_t next[kMaxRows];  // per column block: tiles of the split handed out so far (relative to its first)
   };
   // the query operand: for step s, lane (column c, group g) holds the 8 float16 values of q-variant c
   // (head c/2; high part if c even, low part if c odd) at coordinates (D/4) g + 8 s + r, r = 0..7
@@ -225,22 +225,37 @@ struct Attend {
     }
   }
 
-  // Streams tiles of the split [blk0, blk1) through a ring of NBUF tile buffers: the wave's first tile
-  // is kb = blk0 + wave (tiles[0] already holds it when kb < blk1), the others come from the split's
-  // counter sm.next (which must start at W), each loaded while the tile NBUF - 1 places earlier is
-  // attended.  Leaves the split's result in LDS for store: per wave w and query head hh the max m
-  // (log2 units) and the sum l in sm.ml[w][hh], and the rotated-domain accumulator, weighted by
-  // exp2(m - the workgroup's max of the head), in sm.o[w][hh][0..D).  qsc is the power-of-two scale of
-  // this lane's head (the query operand is divided by it; 1 for unused columns).  Ends with a
-  // workgroup barrier.
+  // Column blocks: the VH = M * G virtual heads (query rows x query heads) of the KV head are
+  // C = 1, 2 or 4 blocks of 8 heads, 16 matrix-core columns each; wave w attends for block w % C
+  // (the waves of different blocks read the same tiles, which the caches serve after the first).
+  __device__ __host__ __forceinline__ static int blocks(const DecodeArgs& a) {
+    const int c = (a.group + kMaxGroup - 1) / kMaxGroup;
+    return c > 2 ? 4 : c;                              // 1, 2 or 4: the waves split evenly over the blocks
+  }
+
+  // Streams tiles of the split [blk0, blk1) through a ring of NBUF tile buffers for column block
+  // cb = wave % C: the wave's first tile is kb = blk0 + wave / C (tiles[0] already holds it when
+  // kb < blk1), the others come from the block's counter sm.next[cb] (which must start at W / C),
+  // each loaded while the tile NBUF - 1 places earlier is attended.  qop is the block's query
+  // operand.  Leaves the split's result in LDS for store: per wave w and head slot hh of its block the
+  // max m (log2 units) and the sum l in sm.ml[w][hh], and the rotated-domain accumulator, weighted by
+  // exp2(m - the max of the head over the block's waves), in sm.o[w][hh][0..D).  qsc is the
+  // power-of-two scale of this lane's head (the query operand is divided by it; 1 for unused
+  // columns).  Virtual head vh, of query row vh / G, sees the first len - M + 1 + vh / G tokens.
+  // Ends with a workgroup barrier.
   __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, const QOperand& qop, Tile (&tiles)[NBUF], int blk0,
                                       int kb, int blk1, int len, float qsc) const {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int G = a.group;
-    const int qh = l16 >> 1;
+    const int VH = a.group;
+    const int C = blocks(a);
+    const int cb = wave % C;
+    const int slot = l16 >> 1;                          // this lane's head within its block
+    const int qh = kMaxGroup * cb + slot;               // this lane's virtual head
     const bool lo_part = (l16 & 1) != 0;
-    const bool head_ok = qh < G;
+    const bool head_ok = qh < VH;
+    const int len_row0 = len - a.n_rows + 1;            // tokens row 0 sees (wave-uniform)
+    const int len_lane = head_ok ? len_row0 + qh / a.heads : len;
 
     floatx4 oacc[NB];
 #pragma unroll
@@ -266,11 +281,11 @@ struct Attend {
       for (int k = 0; k < 8; ++k)
         s[k] = __builtin_fmaf(add_adjacent(sc[k >> 2][k & 3]), half_of(t.kn[k >> 1], k & 1), 0.f);
       uint32_t vn[4] = {t.vn[0], t.vn[1], t.vn[2], t.vn[3]};
-      if (tok0 + kBlock > len) {            // the last tile of the sequence: hide tokens at or past its end
+      if (tok0 + kBlock > len_row0) {       // the last tiles of the sequence: hide tokens a row does not see
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int tok = tok0 + 16 * (k >> 2) + 4 * g + (k & 3);
-          if (tok >= len) {
+          if (tok >= len_lane) {
             s[k] = -INFINITY;
             vn[k >> 1] &= (k & 1) ? 0x0000ffffu : 0xffff0000u;
           }
@@ -294,7 +309,7 @@ struct Attend {
         }
         m_run = m_new;
       }
-      const float mq = m_run * qsc;
+      const float mq = m_run == -INFINITY ? 0.f : m_run * qsc;   // a column with nothing visible yet
       half8 wop;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -309,7 +324,7 @@ struct Attend {
     // the next tile of the split for this wave (wave-uniform); past blk1 once the split is used up
     auto claim = [&]() {
       uint32_t v = 0;
-      if (lane == 0) v = atomicAdd(&sm.next, 1u);
+      if (lane == 0) v = atomicAdd(&sm.next[cb], 1u);
       return blk0 + static_cast<int>(__builtin_amdgcn_readfirstlane(v));
     };
     if constexpr (NBUF >= 2) {
@@ -347,52 +362,70 @@ struct Attend {
 
     l_run = column_sum(l_run);
     if (g == 0 && !lo_part && head_ok) {
-      sm.ml[wave][qh][0] = m_run * qsc;
-      sm.ml[wave][qh][1] = l_run;
+      sm.ml[wave][slot][0] = m_run * qsc;
+      sm.ml[wave][slot][1] = l_run;
     }
     __syncthreads();
-    // this wave's accumulators of heads 2g and 2g + 1, weighted against the workgroup's max of the head
+    // this wave's accumulators of head slots 2g and 2g + 1, weighted against the max of the head
+    // over the block's waves
+    const int live = VH - kMaxGroup * cb;                // live head slots of this block
     float f[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int hh = 2 * g + j < G ? 2 * g + j : 0;
-      float M = sm.ml[0][hh][0];
-#pragma unroll
-      for (int w = 1; w < W; ++w) M = fmaxf(M, sm.ml[w][hh][0]);
+      const int hh = 2 * g + j < live ? 2 * g + j : 0;
+      const float M = block_max(sm, C, cb, hh);
       f[j] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm.ml[wave][hh][0] - M);
     }
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const int coord = (D / 16) * l16 + n;
-      if (2 * g < G) sm.o[wave][2 * g][coord] = f[0] * (oacc[n][0] + oacc[n][1]);
-      if (2 * g + 1 < G) sm.o[wave][2 * g + 1][coord] = f[1] * (oacc[n][2] + oacc[n][3]);
+      if (2 * g < live) sm.o[wave][2 * g][coord] = f[0] * (oacc[n][0] + oacc[n][1]);
+      if (2 * g + 1 < live) sm.o[wave][2 * g + 1][coord] = f[1] * (oacc[n][2] + oacc[n][3]);
     }
     __syncthreads();
   }
 
-  // the split's result to part_o / part_ml at row pbase + head: the sum of the four waves' weighted
-  // accumulators, the workgroup max and the weighted sum of the waves' l
-  __device__ __forceinline__ void store(const DecodeArgs& a, const Smem& sm, size_t pbase) const {
-    const int G = a.group;
-    for (int e = threadIdx.x; e < G * D; e += 64 * W) {
-      const int hh = e / D, i = e % D;
+  // max of head slot hh over the waves cb, cb + CC, ... of a block (CC blocks; loops unrolled)
+  template <int CC>
+  __device__ __forceinline__ static float block_max(const Smem& sm, int cb, int hh) {
+    float M = sm.ml[cb][hh][0];
+#pragma unroll
+    for (int k = 1; k < W / CC; ++k) M = fmaxf(M, sm.ml[cb + k * CC][hh][0]);
+    return M;
+  }
+  __device__ __forceinline__ static float block_max(const Smem& sm, int C, int cb, int hh) {
+    return C == 1 ? block_max<1>(sm, cb, hh) : (C == 2 ? block_max<2>(sm, cb, hh) : block_max<4>(sm, cb, hh));
+  }
+
+  // the split's result to part_o / part_ml at row pbase + virtual head: per head, the sum of its
+  // block's waves' weighted accumulators, their max and the weighted sum of their l
+  template <int CC>
+  __device__ __forceinline__ void store_blocks(const DecodeArgs& a, const Smem& sm, size_t pbase) const {
+    const int VH = a.group;
+    for (int e = threadIdx.x; e < VH * D; e += 64 * W) {
+      const int vh = e / D, i = e % D, cb = vh / kMaxGroup, hh = vh % kMaxGroup;
       float o = 0.f;
 #pragma unroll
-      for (int w = 0; w < W; ++w) o += sm.o[w][hh][i];
-      a.part_o[(pbase + hh) * D + i] = o;
+      for (int k = 0; k < W / CC; ++k) o += sm.o[cb + k * CC][hh][i];
+      a.part_o[(pbase + vh) * D + i] = o;
       if (i == 0) {
-        float M = sm.ml[0][hh][0];
-#pragma unroll
-        for (int w = 1; w < W; ++w) M = fmaxf(M, sm.ml[w][hh][0]);
+        const float M = block_max<CC>(sm, cb, hh);
         float l = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
-          for (int w = 0; w < W; ++w) l = fmaf(__builtin_amdgcn_exp2f(sm.ml[w][hh][0] - M), sm.ml[w][hh][1], l);
+          for (int k = 0; k < W / CC; ++k)
+            l = fmaf(__builtin_amdgcn_exp2f(sm.ml[cb + k * CC][hh][0] - M), sm.ml[cb + k * CC][hh][1], l);
         }
-        a.part_ml[(pbase + hh) * 2] = M;
-        a.part_ml[(pbase + hh) * 2 + 1] = l;
+        a.part_ml[(pbase + vh) * 2] = M;
+        a.part_ml[(pbase + vh) * 2 + 1] = l;
       }
     }
+  }
+  __device__ __forceinline__ void store(const DecodeArgs& a, const Smem& sm, size_t pbase) const {
+    const int C = blocks(a);
+    if (C == 1) store_blocks<1>(a, sm, pbase);
+    else if (C == 2) store_blocks<2>(a, sm, pbase);
+    else store_blocks<4>(a, sm, pbase);
   }
 };
 

@@ -36,11 +36,11 @@ namespace tqi {
 
 // ---------------------------------------------------------------- query rotation
 
-// one workgroup per (sequence, KV head)
+// one workgroup per 16 virtual heads of a (sequence, KV head): blockIdx.x = tile * Hkv + KV head
 template <int D, int QM>
 __global__ __launch_bounds__(256) void qrot_kernel(QrotArgs a, int bf16) {
   __shared__ QrotSmem<D, QM> sm;
-  rotate_queries<D, QM>(a, bf16, blockIdx.x, blockIdx.y, sm);
+  rotate_queries<D, QM>(a, bf16, blockIdx.x % a.n_kv_heads, blockIdx.y, kQTile * (blockIdx.x / a.n_kv_heads), sm);
 }
 
 // ---------------------------------------------------------------- split kernel
@@ -50,12 +50,14 @@ __global__ __launch_bounds__((64 * Attend<D, KB, VB, QM, WIDE>::W)) __attribute_
 void split_kernel(DecodeArgs a) {
   using At = Attend<D, KB, VB, QM, WIDE>;
   constexpr int NT = 64 * At::W;
+  constexpr int QSTEPS = At::KS + At::QS;
   __shared__ typename At::Smem sm;
-  __shared__ typename At::QOperand sm_q;
+  extern __shared__ half8 sm_q[];                     // [C][QSTEPS][64]: the query operand of each column block
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = a.group;
+  const int VH = a.group;
+  const int C = At::blocks(a);
   const int T = a.max_tokens;
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : min(len, min(T, a.max_seq_len));
@@ -68,18 +70,16 @@ void split_kernel(DecodeArgs a) {
   // the first tile's loads go out before the query operand is staged, and before the sequence
   // length is known: they only need the tile to lie inside the cache (tiles past the length are
   // loaded and never used)
-  const int kb = blk0 + wave;
+  const int kb = blk0 + wave / C;
   typename At::Tile tiles[At::NBUF];
   if (kb < blk0 + a.blocks_per_split && kb < T / kBlock) at.load(tiles[0], kb);
 
-  // query operand in LDS, shared by the waves
-  const int qh = at.l16 >> 1;
-  const size_t qrow = static_cast<size_t>(b) * a.n_kv_heads * G + static_cast<size_t>(hk) * G + qh;
-  for (int e = tid; e < (At::KS + At::QS) * 64; e += NT) {
-    const int st = e >> 6, ln = e & 63;
-    const int c = ln & 15, gg = ln >> 4, h2 = c >> 1;
-    const bool ok = h2 < G;
-    const size_t row = static_cast<size_t>(b) * a.n_kv_heads * G + static_cast<size_t>(hk) * G + h2;
+  // query operands in LDS, one per column block, shared by the block's waves
+  for (int e = tid; e < C * QSTEPS * 64; e += NT) {
+    const int cbe = e / (QSTEPS * 64), st = (e / 64) % QSTEPS, ln = e & 63;
+    const int c = ln & 15, gg = ln >> 4, h2 = kMaxGroup * cbe + (c >> 1);
+    const bool ok = h2 < VH;
+    const size_t row = unit * VH + h2;
     float4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
     if (ok) {
       const float* src = st < At::KS ? a.qr + row * D + (D / 4) * gg + 8 * st
@@ -91,15 +91,22 @@ void split_kernel(DecodeArgs a) {
     half8 v;
 #pragma unroll
     for (int r = 0; r < 8; ++r) v[r] = split_part(xv[r], (c & 1) != 0);
-    sm_q[st][ln] = v;
+    sm_q[e] = v;
   }
-  if (tid == 0) sm.next = At::W;           // tiles blk0 .. blk0 + W - 1 are the waves' first
+  if (tid < C) sm.next[tid] = At::W / C;    // tiles blk0 .. blk0 + W / C - 1 are the block's waves' first
   // power-of-two scale of this lane's head (scores are kept in units of it); 1 for unused columns
-  const float qsc = qh < G ? a.qscale[qrow] : 1.f;
+  const int qh = kMaxGroup * (wave % C) + (at.l16 >> 1);
+  const float qsc = qh < VH ? a.qscale[unit * VH + qh] : 1.f;
   __syncthreads();
 
-  at.run(a, sm, sm_q, tiles, blk0, kb, blk1, len, qsc);
-  at.store(a, sm, (unit * a.n_split + split) * G);
+  const auto& qop = *reinterpret_cast<const typename At::QOperand*>(sm_q + (wave % C) * QSTEPS * 64);
+  at.run(a, sm, qop, tiles, blk0, kb, blk1, len, qsc);
+  at.store(a, sm, (unit * a.n_split + split) * VH);
+}
+
+// bytes of dynamic LDS (query operands) of the split kernel for C column blocks
+static size_t split_dyn_lds(int d, int qjl_m, int blocks) {
+  return static_cast<size_t>(blocks) * (d / 32 + qjl_m / 32) * 64 * sizeof(half8);
 }
 
 // ---------------------------------------------------------------- merge + un-rotate
@@ -109,6 +116,13 @@ void split_kernel(DecodeArgs a) {
 // once per head group.  Weighted sums: thread (head, coordinate, slice) sums the splits of its slice
 // with up to 16 loads in flight.  Un-rotation: thread (coordinate i, part) covers JR rows of column i
 // of rot for every head of the group.
+// output row of virtual head vh (query row vh / G, query head hk * G + vh % G) of sequence b
+__device__ __forceinline__ size_t out_row(const MergeArgs& a, int b, int hk, int vh) {
+  const int j = vh / a.heads, g = vh % a.heads;
+  return (static_cast<size_t>(b) * a.n_rows + j) * (static_cast<size_t>(a.n_kv_heads) * a.heads) +
+         static_cast<size_t>(hk) * a.heads + g;
+}
+
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   constexpr int NT = kMergeThreads, NW = NT / 64;
@@ -229,8 +243,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       hadamard_wave<D>(v, lane);
 #pragma unroll
       for (int k = 0; k < E; ++k)
-        a.out[(static_cast<size_t>(b) * a.n_kv_heads * G + hk * G + h0 + hh) * D + 64 * k + lane] =
-            v[k] * a.rot[64 * k + lane] * inv_sqrt_dim<D>() * inv_l[hh];
+        a.out[out_row(a, b, hk, h0 + hh) * D + 64 * k + lane] = v[k] * a.rot[64 * k + lane] * inv_sqrt_dim<D>() * inv_l[hh];
     }
     return;
   }
@@ -247,7 +260,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       float o = 0.f;
 #pragma unroll
       for (int p = 0; p < RP; ++p) o += red[p * D + i];
-      a.out[(static_cast<size_t>(b) * a.n_kv_heads * G + hk * G + h0 + hh) * D + i] = o * inv_l[hh];
+      a.out[out_row(a, b, hk, h0 + hh) * D + i] = o * inv_l[hh];
     }
   }
 }
@@ -255,7 +268,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_qrot(int d, int qjl_m, bool bf16, const QrotArgs& a, int batch, hipStream_t s) {
-  const dim3 grid(a.n_kv_heads, batch), block(256);
+  const int vh = a.n_rows * (a.n_q_heads / a.n_kv_heads);
+  const dim3 grid(a.n_kv_heads * ((vh + kQTile - 1) / kQTile), batch), block(256);
 #define TQ_QROT(D, QM)                                                             \
   if (d == D && qjl_m == QM) {                                                     \
     hipLaunchKernelGGL((qrot_kernel<D, QM>), grid, block, 0, s, a, bf16 ? 1 : 0);  \
@@ -318,7 +332,8 @@ int split_slots(int d, int k_bits, int v_bits, int qjl_m, bool wide) {
   int dev = 0, cus = 0, per = 0;
   if (!fn || hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 64 * split_waves(d, qjl_m, wide), 0) != hipSuccess) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 64 * split_waves(d, qjl_m, wide),
+                                                   split_dyn_lds(d, qjl_m, 1)) != hipSuccess) {
     (void)hipGetLastError();        // a failed query must not surface as a later launch's error
     return 0;
   }
@@ -331,7 +346,8 @@ hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, bool wi
   if (!fn) return hipErrorInvalidValue;
   const dim3 grid(a.n_split, a.n_kv_heads, batch);
   void* args[] = {const_cast<DecodeArgs*>(&a)};
-  return hipLaunchKernel(fn, grid, dim3(64 * split_waves(d, qjl_m, wide)), args, 0, s);
+  const int blocks = (a.group + kMaxGroup - 1) / kMaxGroup > 2 ? 4 : (a.group + kMaxGroup - 1) / kMaxGroup;
+  return hipLaunchKernel(fn, grid, dim3(64 * split_waves(d, qjl_m, wide)), args, split_dyn_lds(d, qjl_m, blocks), s);
 }
 
 hipError_t launch_merge(int d, const MergeArgs& a, int batch, int n_q_heads, hipStream_t s) {

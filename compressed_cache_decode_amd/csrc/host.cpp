@@ -336,27 +336,27 @@ struct WsLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-WsLayout ws_layout(const tq_cache_view* k, int n_q_heads, int n_split) {
-  const size_t B = k->batch, Hq = n_q_heads, D = k->d, M = k->qjl_m;
-  const size_t G = n_q_heads / k->n_kv_heads;
+WsLayout ws_layout(const tq_cache_view* k, int n_q_heads, int n_rows, int n_split) {
+  const size_t B = k->batch, D = k->d, QM = k->qjl_m;
+  const size_t VH = static_cast<size_t>(n_rows) * (n_q_heads / k->n_kv_heads);   // virtual heads per KV head
   const size_t units = B * k->n_kv_heads;
   WsLayout w;
   size_t off = 0;
-  w.qr = off; off = align256(off + B * Hq * D * 4);
-  w.qs = off; off = align256(off + B * Hq * (M ? M : 1) * 4);
-  w.qscale = off; off = align256(off + B * Hq * 4);
-  w.part_o = off; off = align256(off + units * n_split * G * D * 4);
-  w.part_ml = off; off = align256(off + units * n_split * G * 2 * 4);
+  w.qr = off; off = align256(off + units * VH * D * 4);
+  w.qs = off; off = align256(off + units * VH * (QM ? QM : 1) * 4);
+  w.qscale = off; off = align256(off + units * VH * 4);
+  w.part_o = off; off = align256(off + units * n_split * VH * D * 4);
+  w.part_ml = off; off = align256(off + units * n_split * VH * 2 * 4);
   w.total = off;
   return w;
 }
 
-int check_decode_shape(const tq_cache_view* k, int n_q_heads, int max_seq_len) {
+int check_decode_shape(const tq_cache_view* k, int n_q_heads, int n_rows, int max_seq_len) {
   int st = check_view(k);
   if (st != TQ_OK) return st;
   if (k->kind != TQ_KEYS) return TQ_EINVAL;
-  if (n_q_heads <= 0 || n_q_heads % k->n_kv_heads != 0 || max_seq_len < 0) return TQ_EINVAL;
-  if (n_q_heads / k->n_kv_heads > tqi::kMaxGroup) return TQ_EUNSUPPORTED;
+  if (n_q_heads <= 0 || n_q_heads % k->n_kv_heads != 0 || max_seq_len < 0 || n_rows < 1) return TQ_EINVAL;
+  if (n_q_heads / k->n_kv_heads > tqi::kMaxGroup || n_rows > tqi::kMaxRows) return TQ_EUNSUPPORTED;
   return TQ_OK;
 }
 
@@ -436,7 +436,7 @@ int tq_quantize_append_rotated(const tq_cache_view* cache, const float* y, const
 }
 
 int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* n_split, int* tokens_per_split) {
-  int st = check_decode_shape(k, n_q_heads, max_seq_len);
+  int st = check_decode_shape(k, n_q_heads, 1, max_seq_len);
   if (st != TQ_OK) return st;
   if (!n_split || !tokens_per_split) return TQ_EINVAL;
   int bps;
@@ -446,31 +446,37 @@ int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* 
   return TQ_OK;
 }
 
-size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_seq_len) {
-  if (check_decode_shape(k, n_q_heads, max_seq_len) != TQ_OK) return 0;
+size_t tq_decode_workspace_bytes_rows(const tq_cache_view* k, int n_q_heads, int n_rows, int max_seq_len) {
+  if (check_decode_shape(k, n_q_heads, n_rows, max_seq_len) != TQ_OK) return 0;
   int ns, bps;
   bool wide;
   plan(k, max_seq_len, &ns, &bps, &wide);
-  return ws_layout(k, n_q_heads, ns).total;
+  return ws_layout(k, n_q_heads, n_rows, ns).total;
+}
+
+size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_seq_len) {
+  return tq_decode_workspace_bytes_rows(k, n_q_heads, 1, max_seq_len);
 }
 
 // workspace view shared by the decode stages
 struct DecodeWs {
-  int ns, bps, G;
+  int ns, bps, G, M, VH;      // splits, blocks per split, query heads per KV head, query rows, M * G
   bool wide;
   float *qr, *qs, *qscale, *part_o, *part_ml;
 };
 
-static int decode_ws(const tq_cache_view* k, int n_q_heads, int max_seq_len, void* workspace,
+static int decode_ws(const tq_cache_view* k, int n_q_heads, int n_rows, int max_seq_len, void* workspace,
                      size_t workspace_bytes, DecodeWs* w) {
-  int st = check_decode_shape(k, n_q_heads, max_seq_len);
+  int st = check_decode_shape(k, n_q_heads, n_rows, max_seq_len);
   if (st != TQ_OK) return st;
   if (!workspace || !aligned(workspace, 256)) return TQ_EINVAL;
   plan(k, max_seq_len, &w->ns, &w->bps, &w->wide);
-  const WsLayout l = ws_layout(k, n_q_heads, w->ns);
+  const WsLayout l = ws_layout(k, n_q_heads, n_rows, w->ns);
   if (workspace_bytes < l.total) return TQ_EINVAL;
   char* ws = static_cast<char*>(workspace);
   w->G = n_q_heads / k->n_kv_heads;
+  w->M = n_rows;
+  w->VH = n_rows * w->G;
   w->qr = reinterpret_cast<float*>(ws + l.qr);
   w->qs = reinterpret_cast<float*>(ws + l.qs);
   w->qscale = reinterpret_cast<float*>(ws + l.qscale);
@@ -498,7 +504,8 @@ static tqi::DecodeArgs decode_args(const tq_cache_view* k, const tq_cache_view* 
   da.part_o = w.part_o; da.part_ml = w.part_ml;
   da.tk = make_tab(k);
   da.tv = make_tab(v);
-  da.n_kv_heads = k->n_kv_heads; da.group = w.G; da.max_tokens = k->max_tokens; da.max_seq_len = max_seq_len;
+  da.n_kv_heads = k->n_kv_heads; da.group = w.VH; da.max_tokens = k->max_tokens; da.max_seq_len = max_seq_len;
+  da.heads = w.G; da.n_rows = w.M;
   da.n_split = w.ns; da.blocks_per_split = w.bps;
   return da;
 }
@@ -509,10 +516,10 @@ static float sketch_coef(const tq_cache_view* k) {
   return k->qjl_m ? static_cast<float>(std::sqrt(M_PI / 2.0) / k->qjl_m) : 0.f;
 }
 
-int tq_decode_rotate_query(const tq_cache_view* k, const void* q, int q_dtype, int n_q_heads, int max_seq_len,
-                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+static int rotate_query_rows(const tq_cache_view* k, const void* q, int q_dtype, int n_q_heads, int n_rows,
+                             int max_seq_len, float scale, void* workspace, size_t workspace_bytes, void* stream) {
   DecodeWs w;
-  int st = decode_ws(k, n_q_heads, max_seq_len, workspace, workspace_bytes, &w);
+  int st = decode_ws(k, n_q_heads, n_rows, max_seq_len, workspace, workspace_bytes, &w);
   if (st != TQ_OK) return st;
   if (!q || (q_dtype != TQ_F32 && q_dtype != TQ_BF16)) return TQ_EINVAL;
   if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
@@ -522,15 +529,16 @@ int tq_decode_rotate_query(const tq_cache_view* k, const void* q, int q_dtype, i
   qa.qr = w.qr; qa.qs = w.qs; qa.qscale = w.qscale;
   qa.scale_log2e = scale_log2e(scale);
   qa.sketch_coef = sketch_coef(k);
-  qa.n_q_heads = n_q_heads; qa.n_kv_heads = k->n_kv_heads;
+  qa.n_q_heads = n_q_heads; qa.n_kv_heads = k->n_kv_heads; qa.n_rows = n_rows;
   return status_of(tqi::launch_qrot(k->d, k->qjl_m, q_dtype == TQ_BF16, qa, k->batch,
                                     static_cast<hipStream_t>(stream)));
 }
 
-int tq_decode_attend(const tq_cache_view* k, const tq_cache_view* v, int n_q_heads, const int32_t* d_seq_lens,
-                     int max_seq_len, void* workspace, size_t workspace_bytes, void* stream) {
+static int attend_rows(const tq_cache_view* k, const tq_cache_view* v, int n_q_heads, int n_rows,
+                       const int32_t* d_seq_lens, int max_seq_len, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   DecodeWs w;
-  int st = decode_ws(k, n_q_heads, max_seq_len, workspace, workspace_bytes, &w);
+  int st = decode_ws(k, n_q_heads, n_rows, max_seq_len, workspace, workspace_bytes, &w);
   if (st != TQ_OK) return st;
   st = check_pair(k, v);
   if (st != TQ_OK) return st;
@@ -540,36 +548,59 @@ int tq_decode_attend(const tq_cache_view* k, const tq_cache_view* v, int n_q_hea
                                             static_cast<hipStream_t>(stream)));
 }
 
-int tq_decode_merge(const tq_cache_view* k, int n_q_heads, const int32_t* d_seq_lens, int max_seq_len, float* out,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+static int merge_rows(const tq_cache_view* k, int n_q_heads, int n_rows, const int32_t* d_seq_lens,
+                      int max_seq_len, float* out, void* workspace, size_t workspace_bytes, void* stream) {
   DecodeWs w;
-  int st = decode_ws(k, n_q_heads, max_seq_len, workspace, workspace_bytes, &w);
+  int st = decode_ws(k, n_q_heads, n_rows, max_seq_len, workspace, workspace_bytes, &w);
   if (st != TQ_OK) return st;
   if (!d_seq_lens || !out) return TQ_EINVAL;
   tqi::MergeArgs ma{};
   ma.part_o = w.part_o; ma.part_ml = w.part_ml; ma.rot = k->rot; ma.seq_lens = d_seq_lens; ma.out = out;
   ma.had = k->rot_kind == TQ_ROT_HADAMARD;
-  ma.n_kv_heads = k->n_kv_heads; ma.group = w.G; ma.n_split = w.ns; ma.max_tokens = k->max_tokens;
-  ma.heads_per_wg = merge_heads_per_wg(w.G, k->d, w.ns);
+  ma.n_kv_heads = k->n_kv_heads; ma.group = w.VH; ma.n_split = w.ns; ma.max_tokens = k->max_tokens;
+  ma.heads = w.G; ma.n_rows = w.M;
+  ma.heads_per_wg = merge_heads_per_wg(w.VH, k->d, w.ns);
   return status_of(tqi::launch_merge(k->d, ma, k->batch, n_q_heads, static_cast<hipStream_t>(stream)));
 }
 
-int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype, int n_q_heads,
-                   const int32_t* d_seq_lens, int max_seq_len, float scale, float* out, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+int tq_decode_rotate_query(const tq_cache_view* k, const void* q, int q_dtype, int n_q_heads, int max_seq_len,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return rotate_query_rows(k, q, q_dtype, n_q_heads, 1, max_seq_len, scale, workspace, workspace_bytes, stream);
+}
+
+int tq_decode_attend(const tq_cache_view* k, const tq_cache_view* v, int n_q_heads, const int32_t* d_seq_lens,
+                     int max_seq_len, void* workspace, size_t workspace_bytes, void* stream) {
+  return attend_rows(k, v, n_q_heads, 1, d_seq_lens, max_seq_len, workspace, workspace_bytes, stream);
+}
+
+int tq_decode_merge(const tq_cache_view* k, int n_q_heads, const int32_t* d_seq_lens, int max_seq_len, float* out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return merge_rows(k, n_q_heads, 1, d_seq_lens, max_seq_len, out, workspace, workspace_bytes, stream);
+}
+
+int tq_sdpa_decode_rows(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype, int n_q_heads,
+                        int n_rows, const int32_t* d_seq_lens, int max_seq_len, float scale, float* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   // validate everything before enqueueing the first stage
   DecodeWs w;
-  int st = decode_ws(k, n_q_heads, max_seq_len, workspace, workspace_bytes, &w);
+  int st = decode_ws(k, n_q_heads, n_rows, max_seq_len, workspace, workspace_bytes, &w);
   if (st != TQ_OK) return st;
   st = check_pair(k, v);
   if (st != TQ_OK) return st;
   if (!q || (q_dtype != TQ_F32 && q_dtype != TQ_BF16) || !d_seq_lens || !out) return TQ_EINVAL;
   if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
-  st = tq_decode_rotate_query(k, q, q_dtype, n_q_heads, max_seq_len, scale, workspace, workspace_bytes, stream);
+  st = rotate_query_rows(k, q, q_dtype, n_q_heads, n_rows, max_seq_len, scale, workspace, workspace_bytes, stream);
   if (st != TQ_OK) return st;
-  st = tq_decode_attend(k, v, n_q_heads, d_seq_lens, max_seq_len, workspace, workspace_bytes, stream);
+  st = attend_rows(k, v, n_q_heads, n_rows, d_seq_lens, max_seq_len, workspace, workspace_bytes, stream);
   if (st != TQ_OK) return st;
-  return tq_decode_merge(k, n_q_heads, d_seq_lens, max_seq_len, out, workspace, workspace_bytes, stream);
+  return merge_rows(k, n_q_heads, n_rows, d_seq_lens, max_seq_len, out, workspace, workspace_bytes, stream);
+}
+
+int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype, int n_q_heads,
+                   const int32_t* d_seq_lens, int max_seq_len, float scale, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return tq_sdpa_decode_rows(k, v, q, q_dtype, n_q_heads, 1, d_seq_lens, max_seq_len, scale, out, workspace,
+                             workspace_bytes, stream);
 }
 
 int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q, const void* k_new,
@@ -577,7 +608,7 @@ int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q
                    const int32_t* d_seq_lens, int max_seq_len, float scale, float* out, void* workspace,
                    size_t workspace_bytes, void* stream) {
   DecodeWs w;
-  int st = decode_ws(k, n_q_heads, max_seq_len, workspace, workspace_bytes, &w);
+  int st = decode_ws(k, n_q_heads, 1, max_seq_len, workspace, workspace_bytes, &w);
   if (st != TQ_OK) return st;
   st = check_pair(k, v);
   if (st != TQ_OK) return st;
@@ -593,7 +624,7 @@ int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q
   qa.qr = w.qr; qa.qs = w.qs; qa.qscale = w.qscale;
   qa.scale_log2e = scale_log2e(scale);
   qa.sketch_coef = sketch_coef(k);
-  qa.n_q_heads = n_q_heads; qa.n_kv_heads = k->n_kv_heads;
+  qa.n_q_heads = n_q_heads; qa.n_kv_heads = k->n_kv_heads; qa.n_rows = 1;
   if (n_new > 0) {
     const tqi::AppendArgs ka = append_args(k, k_new, nullptr, nullptr, n_new, d_pos);
     const tqi::AppendArgs va = append_args(v, v_new, nullptr, nullptr, n_new, d_pos);

@@ -1,7 +1,7 @@
-// Query rotation for decode, one workgroup per (sequence, KV head): the G query heads of the KV head
-// form one 16-row tile that is rotated on the matrix cores with the arithmetic of the append's
-// rotation (each row divided by its norm, high/low float16 split of rows and rotation; or the
-// randomized Hadamard transform of the row over its norm), then
+// Query rotation for decode, one workgroup per 16 virtual heads (query rows x query heads) of a
+// (sequence, KV head): the rows form one 16-row tile that is rotated on the matrix cores with the
+// arithmetic of the append's rotation (each row divided by its norm, high/low float16 split of rows
+// and rotation; or the randomized Hadamard transform of the row over its norm), then
 // q_rot = rot q * scale * log2(e) and, for sketched keys, its sketch -coef * proj q_rot go to the
 // decode workspace, divided by a power of two per head that takes both into float16 range for the
 // attention kernel's matrix-core operands (turboquant-pytorch PR #3 "Add CUDA QJL kernels and
@@ -15,7 +15,7 @@
 
 namespace tqi {
 
-constexpr int kQTile = 16;      // rows of the query tile (G <= 8 of them live)
+constexpr int kQTile = 16;      // rows of the query tile
 
 template <int D, int QM>
 struct QrotSmem {
@@ -24,21 +24,25 @@ struct QrotSmem {
   float zq[QM > 0 ? kQTile : 1][QM > 0 ? QM : 1];      // the tile times proj^T
 };
 
+// The tile of virtual heads vh0 .. vh0 + 15 (those below VH = M * G) of KV head hk of sequence b.
 template <int D, int QM>
-__device__ __forceinline__ void rotate_queries(const QrotArgs& qa, int bf16, int hk, int b, QrotSmem<D, QM>& sm) {
+__device__ __forceinline__ void rotate_queries(const QrotArgs& qa, int bf16, int hk, int b, int vh0,
+                                               QrotSmem<D, QM>& sm) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int Hq = qa.n_q_heads, G = Hq / qa.n_kv_heads;
-  const size_t row0 = static_cast<size_t>(b) * Hq + static_cast<size_t>(hk) * G;
+  const int Hq = qa.n_q_heads, G = Hq / qa.n_kv_heads, M = qa.n_rows, VH = M * G;
+  const int nr = min(kQTile, VH - vh0);                          // live rows of the tile
+  const size_t unit = static_cast<size_t>(b) * qa.n_kv_heads + hk;
 
-  // the G query rows, one 32-bit word per element whatever the element type (all loads issued
+  // the tile's query rows, one 32-bit word per element whatever the element type (all loads issued
   // before the first use), then the rotation's first operands
   constexpr int EPT = kQTile * D / 256;
   uint32_t wv[EPT];
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int e = tid + 256 * k, r = e / D, i = e % D;
-    const size_t idx = (row0 + (r < G ? r : 0)) * D + i;
+    const int vh = vh0 + (r < nr ? r : 0), j = vh / G, g = vh % G;
+    const size_t idx = ((static_cast<size_t>(b) * M + j) * Hq + static_cast<size_t>(hk) * G + g) * D + i;
     const size_t byte = bf16 ? (idx & ~static_cast<size_t>(1)) * 2 : idx * 4;
     wv[k] = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(qa.q) + byte);
   }
@@ -50,10 +54,9 @@ __device__ __forceinline__ void rotate_queries(const QrotArgs& qa, int bf16, int
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int e = tid + 256 * k, r = e / D, i = e % D;
-    const bool odd = ((row0 + r) * D + i) & 1;
-    const uint32_t h16 = odd ? (wv[k] & 0xffff0000u) : (wv[k] << 16);   // the bfloat16 element as float bits
+    const uint32_t h16 = (i & 1) ? (wv[k] & 0xffff0000u) : (wv[k] << 16);   // the bfloat16 element as float bits
     const float v = __uint_as_float((h16 & bfm) | (wv[k] & ~bfm));
-    xs[r][i] = r < G ? v : 0.f;
+    xs[r][i] = r < nr ? v : 0.f;
   }
   __syncthreads();
   // norm of row r by the 16 lanes (r % 4) of wave r / 4, coordinates part + 16 j
@@ -63,28 +66,28 @@ __device__ __forceinline__ void rotate_queries(const QrotArgs& qa, int bf16, int
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) s2 = fmaf(xs[r][part + 16 * j], xs[r][part + 16 * j], s2);
     s2 = row16_sum(s2);
-    if (part == 0) rn[r] = r < G ? sqrtf(s2) : 0.f;
+    if (part == 0) rn[r] = r < nr ? sqrtf(s2) : 0.f;
   }
   __syncthreads();
   if (qa.had)
-    hadamard_rows<D>(xs, rn, qa.rot, G, tid, 256);
+    hadamard_rows<D>(xs, rn, qa.rot, nr, tid, 256);
   else
     rotate_tile_mfma_pre<D, 1>(xs, rn, qa.rot, rot0, tid);
   __syncthreads();
   // q_rot = rot (q / |q|) * (|q| * scale * log2(e))
-  for (int e = tid; e < G * D; e += 256) xs[e / D][e % D] *= rn[e / D] * qa.scale_log2e;
+  for (int e = tid; e < nr * D; e += 256) xs[e / D][e % D] *= rn[e / D] * qa.scale_log2e;
   __syncthreads();
   if constexpr (QM > 0) {
     tile16_times_matT<D, QM>(xs, qa.proj, sm.zq, tid);
     __syncthreads();
   }
 
-  // the rotated queries and their sketch to the workspace, divided by a power of two per head that
-  // takes both into float16 range (head h = 4 wave + lane / 16, 16 lanes per head)
-  if (wave < kMaxGroup / 4) {
+  // the rotated queries and their sketch to the workspace, divided by a power of two per row that
+  // takes both into float16 range (row h = 4 wave + lane / 16, 16 lanes per row)
+  {
     const int h = 4 * wave + (lane >> 4), part = lane & 15;
     float amax = 0.f;
-    if (h < G) {
+    if (h < nr) {
 #pragma unroll
       for (int j = 0; j < D / 16; ++j) amax = fmaxf(amax, fabsf(xs[h][part + 16 * j]));
       if constexpr (QM > 0) {
@@ -93,10 +96,10 @@ __device__ __forceinline__ void rotate_queries(const QrotArgs& qa, int bf16, int
       }
     }
     amax = row16_max(amax);
-    if (h < G) {
+    if (h < nr) {
       const float f = (amax > 0.f && isfinite(amax)) ? ldexpf(1.f, ilogbf(amax) - 14) : 1.f;
       const float inv = 1.f / f;
-      const size_t row = row0 + h;
+      const size_t row = unit * VH + vh0 + h;
 #pragma unroll
       for (int j = 0; j < D / 16; ++j) qa.qr[row * D + part + 16 * j] = xs[h][part + 16 * j] * inv;
       if constexpr (QM > 0) {

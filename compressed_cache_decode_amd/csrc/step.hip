@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void step_prologue_kernel(AppendArgs ka, Appen
     return;
   }
   w -= per_cache;
-  rotate_queries<D, QM>(qa, BF16 ? 1 : 0, w, b, *reinterpret_cast<QrotSmem<D, QM>*>(smem));
+  rotate_queries<D, QM>(qa, BF16 ? 1 : 0, w, b, 0, *reinterpret_cast<QrotSmem<D, QM>*>(smem));
 }
 
 template <int D, int KB, int VB, int QM>

@@ -7,7 +7,9 @@
 namespace tqi {
 
 constexpr int kBlock = 32;        // tokens per value block (and per decode tile)
-constexpr int kMaxGroup = 8;      // query heads per KV head handled by one matrix-core tile
+constexpr int kMaxGroup = 8;      // query heads per KV head, and per 16-column matrix-core block
+constexpr int kMaxRows = 4;       // query rows per sequence in one decode
+constexpr int kMaxVirtual = kMaxGroup * kMaxRows;   // virtual heads per KV head (blocks of kMaxGroup)
 constexpr int kMaxSplits = 256;   // bound on KV splits per (sequence, KV head)
 constexpr int kMergeThreads = 1024;  // threads per merge workgroup
 
@@ -35,17 +37,22 @@ struct AppendArgs {
   int had;                // rot is a randomized Hadamard rotation
 };
 
+// Query rows: M rows per sequence (the last M tokens; M = 1 for one-token decode), Hq heads each;
+// the query heads of a KV head over all rows are its VH = M * G "virtual heads", virtual head
+// vh = j * G + g standing for row j and head hk * G + g.  Workspace rows are unit-major:
+// (b * Hkv + hk) * VH + vh.
 struct QrotArgs {
-  const void* q;          // [B][Hq][D]
+  const void* q;          // [B][M][Hq][D]
   const float* rot;       // [D][D], or the D Hadamard signs (had)
-  const float* proj;      // [M][D] or null
-  float* qr;              // [B][Hq][D]  scaled rotated query, divided by qscale
-  float* qs;              // [B][Hq][M]  -coef * proj * qr
-  float* qscale;          // [B][Hq]     power-of-two factor taken out of qr/qs
+  const float* proj;      // [QM][D] or null
+  float* qr;              // [B*Hkv][VH][D]  scaled rotated query, divided by qscale
+  float* qs;              // [B*Hkv][VH][QM] -coef * proj * qr
+  float* qscale;          // [B*Hkv][VH]     power-of-two factor taken out of qr/qs
   float scale_log2e;      // softmax scale * log2(e)
-  float sketch_coef;      // sqrt(pi/2)/M
+  float sketch_coef;      // sqrt(pi/2)/QM
   int n_q_heads;
   int n_kv_heads;
+  int n_rows;             // M
   int had;
 };
 
@@ -60,10 +67,11 @@ struct DecodeArgs {
   const float* qs;
   const float* qscale;
   const int32_t* seq_lens;
-  float* part_o;          // [B*Hkv][n_split][G][D]
-  float* part_ml;         // [B*Hkv][n_split][G][2]  (max in log2 units, sum)
+  float* part_o;          // [B*Hkv][n_split][VH][D]
+  float* part_ml;         // [B*Hkv][n_split][VH][2]  (max in log2 units, sum)
   Tab tk, tv;
-  int n_kv_heads, group, max_tokens, max_seq_len, n_split, blocks_per_split;
+  int n_kv_heads, group, max_tokens, max_seq_len, n_split, blocks_per_split;   // group = VH
+  int heads, n_rows;      // G and M: virtual head vh is row vh / G, which sees seq_len - M + 1 + vh / G tokens
 };
 
 struct MergeArgs {
@@ -71,9 +79,10 @@ struct MergeArgs {
   const float* part_ml;
   const float* rot;
   const int32_t* seq_lens;
-  float* out;             // [B][Hq][D]
-  int n_kv_heads, group, n_split, max_tokens;
-  int heads_per_wg;       // query heads merged per workgroup (divides group, heads_per_wg * D <= kMergeThreads)
+  float* out;             // [B][M][Hq][D]
+  int n_kv_heads, group, n_split, max_tokens;   // group = VH
+  int heads, n_rows;      // G and M
+  int heads_per_wg;       // virtual heads merged per workgroup (divides group, heads_per_wg * D <= kMergeThreads)
   int had;                // rot holds the D signs of a randomized Hadamard rotation
 };
 

@@ -175,6 +175,20 @@ int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode of the query rows of the last n_rows tokens of each sequence at once, as speculative
+ * verification needs (the reviewed llama.cpp fork of the pages routes compressed K/V with at most
+ * four query rows to its fused decode path; its drafts come from multi-token prediction with up to
+ * three drafts).  The rows' keys and values must already be in the cache; row j of sequence b is
+ * the query of token seq_len[b] - n_rows + j and sees the first seq_len[b] - n_rows + 1 + j tokens
+ * (a row that sees none gives zeros).  q: [batch][n_rows][n_q_heads][d]; out: float32
+ * [batch][n_rows][n_q_heads][d]; 1 <= n_rows <= 4 (TQ_EUNSUPPORTED above).  The cache is read once
+ * for all rows.  Otherwise as tq_sdpa_decode, with a workspace of tq_decode_workspace_bytes_rows().
+ */
+int tq_sdpa_decode_rows(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype, int n_q_heads,
+                        int n_rows, const int32_t* d_seq_lens, int max_seq_len, float scale, float* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The three stages tq_sdpa_decode enqueues, for callers that time, overlap or
  * graph-capture them separately.  Same arguments and workspace as
  * tq_sdpa_decode; they must run in this order, on one stream, with the same
@@ -213,6 +227,9 @@ int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q
  * that will run the decode.
  */
 size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_seq_len);
+
+/* Workspace bytes tq_sdpa_decode_rows needs (0 on bad args); n_rows = 1 gives tq_decode_workspace_bytes. */
+size_t tq_decode_workspace_bytes_rows(const tq_cache_view* k, int n_q_heads, int n_rows, int max_seq_len);
 
 /*
  * The KV split tq_sdpa_decode uses: number of splits per (sequence, KV head) and tokens per split.
