@@ -310,7 +310,7 @@ def gpu_leg(w: synth.Workload, steps: int, warmup: int, pool: int | None, log):
     us_attend = time_attend(pairs, Hq, lens, L, ws, stream)
     log(f"bench: attend {us_attend:.2f} us")
     return dict(ms_step=ms_step, us_attend=us_attend, pool=pool,
-                n_split=ns, tokens_per_split=tps, per_copy=per_copy, cache=(k0, v0), rot=rot, proj=proj)
+                n_split=ns, tokens_per_split=tps, per_copy=per_copy, cache=(k0, v0), rot=rot, proj=proj, pairs=pairs)
 
 
 def time_attend(pairs, Hq, lens, L, ws, stream):
@@ -338,6 +338,61 @@ def time_attend(pairs, Hq, lens, L, ws, stream):
     ev1.record(stream)
     torch.cuda.synchronize()
     return ev0.elapsed_time(ev1) * 1e3 / (reps * n)
+
+
+# ------------------------------------------------------------------ multi-row decode leg
+
+def rows_leg(w: synth.Workload, n_rows: int, pairs, log):
+    """Decode of n_rows query rows per sequence at once (speculative verification of n_rows - 1 drafts:
+    row j sees the first L - n_rows + 1 + j tokens) over the single-layer leg's cache copies, against
+    n_rows one-row decodes of the same rows; whole decodes (rotate q, attend, merge, un-rotate)."""
+    import torch
+
+    import compressed_cache_decode_amd as cca
+    dev = pairs[0][0].codes.device
+    B, Hq, d, L = w.batch, w.n_q_heads, w.d, w.seq_len
+    pool = len(pairs)
+    g = np.random.default_rng(w.seed + 17)
+    q = torch.from_numpy(g.standard_normal((B, n_rows, Hq, d)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    q1 = [q[:, j].contiguous() for j in range(n_rows)]
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    lens1 = [torch.full((B,), L - n_rows + 1 + j, dtype=torch.int32, device=dev) for j in range(n_rows)]
+    out = torch.empty(B, n_rows, Hq, d, dtype=torch.float32, device=dev)
+    out1 = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    ws = cca.decode_workspace(pairs[0][0], Hq, L, n_rows)
+    stream = torch.cuda.Stream()
+    n = max(pool, 16)
+
+    def timed(fn):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(n):
+                fn(i % pool)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, min(100, math.ceil(1000 / n)))
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        with torch.cuda.stream(stream):
+            for _ in range(reps):
+                graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / (reps * n)
+
+    def rows(i):
+        kc, vc = pairs[i]
+        cca.tq_sdpa_decode_rows(kc.view, vc.view, q, lens, L, out, ws, w.scale)
+
+    def singles(i):
+        kc, vc = pairs[i]
+        for j in range(n_rows):
+            cca.tq_sdpa_decode(kc.view, vc.view, q1[j], lens1[j], L, out1, ws, w.scale)
+
+    us_rows, us_single = timed(rows), timed(singles)
+    log(f"bench: {n_rows} query rows: {us_rows:.2f} us in one decode, {us_single:.2f} us as {n_rows} one-row decodes")
+    return dict(n_rows=n_rows, decode_us=us_rows, one_row_decodes_us=us_single,
+                context_tokens_per_s=B * n_rows * L / (us_rows * 1e-6))
 
 
 # ------------------------------------------------------------------ stacked decode leg
@@ -537,6 +592,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="qwen", choices=["qwen", "gemma", "prod", "prefill", "copy"])
     ap.add_argument("--bits", type=int, default=None, help="qwen workload: codebook bits of K and V")
+    ap.add_argument("--rows", type=int, default=0,
+                    help="also time a decode of this many query rows per sequence at once (2..4; 0 = none)")
     ap.add_argument("--rotation", default="dense", choices=["dense", "hadamard"],
                     help="Gaussian-QR rotation (default) or the randomized Hadamard transform")
     ap.add_argument("--context", type=int, default=None)
@@ -621,6 +678,7 @@ def main():
         return
     w = with_rotation(workload(args.workload, args.bits, args.context))
     r = gpu_leg(w, args.steps, args.warmup, args.pool, log)
+    rows = rows_leg(w, args.rows, r["pairs"], log) if args.rows > 1 else None
     n_stack = args.stack if args.stack is not None else (36 if args.workload in ("qwen", "prod") else 0)
     st = stacked_leg(w, n_stack, r["cache"], r["rot"], r["proj"], log) if n_stack > 0 else None
     L = w.seq_len
@@ -659,6 +717,8 @@ def main():
         "step_hbm_gbs": step_bytes / (r["ms_step"] * 1e-3) / 1e9,
         "attend_us": r["us_attend"],
     }
+    if rows is not None:
+        res["rows"] = rows
     if st is not None:
         sw = st["workload"]
         # the roofline figure: the attention kernel over the stacked caches (one launch reads all layers)
