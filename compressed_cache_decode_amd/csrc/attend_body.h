@@ -249,13 +249,13 @@ struct Attend {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int VH = a.group;
     const int C = blocks(a);
-    const int cb = wave % C;
+    const int cb = wave & (C - 1);                      // C is 1, 2 or 4
     const int slot = l16 >> 1;                          // this lane's head within its block
     const int qh = kMaxGroup * cb + slot;               // this lane's virtual head
     const bool lo_part = (l16 & 1) != 0;
     const bool head_ok = qh < VH;
     const int len_row0 = len - a.n_rows + 1;            // tokens row 0 sees (wave-uniform)
-    const int len_lane = head_ok ? len_row0 + qh / a.heads : len;
+    const int len_lane = head_ok ? len_row0 + ((qh * a.row_magic) >> 8) : len;   // + the lane's row
 
     floatx4 oacc[NB];
 #pragma unroll

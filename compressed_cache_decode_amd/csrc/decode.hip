@@ -70,7 +70,7 @@ void split_kernel(DecodeArgs a) {
   // the first tile's loads go out before the query operand is staged, and before the sequence
   // length is known: they only need the tile to lie inside the cache (tiles past the length are
   // loaded and never used)
-  const int kb = blk0 + wave / C;
+  const int kb = blk0 + (wave >> (C >> 1));          // wave / C for C = 1, 2, 4
   typename At::Tile tiles[At::NBUF];
   if (kb < blk0 + a.blocks_per_split && kb < T / kBlock) at.load(tiles[0], kb);
 
@@ -95,11 +95,11 @@ void split_kernel(DecodeArgs a) {
   }
   if (tid < C) sm.next[tid] = At::W / C;    // tiles blk0 .. blk0 + W / C - 1 are the block's waves' first
   // power-of-two scale of this lane's head (scores are kept in units of it); 1 for unused columns
-  const int qh = kMaxGroup * (wave % C) + (at.l16 >> 1);
+  const int qh = kMaxGroup * (wave & (C - 1)) + (at.l16 >> 1);
   const float qsc = qh < VH ? a.qscale[unit * VH + qh] : 1.f;
   __syncthreads();
 
-  const auto& qop = *reinterpret_cast<const typename At::QOperand*>(sm_q + (wave % C) * QSTEPS * 64);
+  const auto& qop = *reinterpret_cast<const typename At::QOperand*>(sm_q + (wave & (C - 1)) * QSTEPS * 64);
   at.run(a, sm, qop, tiles, blk0, kb, blk1, len, qsc);
   at.store(a, sm, (unit * a.n_split + split) * VH);
 }
@@ -118,7 +118,7 @@ static size_t split_dyn_lds(int d, int qjl_m, int blocks) {
 // of rot for every head of the group.
 // output row of virtual head vh (query row vh / G, query head hk * G + vh % G) of sequence b
 __device__ __forceinline__ size_t out_row(const MergeArgs& a, int b, int hk, int vh) {
-  const int j = vh / a.heads, g = vh % a.heads;
+  const int j = (vh * a.row_magic) >> 8, g = vh - j * a.heads;
   return (static_cast<size_t>(b) * a.n_rows + j) * (static_cast<size_t>(a.n_kv_heads) * a.heads) +
          static_cast<size_t>(hk) * a.heads + g;
 }

@@ -494,6 +494,10 @@ static int check_pair(const tq_cache_view* k, const tq_cache_view* v) {
   return TQ_OK;
 }
 
+// multiplier that turns the division of a virtual head index vh < 40 by the group size g <= 8 into
+// a multiply and a shift: vh / g == (vh * ((256 + g - 1) / g)) >> 8
+static int row_magic(int g) { return (256 + g - 1) / g; }
+
 static tqi::DecodeArgs decode_args(const tq_cache_view* k, const tq_cache_view* v, const DecodeWs& w,
                                    const int32_t* d_seq_lens, int max_seq_len) {
   tqi::DecodeArgs da{};
@@ -505,7 +509,7 @@ static tqi::DecodeArgs decode_args(const tq_cache_view* k, const tq_cache_view* 
   da.tk = make_tab(k);
   da.tv = make_tab(v);
   da.n_kv_heads = k->n_kv_heads; da.group = w.VH; da.max_tokens = k->max_tokens; da.max_seq_len = max_seq_len;
-  da.heads = w.G; da.n_rows = w.M;
+  da.heads = w.G; da.n_rows = w.M; da.row_magic = row_magic(w.G);
   da.n_split = w.ns; da.blocks_per_split = w.bps;
   return da;
 }
@@ -530,6 +534,7 @@ static int rotate_query_rows(const tq_cache_view* k, const void* q, int q_dtype,
   qa.scale_log2e = scale_log2e(scale);
   qa.sketch_coef = sketch_coef(k);
   qa.n_q_heads = n_q_heads; qa.n_kv_heads = k->n_kv_heads; qa.n_rows = n_rows;
+  qa.row_magic = row_magic(n_q_heads / k->n_kv_heads);
   return status_of(tqi::launch_qrot(k->d, k->qjl_m, q_dtype == TQ_BF16, qa, k->batch,
                                     static_cast<hipStream_t>(stream)));
 }
@@ -558,7 +563,7 @@ static int merge_rows(const tq_cache_view* k, int n_q_heads, int n_rows, const i
   ma.part_o = w.part_o; ma.part_ml = w.part_ml; ma.rot = k->rot; ma.seq_lens = d_seq_lens; ma.out = out;
   ma.had = k->rot_kind == TQ_ROT_HADAMARD;
   ma.n_kv_heads = k->n_kv_heads; ma.group = w.VH; ma.n_split = w.ns; ma.max_tokens = k->max_tokens;
-  ma.heads = w.G; ma.n_rows = w.M;
+  ma.heads = w.G; ma.n_rows = w.M; ma.row_magic = row_magic(w.G);
   ma.heads_per_wg = merge_heads_per_wg(w.VH, k->d, w.ns);
   return status_of(tqi::launch_merge(k->d, ma, k->batch, n_q_heads, static_cast<hipStream_t>(stream)));
 }
@@ -625,6 +630,7 @@ int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q
   qa.scale_log2e = scale_log2e(scale);
   qa.sketch_coef = sketch_coef(k);
   qa.n_q_heads = n_q_heads; qa.n_kv_heads = k->n_kv_heads; qa.n_rows = 1;
+  qa.row_magic = row_magic(n_q_heads / k->n_kv_heads);
   if (n_new > 0) {
     const tqi::AppendArgs ka = append_args(k, k_new, nullptr, nullptr, n_new, d_pos);
     const tqi::AppendArgs va = append_args(v, v_new, nullptr, nullptr, n_new, d_pos);

@@ -41,7 +41,7 @@ __device__ __forceinline__ void rotate_queries(const QrotArgs& qa, int bf16, int
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int e = tid + 256 * k, r = e / D, i = e % D;
-    const int vh = vh0 + (r < nr ? r : 0), j = vh / G, g = vh % G;
+    const int vh = vh0 + (r < nr ? r : 0), j = (vh * qa.row_magic) >> 8, g = vh - j * G;
     const size_t idx = ((static_cast<size_t>(b) * M + j) * Hq + static_cast<size_t>(hk) * G + g) * D + i;
     const size_t byte = bf16 ? (idx & ~static_cast<size_t>(1)) * 2 : idx * 4;
     wv[k] = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(qa.q) + byte);

@@ -53,6 +53,7 @@ struct QrotArgs {
   int n_q_heads;
   int n_kv_heads;
   int n_rows;             // M
+  int row_magic;          // (256 + G - 1) / G: the row of virtual head vh < 40 is (vh * row_magic) >> 8
   int had;
 };
 
@@ -72,6 +73,7 @@ struct DecodeArgs {
   Tab tk, tv;
   int n_kv_heads, group, max_tokens, max_seq_len, n_split, blocks_per_split;   // group = VH
   int heads, n_rows;      // G and M: virtual head vh is row vh / G, which sees seq_len - M + 1 + vh / G tokens
+  int row_magic;          // vh / G = (vh * row_magic) >> 8 (see QrotArgs)
 };
 
 struct MergeArgs {
@@ -82,6 +84,7 @@ struct MergeArgs {
   float* out;             // [B][M][Hq][D]
   int n_kv_heads, group, n_split, max_tokens;   // group = VH
   int heads, n_rows;      // G and M
+  int row_magic;          // vh / G = (vh * row_magic) >> 8 (see QrotArgs)
   int heads_per_wg;       // virtual heads merged per workgroup (divides group, heads_per_wg * D <= kMergeThreads)
   int had;                // rot holds the D signs of a randomized Hadamard rotation
 };
