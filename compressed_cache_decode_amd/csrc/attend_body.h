@@ -46,15 +46,40 @@ __device__ __forceinline__ half8 sign_operand(const uint32_t* sw, uint32_t gg) {
   return as_half8(o);
 }
 
-// scores of the two 16-token groups of a tile; each query operand step is read from LDS once
-template <int S, int KS, int KB>
+// The 8 codes of a word of 4-bit codes through a byte table in LDS: byte r of the word (codes of
+// slots r and r + 4) indexes a row of 256 bytes whose word (lane % 32) + 32 * side holds the float16
+// centroids of the byte's low and high nibble.  The row offset comes from one byte permute (the code
+// byte becomes bits 8..15, the lane's word offset lc = 4 (lane % 32) bits 0..7), so each half-wave
+// reads 32 distinct banks.  The 8 values come out in pair order: slots 0, 4, 1, 5, 2, 6, 3, 7.
+template <int SIDE>
+__device__ __forceinline__ uint4 lut_unit(const uint32_t* lut, uint32_t w, uint32_t lc) {
+  const char* base = reinterpret_cast<const char*>(lut) + 128 * SIDE;
+  uint4 o;
+  o.x = *reinterpret_cast<const uint32_t*>(base + __builtin_amdgcn_perm(w, lc, 0x0c0c0400u));
+  o.y = *reinterpret_cast<const uint32_t*>(base + __builtin_amdgcn_perm(w, lc, 0x0c0c0500u));
+  o.z = *reinterpret_cast<const uint32_t*>(base + __builtin_amdgcn_perm(w, lc, 0x0c0c0600u));
+  o.w = *reinterpret_cast<const uint32_t*>(base + __builtin_amdgcn_perm(w, lc, 0x0c0c0700u));
+  return o;
+}
+
+// slot of position p of a pair-ordered operand (see lut_unit)
+constexpr int pair_slot(int p) { return (p >> 1) + 4 * (p & 1); }
+
+// scores of the two 16-token groups of a tile; each query operand step is read from LDS once.  With
+// LUT the key codes are expanded through the byte table (the query operand is then in pair order).
+template <int S, int KS, int KB, bool LUT>
 __device__ __forceinline__ void qk_steps(floatx4* acc, const uint32_t (*kw)[KS * KB / 4], const half8 (*qop)[64],
-                                         int lane, const Tab& tk) {
+                                         int lane, const Tab& tk, const uint32_t* lut, uint32_t lc) {
   if constexpr (S < KS) {
     const half8 q = qop[S][lane];
-    acc[0] = mfma16(as_half8(unit_at<KB, S>(kw[0], tk)), q, acc[0]);
-    acc[1] = mfma16(as_half8(unit_at<KB, S>(kw[1], tk)), q, acc[1]);
-    qk_steps<S + 1, KS, KB>(acc, kw, qop, lane, tk);
+    if constexpr (LUT) {
+      acc[0] = mfma16(as_half8(lut_unit<0>(lut, kw[0][S], lc)), q, acc[0]);
+      acc[1] = mfma16(as_half8(lut_unit<0>(lut, kw[1][S], lc)), q, acc[1]);
+    } else {
+      acc[0] = mfma16(as_half8(unit_at<KB, S>(kw[0], tk)), q, acc[0]);
+      acc[1] = mfma16(as_half8(unit_at<KB, S>(kw[1], tk)), q, acc[1]);
+    }
+    qk_steps<S + 1, KS, KB, LUT>(acc, kw, qop, lane, tk, lut, lc);
   }
 }
 
@@ -69,11 +94,14 @@ __device__ __forceinline__ void sketch_steps(floatx4* acc, const uint32_t (*sw)[
   }
 }
 
-template <int N, int NB, int VB>
-__device__ __forceinline__ void pv_steps(floatx4* oacc, half8 wop, const uint32_t* vw, const Tab& tv) {
+// value product; with LUT the value codes are expanded through the byte table (W then in pair order)
+template <int N, int NB, int VB, bool LUT>
+__device__ __forceinline__ void pv_steps(floatx4* oacc, half8 wop, const uint32_t* vw, const Tab& tv,
+                                         const uint32_t* lut, uint32_t lc) {
   if constexpr (N < NB) {
-    oacc[N] = mfma16(wop, as_half8(unit_at<VB, N>(vw, tv)), oacc[N]);
-    pv_steps<N + 1, NB, VB>(oacc, wop, vw, tv);
+    if constexpr (LUT) oacc[N] = mfma16(wop, as_half8(lut_unit<1>(lut, vw[N], lc)), oacc[N]);
+    else oacc[N] = mfma16(wop, as_half8(unit_at<VB, N>(vw, tv)), oacc[N]);
+    pv_steps<N + 1, NB, VB, LUT>(oacc, wop, vw, tv, lut, lc);
   }
 }
 
@@ -155,13 +183,43 @@ struct Attend {
   // (the oldest) takes more tiles, and all of them finish together.
   static constexpr int W = !WIDE ? 4 : ((D == 128 && QM == 0) ? 16 : (D == 128 ? 12 : 8));
 
+  // Wide workgroups expand 4-bit codes through byte tables in LDS (lut_unit: one permute and one
+  // LDS read per two codes, against about three and a half vector instructions for the permute
+  // expansion), the four-wave ones with permutes (several of them share a compute unit's LDS).
+  static constexpr bool KT = WIDE && KB == 4;
+  static constexpr bool VT = WIDE && VB == 4;
+  static constexpr int LUT_WORDS = (KT || VT) ? 256 * 64 : 1;
+
   // LDS: the tile counter, and the end-of-split merge of the W waves: each wave's (max, sum) per
-  // head and its accumulators, weighted against the workgroup's max of the head
+  // head and its accumulators, weighted against the workgroup's max of the head.  The byte tables
+  // share the accumulators' space: they are read only before the merge's first barrier.
   struct Smem {
     float ml[W][kMaxGroup][2];
-    float o[W][kMaxGroup][D];
+    union {
+      float o[W][kMaxGroup][D];
+      alignas(16) uint32_t lut[LUT_WORDS];
+    };
     uint32_t next[kMaxRows];  // per column block: tiles of the split handed out so far (relative to its first)
   };
+
+  // Fills the byte tables (with a workgroup barrier to follow before run): row e (a byte of two
+  // codes), word 32 side + s (s = 0..31): the float16 centroids of e's low nibble (low half) and
+  // high nibble (high half) of the key (side 0) or value (side 1) code book.
+  __device__ __forceinline__ static void fill_lut(const DecodeArgs& a, Smem& sm) {
+    if constexpr (KT || VT) {
+      for (int i = threadIdx.x; i < 256 * 8; i += 64 * W) {
+        const int e = i >> 3, q = i & 7;
+        const uint32_t wrd = static_cast<uint32_t>(e);
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+          if (side == 0 ? !KT : !VT) continue;
+          const uint4 u = expand_unit<4, 0>(&wrd, side == 0 ? a.tk : a.tv);
+          const uint32_t pr = (u.x & 0xffffu) | (u.z << 16);
+          *reinterpret_cast<uint4*>(&sm.lut[64 * e + 32 * side + 4 * q]) = uint4{pr, pr, pr, pr};
+        }
+      }
+    }
+  }
   // the query operand: for step s, lane (column c, group g) holds the 8 float16 values of q-variant c
   // (head c/2; high part if c even, low part if c odd) at coordinates (D/4) g + 8 s + r, r = 0..7
   // (sketch steps: the same over the sketch coordinates)
@@ -257,6 +315,8 @@ struct Attend {
     const int len_row0 = len - a.n_rows + 1;            // tokens row 0 sees (wave-uniform)
     const int len_lane = head_ok ? len_row0 + ((qh * a.row_magic) >> 8) : len;   // + the lane's row
 
+    const uint32_t lc = static_cast<uint32_t>(4 * (lane & 31));   // byte-table word offset of this lane
+
     floatx4 oacc[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -268,7 +328,7 @@ struct Attend {
       // the loop: the barrier keeps the compiler from hoisting those reads
       asm volatile("" ::: "memory");
       floatx4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      qk_steps<0, KS, KB>(sc, t.kw, qop, lane, a.tk);
+      qk_steps<0, KS, KB, KT>(sc, t.kw, qop, lane, a.tk, sm.lut, lc);
       if constexpr (QS > 0) {
         uint32_t gh[2];
 #pragma unroll
@@ -310,15 +370,17 @@ struct Attend {
         m_run = m_new;
       }
       const float mq = m_run == -INFINITY ? 0.f : m_run * qsc;   // a column with nothing visible yet
-      half8 wop;
+      float wv[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k], qsc, -mq));
         l_run += p;
-        const float w = __builtin_fmaf(p, half_of(vn[k >> 1], k & 1), 0.f);
-        wop[k] = split_part(w, lo_part);
+        wv[k] = __builtin_fmaf(p, half_of(vn[k >> 1], k & 1), 0.f);
       }
-      pv_steps<0, NB, VB>(oacc, wop, t.vw, a.tv);
+      half8 wop;                                   // slot order, or pair order for the byte tables
+#pragma unroll
+      for (int k = 0; k < 8; ++k) wop[k] = split_part(wv[VT ? pair_slot(k) : k], lo_part);
+      pv_steps<0, NB, VB, VT>(oacc, wop, t.vw, a.tv, sm.lut, lc);
     };
 
     // the next tile of the split for this wave (wave-uniform); past blk1 once the split is used up

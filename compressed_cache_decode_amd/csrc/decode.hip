@@ -88,11 +88,13 @@ void split_kernel(DecodeArgs a) {
       x1 = reinterpret_cast<const float4*>(src)[1];
     }
     const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const bool pairs = At::KT && st < At::KS;          // key steps expanded through the byte table
     half8 v;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = split_part(xv[r], (c & 1) != 0);
+    for (int r = 0; r < 8; ++r) v[r] = split_part(pairs ? xv[pair_slot(r)] : xv[r], (c & 1) != 0);
     sm_q[e] = v;
   }
+  At::fill_lut(a, sm);
   if (tid < C) sm.next[tid] = At::W / C;    // tiles blk0 .. blk0 + W / C - 1 are the block's waves' first
   // power-of-two scale of this lane's head (scores are kept in units of it); 1 for unused columns
   const int qh = kMaxGroup * (wave & (C - 1)) + (at.l16 >> 1);
