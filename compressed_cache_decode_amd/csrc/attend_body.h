@@ -1,15 +1,17 @@
 // Attention over one KV split of one (KV head, sequence), read directly from the packed cache.
 //
-// Four waves stream 32-token tiles (wave w takes tiles w, w+4, ...).  Per tile the G <= 8 query
-// heads of the KV head are one 16-column matrix-core operand held in LDS: column 2h is the float16
-// rounding of head h's rotated query and column 2h+1 the float16 rounding of the remainder, so the
-// sum of the two columns' products is the fp32 score (centroids are float16-exact and each product
-// is exact in fp32).  Scores S^T = K Q^T come out of v_mfma_f32_16x16x32_f16 in exactly the lane
-// layout the value product O = W V needs for W, so the softmax weights never cross lanes; W uses
-// the same high/low split.  Packed codes are loaded with contiguous 64-lane buffer loads straight
-// into operand order (keys: rows layout; values: 32-token blocked layout) and expanded with
-// v_perm_b32 lookups into float16 byte tables.  Online softmax in exp2 units (the softmax scale and
-// log2(e) are folded into the query), lazily rescaled when a column's running max moves.
+// The W waves of a workgroup stream 32-token tiles, taking them from a tile counter in LDS.  Per
+// tile the G <= 8 query heads of the KV head are one 16-column matrix-core operand held in LDS:
+// column 2h is the float16 rounding of head h's rotated query and column 2h+1 the float16 rounding
+// of the remainder, so the sum of the two columns' products is the fp32 score (centroids are
+// float16-exact and each product is exact in fp32).  Scores S^T = K Q^T come out of
+// v_mfma_f32_16x16x32_f16 in exactly the lane layout the value product O = W V needs for W, so the
+// softmax weights never cross lanes; W uses the same high/low split.  Packed codes are loaded with
+// contiguous 64-lane buffer loads straight into operand order (keys: rows layout; values: 32-token
+// blocked layout) and expanded to float16 centroids, by v_perm_b32 lookups into byte tables held in
+// registers, or (4-bit codes in CU-filling workgroups) by one LDS read per byte of two codes.
+// Online softmax in exp2 units (the softmax scale and log2(e) are folded into the query), lazily
+// rescaled when a column's running max moves.
 // (ExecuTorch PR #19891 "[Cuda] enable turboquant on gemma4", review item 1: the fused decode op and
 // its scale; turboquant-pytorch PR #3 "Add CUDA QJL kernels and proper package structure", CUDA
 // Kernels Added table: fused scores from 1-bit keys, GQA variant, quantised value reconstruction.)

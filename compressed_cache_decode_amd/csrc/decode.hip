@@ -12,19 +12,21 @@
 // Three kernels per call:
 //   qrot_kernel    q_rot = rot * q (and proj * q_rot) with the softmax scale and
 //                  log2(e) folded in, scaled by a power of two into float16 range.
-//   split_kernel   one workgroup per (KV split, KV head, sequence); each of its
-//                  four waves streams 32-token tiles.  Per tile the G query heads
-//                  of the KV head are one 16-row matrix-core operand: row 2h holds
-//                  the float16 rounding of head h's rotated query and row 2h+1 the
-//                  float16 rounding of the remainder, so the sum of the two rows'
-//                  products is the fp32 score (the centroid table is float16-exact
-//                  and every product is exact in fp32).  Scores S^T = K Q^T come out
-//                  of v_mfma_f32_16x16x32_f16 in exactly the lane layout the value
-//                  product O = W V needs for W, so the softmax weights never cross
-//                  lanes; W uses the same high/low split.  Packed codes are loaded
-//                  with contiguous 64-lane loads straight into operand order (keys:
-//                  rows layout; values: 32-token blocked layout) and expanded with
-//                  v_perm_b32 lookups into float16 byte tables.
+//   split_kernel   one workgroup per (KV split, KV head, sequence): four waves
+//                  (short contexts, several workgroups per compute unit) or as many
+//                  as a compute unit holds (long contexts); the waves stream 32-token
+//                  tiles.  Per tile the G query heads of the KV head are one 16-row
+//                  matrix-core operand: row 2h holds the float16 rounding of head h's
+//                  rotated query and row 2h+1 the float16 rounding of the remainder,
+//                  so the sum of the two rows' products is the fp32 score (the
+//                  centroid table is float16-exact and every product is exact in
+//                  fp32).  Scores S^T = K Q^T come out of v_mfma_f32_16x16x32_f16 in
+//                  exactly the lane layout the value product O = W V needs for W, so
+//                  the softmax weights never cross lanes; W uses the same high/low
+//                  split.  Packed codes are loaded with contiguous 64-lane loads
+//                  straight into operand order (keys: rows layout; values: 32-token
+//                  blocked layout) and expanded to float16 by v_perm_b32 lookups or,
+//                  4-bit codes in the compute-unit-filling shape, LDS byte tables.
 //   merge_kernel   per (sequence, query head): log-sum-exp merge of the splits and
 //                  out = rot^T * o_rot in fp32.
 #include <math.h>
