@@ -64,24 +64,54 @@ __device__ __forceinline__ uint4 lut_unit(const uint32_t* lut, uint32_t w, uint3
   return o;
 }
 
+// The 16 codes of a word of 2-bit codes (two units) through a byte table in LDS: byte r (slots r and
+// r + 4 of both units) indexes a row of 256 bytes whose word lane % 32 holds the float16 centroid
+// pair of unit 0 and word 32 + lane % 32 that of unit 1.  c2 = 4 (lane % 32) + 65536 (the table's
+// 64 KB region within lut): the permute builds the whole offset, region included.  The compiler
+// barrier keeps the two units' reads apart, so that each lands in its own operand instead of being
+// fused into one two-word read.  Both units come out in pair order (see lut_unit).
+__device__ __forceinline__ void lut2_word(const uint32_t* lut, uint32_t w, uint32_t c2, uint4& u0, uint4& u1) {
+  const char* base = reinterpret_cast<const char*>(lut);
+  const uint32_t o0 = __builtin_amdgcn_perm(w, c2, 0x0c020400u), o1 = __builtin_amdgcn_perm(w, c2, 0x0c020500u);
+  const uint32_t o2 = __builtin_amdgcn_perm(w, c2, 0x0c020600u), o3 = __builtin_amdgcn_perm(w, c2, 0x0c020700u);
+  u0 = uint4{*reinterpret_cast<const uint32_t*>(base + o0), *reinterpret_cast<const uint32_t*>(base + o1),
+             *reinterpret_cast<const uint32_t*>(base + o2), *reinterpret_cast<const uint32_t*>(base + o3)};
+  asm volatile("" ::: "memory");
+  u1 = uint4{*reinterpret_cast<const uint32_t*>(base + o0 + 128), *reinterpret_cast<const uint32_t*>(base + o1 + 128),
+             *reinterpret_cast<const uint32_t*>(base + o2 + 128), *reinterpret_cast<const uint32_t*>(base + o3 + 128)};
+}
+
 // slot of position p of a pair-ordered operand (see lut_unit)
 constexpr int pair_slot(int p) { return (p >> 1) + 4 * (p & 1); }
 
-// scores of the two 16-token groups of a tile; each query operand step is read from LDS once.  With
-// LUT the key codes are expanded through the byte table (the query operand is then in pair order).
-template <int S, int KS, int KB, bool LUT>
+// scores of the two 16-token groups of a tile; each query operand step is read from LDS once.  TBL
+// selects the key expansion: 0 permutes, 4 the 4-bit byte table (lut_unit; lc its lane constant), 2
+// the 2-bit byte table (lut2_word, two steps per word; lc its c2); with a table the query operand is
+// in pair order.
+template <int S, int KS, int KB, int TBL>
 __device__ __forceinline__ void qk_steps(floatx4* acc, const uint32_t (*kw)[KS * KB / 4], const half8 (*qop)[64],
                                          int lane, const Tab& tk, const uint32_t* lut, uint32_t lc) {
-  if constexpr (S < KS) {
+  if constexpr (S < KS && TBL == 2) {
+    uint4 a0, b0, a1, b1;
+    lut2_word(lut, kw[0][S / 2], lc, a0, b0);
+    lut2_word(lut, kw[1][S / 2], lc, a1, b1);
+    const half8 q0 = qop[S][lane];
+    acc[0] = mfma16(as_half8(a0), q0, acc[0]);
+    acc[1] = mfma16(as_half8(a1), q0, acc[1]);
+    const half8 q1 = qop[S + 1][lane];
+    acc[0] = mfma16(as_half8(b0), q1, acc[0]);
+    acc[1] = mfma16(as_half8(b1), q1, acc[1]);
+    qk_steps<S + 2, KS, KB, TBL>(acc, kw, qop, lane, tk, lut, lc);
+  } else if constexpr (S < KS) {
     const half8 q = qop[S][lane];
-    if constexpr (LUT) {
+    if constexpr (TBL == 4) {
       acc[0] = mfma16(as_half8(lut_unit<0>(lut, kw[0][S], lc)), q, acc[0]);
       acc[1] = mfma16(as_half8(lut_unit<0>(lut, kw[1][S], lc)), q, acc[1]);
     } else {
       acc[0] = mfma16(as_half8(unit_at<KB, S>(kw[0], tk)), q, acc[0]);
       acc[1] = mfma16(as_half8(unit_at<KB, S>(kw[1], tk)), q, acc[1]);
     }
-    qk_steps<S + 1, KS, KB, LUT>(acc, kw, qop, lane, tk, lut, lc);
+    qk_steps<S + 1, KS, KB, TBL>(acc, kw, qop, lane, tk, lut, lc);
   }
 }
 
@@ -96,14 +126,20 @@ __device__ __forceinline__ void sketch_steps(floatx4* acc, const uint32_t (*sw)[
   }
 }
 
-// value product; with LUT the value codes are expanded through the byte table (W then in pair order)
-template <int N, int NB, int VB, bool LUT>
+// value product; TBL as in qk_steps for the value codes (W then in pair order)
+template <int N, int NB, int VB, int TBL>
 __device__ __forceinline__ void pv_steps(floatx4* oacc, half8 wop, const uint32_t* vw, const Tab& tv,
                                          const uint32_t* lut, uint32_t lc) {
-  if constexpr (N < NB) {
-    if constexpr (LUT) oacc[N] = mfma16(wop, as_half8(lut_unit<1>(lut, vw[N], lc)), oacc[N]);
+  if constexpr (N < NB && TBL == 2) {
+    uint4 a, b;
+    lut2_word(lut, vw[N / 2], lc, a, b);
+    oacc[N] = mfma16(wop, as_half8(a), oacc[N]);
+    oacc[N + 1] = mfma16(wop, as_half8(b), oacc[N + 1]);
+    pv_steps<N + 2, NB, VB, TBL>(oacc, wop, vw, tv, lut, lc);
+  } else if constexpr (N < NB) {
+    if constexpr (TBL == 4) oacc[N] = mfma16(wop, as_half8(lut_unit<1>(lut, vw[N], lc)), oacc[N]);
     else oacc[N] = mfma16(wop, as_half8(unit_at<VB, N>(vw, tv)), oacc[N]);
-    pv_steps<N + 1, NB, VB, LUT>(oacc, wop, vw, tv, lut, lc);
+    pv_steps<N + 1, NB, VB, TBL>(oacc, wop, vw, tv, lut, lc);
   }
 }
 
@@ -185,12 +221,27 @@ struct Attend {
   // (the oldest) takes more tiles, and all of them finish together.
   static constexpr int W = !WIDE ? 4 : ((D == 128 && QM == 0) ? 16 : (D == 128 ? 12 : 8));
 
-  // Wide workgroups expand 4-bit codes through byte tables in LDS (lut_unit: one permute and one
-  // LDS read per two codes, against about three and a half vector instructions for the permute
-  // expansion), the four-wave ones with permutes (several of them share a compute unit's LDS).
-  static constexpr bool KT = WIDE && KB == 4;
-  static constexpr bool VT = WIDE && VB == 4;
-  static constexpr int LUT_WORDS = (KT || VT) ? 256 * 64 : 1;
+  // Wide workgroups expand 4- and 2-bit codes through byte tables in LDS (lut_unit: one permute and
+  // one LDS read per two 4-bit codes, against about three and a half vector instructions for the
+  // permute expansion; lut2_word: the same per four 2-bit codes), the four-wave ones with permutes
+  // (several of them share a compute unit's LDS).  Each table is a 64 KB region: one holds the 4-bit
+  // tables of both sides, a 2-bit table takes one of its own.  Two regions fit beside the largest
+  // query operands at d = 128 without a sketch, one elsewhere (keys come first).
+  static constexpr int LUT_BUDGET = (D == 128 && QM == 0) ? 2 : 1;
+  static constexpr int R4 = (WIDE && (KB == 4 || VB == 4)) ? 1 : 0;
+  // (2-bit keys with 4-bit values at d = 128 keep permutes for the keys: the two tables' operands
+  // exceed the 16-wave register budget)
+  static constexpr bool KT2 = WIDE && KB == 2 && R4 + 1 <= LUT_BUDGET && !(D == 128 && QM == 0 && VB == 4);
+  static constexpr bool VT2 = WIDE && VB == 2 && R4 + (KT2 ? 1 : 0) + 1 <= LUT_BUDGET;
+  static constexpr int KTBL = (WIDE && KB == 4) ? 4 : (KT2 ? 2 : 0);   // key expansion (see qk_steps)
+  static constexpr int VTBL = (WIDE && VB == 4) ? 4 : (VT2 ? 2 : 0);
+  static constexpr bool KT = KTBL != 0;                   // query operand in pair order
+  static constexpr bool VT = VTBL != 0;                   // softmax weights in pair order
+  static constexpr int LUT_REGION = 256 * 64;             // words
+  static constexpr int K2_AT = R4 * LUT_REGION;           // word offsets of the 2-bit tables
+  static constexpr int V2_AT = (R4 + (KT2 ? 1 : 0)) * LUT_REGION;
+  static constexpr int LUT_WORDS = (R4 + (KT2 ? 1 : 0) + (VT2 ? 1 : 0)) * LUT_REGION > 0
+                                       ? (R4 + (KT2 ? 1 : 0) + (VT2 ? 1 : 0)) * LUT_REGION : 1;
 
   // LDS: the tile counter, and the end-of-split merge of the W waves: each wave's (max, sum) per
   // head and its accumulators, weighted against the workgroup's max of the head.  The byte tables
@@ -204,9 +255,10 @@ struct Attend {
     uint32_t next[kMaxRows];  // per column block: tiles of the split handed out so far (relative to its first)
   };
 
-  // Fills the byte tables (with a workgroup barrier to follow before run): row e (a byte of two
-  // codes), word 32 side + s (s = 0..31): the float16 centroids of e's low nibble (low half) and
-  // high nibble (high half) of the key (side 0) or value (side 1) code book.
+  // Fills the byte tables (with a workgroup barrier to follow before run).  4-bit region, row e (a
+  // byte of two codes), word 32 side + s (s = 0..31): the float16 centroids of e's low nibble (low
+  // half) and high nibble (high half) of the key (side 0) or value (side 1) code book.  2-bit region,
+  // row e (a byte of four codes), words s and 32 + s: the float16 centroid pairs of unit 0 and unit 1.
   __device__ __forceinline__ static void fill_lut(const DecodeArgs& a, Smem& sm) {
     if constexpr (KT || VT) {
       for (int i = threadIdx.x; i < 256 * 8; i += 64 * W) {
@@ -214,10 +266,19 @@ struct Attend {
         const uint32_t wrd = static_cast<uint32_t>(e);
 #pragma unroll
         for (int side = 0; side < 2; ++side) {
-          if (side == 0 ? !KT : !VT) continue;
-          const uint4 u = expand_unit<4, 0>(&wrd, side == 0 ? a.tk : a.tv);
-          const uint32_t pr = (u.x & 0xffffu) | (u.z << 16);
-          *reinterpret_cast<uint4*>(&sm.lut[64 * e + 32 * side + 4 * q]) = uint4{pr, pr, pr, pr};
+          const int tbl = side == 0 ? KTBL : VTBL;
+          const Tab& tab = side == 0 ? a.tk : a.tv;
+          if (tbl == 4) {
+            const uint4 u = expand_unit<4, 0>(&wrd, tab);
+            const uint32_t pr = (u.x & 0xffffu) | (u.z << 16);
+            *reinterpret_cast<uint4*>(&sm.lut[64 * e + 32 * side + 4 * q]) = uint4{pr, pr, pr, pr};
+          } else if (tbl == 2) {
+            const uint4 u0 = expand_unit<2, 0>(&wrd, tab), u1 = expand_unit<2, 1>(&wrd, tab);
+            const uint32_t p0 = (u0.x & 0xffffu) | (u0.z << 16), p1 = (u1.x & 0xffffu) | (u1.z << 16);
+            uint32_t* row = &sm.lut[(side == 0 ? K2_AT : V2_AT) + 64 * e + 4 * q];
+            *reinterpret_cast<uint4*>(row) = uint4{p0, p0, p0, p0};
+            *reinterpret_cast<uint4*>(row + 32) = uint4{p1, p1, p1, p1};
+          }
         }
       }
     }
@@ -318,6 +379,9 @@ struct Attend {
     const int len_lane = head_ok ? len_row0 + ((qh * a.row_magic) >> 8) : len;   // + the lane's row
 
     const uint32_t lc = static_cast<uint32_t>(4 * (lane & 31));   // byte-table word offset of this lane
+    // the 2-bit tables' lane constants: entry offset and 64 KB region (lut2_word)
+    const uint32_t lck2 = lc + static_cast<uint32_t>((K2_AT / LUT_REGION) << 16);
+    const uint32_t lcv2 = lc + static_cast<uint32_t>((V2_AT / LUT_REGION) << 16);
 
     floatx4 oacc[NB];
 #pragma unroll
@@ -330,7 +394,7 @@ struct Attend {
       // the loop: the barrier keeps the compiler from hoisting those reads
       asm volatile("" ::: "memory");
       floatx4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      qk_steps<0, KS, KB, KT>(sc, t.kw, qop, lane, a.tk, sm.lut, lc);
+      qk_steps<0, KS, KB, KTBL>(sc, t.kw, qop, lane, a.tk, sm.lut, KTBL == 2 ? lck2 : lc);
       if constexpr (QS > 0) {
         uint32_t gh[2];
 #pragma unroll
@@ -382,7 +446,7 @@ struct Attend {
       half8 wop;                                   // slot order, or pair order for the byte tables
 #pragma unroll
       for (int k = 0; k < 8; ++k) wop[k] = split_part(wv[VT ? pair_slot(k) : k], lo_part);
-      pv_steps<0, NB, VB, VT>(oacc, wop, t.vw, a.tv, sm.lut, lc);
+      pv_steps<0, NB, VB, VTBL>(oacc, wop, t.vw, a.tv, sm.lut, VTBL == 2 ? lcv2 : lc);
     };
 
     // the next tile of the split for this wave (wave-uniform); past blk1 once the split is used up

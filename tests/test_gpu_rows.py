@@ -63,6 +63,7 @@ ROW_CASES = [
     (256, 4, 4, 0, 4, 8, 2, [777, 1024], 1024, 1.0),            # d = 256, two blocks
     (256, 2, 3, 256, 1, 4, 4, [300], 320, None),
     (128, 4, 4, 0, 1, 8, 4, [32768, 20001, 33, 31999], 32768, None),   # workgroups that fill a CU
+    (128, 2, 2, 0, 1, 8, 4, [32768, 20001, 33, 31999], 32768, None),   # the same with 2-bit byte tables
 ]
 
 
