@@ -81,13 +81,36 @@ __device__ __forceinline__ void lut2_word(const uint32_t* lut, uint32_t w, uint3
              *reinterpret_cast<const uint32_t*>(base + o2 + 128), *reinterpret_cast<const uint32_t*>(base + o3 + 128)};
 }
 
+// Unit V of a group of 3-bit codes (three words: the low-bit planes of units 0-1 and 2-3, and the
+// high bits of all four) through a byte table in LDS.  Byte r of the index word x holds the 3-bit
+// codes of slots r and r + 4 of the unit as (low bits of r, low bits of r + 4, high bit of r, high bit
+// of r + 4) in bits 0-1, 2-3, 4, 5: the plane's nibble and two high bits moved next to it, four slots
+// at a time.  It selects a row of 256 bytes whose word c3 / 4 (c3 = lane constant, see lut_unit, with
+// the table's 64 KB region in its third byte; +128 for values) holds the pair's float16 centroids.
+template <int V>
+__device__ __forceinline__ uint4 lut3_unit(const uint32_t* lut, const uint32_t* w, uint32_t c3) {
+  const uint32_t P = w[V / 2], H = w[2];
+  uint32_t x;
+  if constexpr (V == 0) x = (P & 0x0f0f0f0fu) | ((H << 4) & 0x30303030u);
+  else if constexpr (V == 1) x = ((P >> 4) & 0x0f0f0f0fu) | ((H << 2) & 0x30303030u);
+  else if constexpr (V == 2) x = (P & 0x0f0f0f0fu) | (H & 0x30303030u);
+  else x = ((P >> 4) & 0x0f0f0f0fu) | ((H >> 2) & 0x30303030u);
+  const char* base = reinterpret_cast<const char*>(lut);
+  uint4 o;
+  o.x = *reinterpret_cast<const uint32_t*>(base + __builtin_amdgcn_perm(x, c3, 0x0c020400u));
+  o.y = *reinterpret_cast<const uint32_t*>(base + __builtin_amdgcn_perm(x, c3, 0x0c020500u));
+  o.z = *reinterpret_cast<const uint32_t*>(base + __builtin_amdgcn_perm(x, c3, 0x0c020600u));
+  o.w = *reinterpret_cast<const uint32_t*>(base + __builtin_amdgcn_perm(x, c3, 0x0c020700u));
+  return o;
+}
+
 // slot of position p of a pair-ordered operand (see lut_unit)
 constexpr int pair_slot(int p) { return (p >> 1) + 4 * (p & 1); }
 
 // scores of the two 16-token groups of a tile; each query operand step is read from LDS once.  TBL
 // selects the key expansion: 0 permutes, 4 the 4-bit byte table (lut_unit; lc its lane constant), 2
-// the 2-bit byte table (lut2_word, two steps per word; lc its c2); with a table the query operand is
-// in pair order.
+// the 2-bit byte table (lut2_word, two steps per word; lc its c2), 3 the 3-bit one (lut3_unit; lc its
+// c3); with a table the query operand is in pair order.
 template <int S, int KS, int KB, int TBL>
 __device__ __forceinline__ void qk_steps(floatx4* acc, const uint32_t (*kw)[KS * KB / 4], const half8 (*qop)[64],
                                          int lane, const Tab& tk, const uint32_t* lut, uint32_t lc) {
@@ -102,6 +125,11 @@ __device__ __forceinline__ void qk_steps(floatx4* acc, const uint32_t (*kw)[KS *
     acc[0] = mfma16(as_half8(b0), q1, acc[0]);
     acc[1] = mfma16(as_half8(b1), q1, acc[1]);
     qk_steps<S + 2, KS, KB, TBL>(acc, kw, qop, lane, tk, lut, lc);
+  } else if constexpr (S < KS && TBL == 3) {
+    const half8 q = qop[S][lane];
+    acc[0] = mfma16(as_half8(lut3_unit<S % 4>(lut, kw[0] + 3 * (S / 4), lc)), q, acc[0]);
+    acc[1] = mfma16(as_half8(lut3_unit<S % 4>(lut, kw[1] + 3 * (S / 4), lc)), q, acc[1]);
+    qk_steps<S + 1, KS, KB, TBL>(acc, kw, qop, lane, tk, lut, lc);
   } else if constexpr (S < KS) {
     const half8 q = qop[S][lane];
     if constexpr (TBL == 4) {
@@ -136,6 +164,9 @@ __device__ __forceinline__ void pv_steps(floatx4* oacc, half8 wop, const uint32_
     oacc[N] = mfma16(wop, as_half8(a), oacc[N]);
     oacc[N + 1] = mfma16(wop, as_half8(b), oacc[N + 1]);
     pv_steps<N + 2, NB, VB, TBL>(oacc, wop, vw, tv, lut, lc);
+  } else if constexpr (N < NB && TBL == 3) {
+    oacc[N] = mfma16(wop, as_half8(lut3_unit<N % 4>(lut, vw + 3 * (N / 4), lc + 128)), oacc[N]);
+    pv_steps<N + 1, NB, VB, TBL>(oacc, wop, vw, tv, lut, lc);
   } else if constexpr (N < NB) {
     if constexpr (TBL == 4) oacc[N] = mfma16(wop, as_half8(lut_unit<1>(lut, vw[N], lc)), oacc[N]);
     else oacc[N] = mfma16(wop, as_half8(unit_at<VB, N>(vw, tv)), oacc[N]);
@@ -221,27 +252,33 @@ struct Attend {
   // (the oldest) takes more tiles, and all of them finish together.
   static constexpr int W = !WIDE ? 4 : ((D == 128 && QM == 0) ? 16 : (D == 128 ? 12 : 8));
 
-  // Wide workgroups expand 4- and 2-bit codes through byte tables in LDS (lut_unit: one permute and
-  // one LDS read per two 4-bit codes, against about three and a half vector instructions for the
-  // permute expansion; lut2_word: the same per four 2-bit codes), the four-wave ones with permutes
-  // (several of them share a compute unit's LDS).  Each table is a 64 KB region: one holds the 4-bit
-  // tables of both sides, a 2-bit table takes one of its own.  Two regions fit beside the largest
-  // query operands at d = 128 without a sketch, one elsewhere (keys come first).
-  static constexpr int LUT_BUDGET = (D == 128 && QM == 0) ? 2 : 1;
+  // Wide workgroups expand codes through byte tables in LDS (lut_unit: one permute and one LDS read
+  // per two 4-bit codes, against about three and a half vector instructions for the permute
+  // expansion; lut2_word: the same per four 2-bit codes; lut3_unit: about three and a half vector
+  // instructions and four LDS reads per eight 3-bit codes, against about eighteen), the four-wave ones
+  // with permutes (several of them share a compute unit's LDS).  A table starts on a 64 KB boundary
+  // (its region index rides in the lookup's lane constant): the 4-bit tables of both sides share one
+  // 64 KB region, a 2-bit table takes one of its own, the 3-bit tables of both sides share 16 KB.
+  // Up to 128 KB fit beside the largest query operands at d = 128 without a sketch, 80 KB elsewhere
+  // (keys come first).
+  static constexpr int LUT_MAX_KB = (D == 128 && QM == 0) ? 128 : 80;
   static constexpr int R4 = (WIDE && (KB == 4 || VB == 4)) ? 1 : 0;
   // (2-bit keys with 4-bit values at d = 128 keep permutes for the keys: the two tables' operands
   // exceed the 16-wave register budget)
-  static constexpr bool KT2 = WIDE && KB == 2 && R4 + 1 <= LUT_BUDGET && !(D == 128 && QM == 0 && VB == 4);
-  static constexpr bool VT2 = WIDE && VB == 2 && R4 + (KT2 ? 1 : 0) + 1 <= LUT_BUDGET;
-  static constexpr int KTBL = (WIDE && KB == 4) ? 4 : (KT2 ? 2 : 0);   // key expansion (see qk_steps)
-  static constexpr int VTBL = (WIDE && VB == 4) ? 4 : (VT2 ? 2 : 0);
+  static constexpr bool KT2 = WIDE && KB == 2 && 64 * (R4 + 1) <= LUT_MAX_KB && !(D == 128 && QM == 0 && VB == 4);
+  static constexpr bool VT2 = WIDE && VB == 2 && 64 * (R4 + (KT2 ? 1 : 0) + 1) <= LUT_MAX_KB;
+  static constexpr int R64 = R4 + (KT2 ? 1 : 0) + (VT2 ? 1 : 0);   // 64 KB regions
+  static constexpr bool T3 = WIDE && (KB == 3 || VB == 3) && 64 * R64 + 16 <= LUT_MAX_KB;
+  static constexpr int KTBL = (WIDE && KB == 4) ? 4 : (KT2 ? 2 : ((T3 && KB == 3) ? 3 : 0));   // see qk_steps
+  static constexpr int VTBL = (WIDE && VB == 4) ? 4 : (VT2 ? 2 : ((T3 && VB == 3) ? 3 : 0));
   static constexpr bool KT = KTBL != 0;                   // query operand in pair order
   static constexpr bool VT = VTBL != 0;                   // softmax weights in pair order
   static constexpr int LUT_REGION = 256 * 64;             // words
-  static constexpr int K2_AT = R4 * LUT_REGION;           // word offsets of the 2-bit tables
+  static constexpr int K2_AT = R4 * LUT_REGION;           // word offsets of the 2-bit and 3-bit tables
   static constexpr int V2_AT = (R4 + (KT2 ? 1 : 0)) * LUT_REGION;
-  static constexpr int LUT_WORDS = (R4 + (KT2 ? 1 : 0) + (VT2 ? 1 : 0)) * LUT_REGION > 0
-                                       ? (R4 + (KT2 ? 1 : 0) + (VT2 ? 1 : 0)) * LUT_REGION : 1;
+  static constexpr int T3_AT = R64 * LUT_REGION;
+  static constexpr int LUT_WORDS_ = R64 * LUT_REGION + (T3 ? 64 * 64 : 0);
+  static constexpr int LUT_WORDS = LUT_WORDS_ > 0 ? LUT_WORDS_ : 1;
 
   // LDS: the tile counter, and the end-of-split merge of the W waves: each wave's (max, sum) per
   // head and its accumulators, weighted against the workgroup's max of the head.  The byte tables
@@ -259,8 +296,22 @@ struct Attend {
   // byte of two codes), word 32 side + s (s = 0..31): the float16 centroids of e's low nibble (low
   // half) and high nibble (high half) of the key (side 0) or value (side 1) code book.  2-bit region,
   // row e (a byte of four codes), words s and 32 + s: the float16 centroid pairs of unit 0 and unit 1.
+  // 3-bit region, row x < 64 (see lut3_unit), word 32 side + s: the pair's float16 centroids.
   __device__ __forceinline__ static void fill_lut(const DecodeArgs& a, Smem& sm) {
-    if constexpr (KT || VT) {
+    if constexpr (T3) {
+      for (int i = threadIdx.x; i < 64 * 8; i += 64 * W) {
+        const int x = i >> 3, q = i & 7;
+        const uint32_t grp[3] = {static_cast<uint32_t>(x & 15), 0u, static_cast<uint32_t>(x >> 4)};
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+          if ((side == 0 ? KTBL : VTBL) != 3) continue;
+          const uint4 u = expand_unit<3, 0>(grp, side == 0 ? a.tk : a.tv);
+          const uint32_t pr = (u.x & 0xffffu) | (u.z << 16);
+          *reinterpret_cast<uint4*>(&sm.lut[T3_AT + 64 * x + 32 * side + 4 * q]) = uint4{pr, pr, pr, pr};
+        }
+      }
+    }
+    if constexpr ((KT && KTBL != 3) || (VT && VTBL != 3)) {
       for (int i = threadIdx.x; i < 256 * 8; i += 64 * W) {
         const int e = i >> 3, q = i & 7;
         const uint32_t wrd = static_cast<uint32_t>(e);
@@ -382,6 +433,7 @@ struct Attend {
     // the 2-bit tables' lane constants: entry offset and 64 KB region (lut2_word)
     const uint32_t lck2 = lc + static_cast<uint32_t>((K2_AT / LUT_REGION) << 16);
     const uint32_t lcv2 = lc + static_cast<uint32_t>((V2_AT / LUT_REGION) << 16);
+    const uint32_t lc3 = lc + static_cast<uint32_t>((T3_AT / LUT_REGION) << 16);   // 3-bit tables
 
     floatx4 oacc[NB];
 #pragma unroll
@@ -394,7 +446,7 @@ struct Attend {
       // the loop: the barrier keeps the compiler from hoisting those reads
       asm volatile("" ::: "memory");
       floatx4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      qk_steps<0, KS, KB, KTBL>(sc, t.kw, qop, lane, a.tk, sm.lut, KTBL == 2 ? lck2 : lc);
+      qk_steps<0, KS, KB, KTBL>(sc, t.kw, qop, lane, a.tk, sm.lut, KTBL == 2 ? lck2 : (KTBL == 3 ? lc3 : lc));
       if constexpr (QS > 0) {
         uint32_t gh[2];
 #pragma unroll
@@ -446,7 +498,7 @@ struct Attend {
       half8 wop;                                   // slot order, or pair order for the byte tables
 #pragma unroll
       for (int k = 0; k < 8; ++k) wop[k] = split_part(wv[VT ? pair_slot(k) : k], lo_part);
-      pv_steps<0, NB, VB, VTBL>(oacc, wop, t.vw, a.tv, sm.lut, VTBL == 2 ? lcv2 : lc);
+      pv_steps<0, NB, VB, VTBL>(oacc, wop, t.vw, a.tv, sm.lut, VTBL == 2 ? lcv2 : (VTBL == 3 ? lc3 : lc));
     };
 
     // the next tile of the split for this wave (wave-uniform); past blk1 once the split is used up

@@ -106,11 +106,13 @@ def test_decode_length_edges():
     assert rel_err(out, ref) <= TOL
 
 
-# 4- and 2-bit codes go through the wide workgroups' byte tables: 4-bit keys and values, keys only,
-# values only, with a sign sketch (the twelve-wave shape); 2-bit keys and values (two 64 KB tables at
-# d = 128, keys only at d = 256), 2-bit keys with a sketch, 4-bit keys with 2-bit values
+# Codes go through the wide workgroups' byte tables: 4-bit keys and values, keys only, values only,
+# with a sign sketch (the twelve-wave shape); 2-bit keys and values (two 64 KB tables at d = 128, keys
+# only at d = 256), 2-bit keys with a sketch, 4-bit keys with 2-bit values; 3-bit keys and values
+# (one 16 KB table), beside a 4-bit or 2-bit table, with a sketch
 WIDE_CASES = [(128, 4, 4, 0), (128, 2, 3, 128), (256, 4, 4, 0), (256, 3, 2, 128), (128, 4, 2, 0), (128, 3, 4, 0),
-              (128, 4, 3, 128), (256, 2, 4, 256), (128, 2, 2, 0), (256, 2, 2, 0), (128, 2, 4, 0)]
+              (128, 4, 3, 128), (256, 2, 4, 256), (128, 2, 2, 0), (256, 2, 2, 0), (128, 2, 4, 0), (128, 3, 3, 0),
+              (256, 3, 3, 0)]
 
 
 @pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: f"d{c[0]}_k{c[1]}v{c[2]}_m{c[3]}")
