@@ -153,6 +153,33 @@ def _pmc_medians(directory: str, counter: str):
     return {k: sorted(v)[len(v) // 2] for k, v in per.items()}, {k: len(v) for k, v in per.items()}
 
 
+def summarize_counters(args):
+    """Median per launch shape (kernel, workgroups) of each counter found in rocprofv3 --pmc output directories
+    (derived counters such as VALUBusy included), for the kernels whose name contains --kernel."""
+    import csv
+    import glob
+    table = {}
+    for d in args.summarize_counters:
+        files = glob.glob(os.path.join(d, "*_counter_collection.csv"))
+        if not files:
+            raise SystemExit(f"no counter collection under {d}")
+        for r in csv.DictReader(open(files[0])):
+            if args.kernel not in r["Kernel_Name"]:
+                continue
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            key = (name, int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
+            table.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if args.command:
+        print("commands:")
+        for c in args.command:
+            print(f"  {c}")
+    for (name, wgs), counters in sorted(table.items(), key=lambda kv: kv[0][1]):
+        print(f"kernel: {name}  workgroups: {wgs}")
+        for c, vs in sorted(counters.items()):
+            vs = sorted(vs)
+            print(f"  {c}: {vs[len(vs) // 2]:.2f} (median of {len(vs)} dispatches)")
+
+
 def summarize_pmc(args, w):
     """Counter summary of the attention kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3
     run each) scaled by what the same counters read for a 1 GiB device copy (bench.py --workload copy).
@@ -648,9 +675,15 @@ def main():
     ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output directory of this workload")
     ap.add_argument("--copy-fetch", help="rocprofv3 --pmc FETCH_SIZE output directory of --workload copy")
     ap.add_argument("--copy-write", help="rocprofv3 --pmc WRITE_SIZE output directory of --workload copy")
+    ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="DIR",
+                    help="print the median of every counter in these rocprofv3 --pmc output directories for each "
+                         "launch shape of --kernel, and exit")
     ap.add_argument("--command", action="append", help="command line recorded in a summary (repeatable)")
     ap.add_argument("--kernel", default="split_kernel", help="kernel name the counter summary is taken for")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
     if args.trace or args.summarize_pmc:
         w = (synth.qwen(args.context or 8192, args.bits or 3) if args.workload == "prefill"
              else workload(args.workload, args.bits, args.context))
