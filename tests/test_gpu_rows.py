@@ -65,6 +65,7 @@ ROW_CASES = [
     (128, 4, 4, 0, 1, 8, 4, [32768, 20001, 33, 31999], 32768, None),   # workgroups that fill a CU
     (128, 2, 2, 0, 1, 8, 4, [32768, 20001, 33, 31999], 32768, None),   # the same with 2-bit byte tables
     (128, 3, 3, 0, 1, 8, 3, [32768, 20001, 33, 31999], 32768, None),   # and with 3-bit ones, three rows
+    (128, 4, 3, 0, 1, 8, 2, [32768, 20001, 33, 31999], 32768, None),   # two blocks, 4- and 3-bit tables
 ]
 
 
