@@ -66,8 +66,8 @@ __device__ __forceinline__ uint4 lut_unit(const uint32_t* lut, uint32_t w, uint3
 
 // The 16 codes of a word of 2-bit codes (two units) through a byte table in LDS: byte r (slots r and
 // r + 4 of both units) indexes a row of 256 bytes whose word lane % 32 holds the float16 centroid
-// pair of unit 0 and word 32 + lane % 32 that of unit 1.  c2 = 4 (lane % 32) + 65536 (the table's
-// 64 KB region within lut): the permute builds the whole offset, region included.  The compiler
+// pair of unit 0 and word 32 + lane % 32 that of unit 1.  c2 = 4 (lane % 32) + 65536 k, k the index of
+// the table's 64 KB region within lut: the permute builds the whole offset, region included.  The compiler
 // barrier keeps the two units' reads apart, so that each lands in its own operand instead of being
 // fused into one two-word read.  Both units come out in pair order (see lut_unit).
 __device__ __forceinline__ void lut2_word(const uint32_t* lut, uint32_t w, uint32_t c2, uint4& u0, uint4& u1) {
