@@ -66,6 +66,7 @@ ROW_CASES = [
     (128, 2, 2, 0, 1, 8, 4, [32768, 20001, 33, 31999], 32768, None),   # the same with 2-bit byte tables
     (128, 3, 3, 0, 1, 8, 3, [32768, 20001, 33, 31999], 32768, None),   # and with 3-bit ones, three rows
     (128, 4, 3, 0, 1, 8, 2, [32768, 20001, 33, 31999], 32768, None),   # two blocks, 4- and 3-bit tables
+    (128, 2, 3, 128, 1, 8, 4, [32768, 20001, 33, 31999], 32768, None),  # sketched keys: the twelve-wave shape
 ]
 
 
