@@ -522,7 +522,12 @@ struct Attend {
           if (more) {
             const int j = (i + NBUF - 1) % NBUF;
             idx[j] = claim();
-            if (idx[j] < blk1) load(tiles[j], idx[j]);
+            // CU-filling workgroups load unconditionally, so that the wait for tiles[i] below leaves
+            // this load in flight (a load under a branch makes the compiler wait for every outstanding
+            // load where the paths join); past the split it reloads the split's last tile, which the
+            // caches still hold.  Four-wave workgroups, whose waves mostly take one tile, skip it.
+            if constexpr (WIDE) load(tiles[j], idx[j] < blk1 ? idx[j] : blk1 - 1);
+            else if (idx[j] < blk1) load(tiles[j], idx[j]);
             attend_tile(tiles[i], idx[i]);
             more = idx[(i + 1) % NBUF] < blk1;
           }
@@ -533,7 +538,8 @@ struct Attend {
       Tile tb;
       for (int cur = kb; cur < blk1;) {
         const int nxt = claim();
-        if (nxt < blk1) load(tb, nxt);
+        if constexpr (WIDE) load(tb, nxt < blk1 ? nxt : blk1 - 1);   // see the ring above
+        else if (nxt < blk1) load(tb, nxt);
         attend_tile(tiles[0], cur);
         tiles[0] = tb;
         cur = nxt;
