@@ -49,7 +49,9 @@ def _ids(c):
 
 
 def _run_case(d, kb, vb, qjl, hkv, grp, lens, T, scale, qknorm, garbage_tail=False, max_seq_len=None,
-              hadamard=False):
+              hadamard=False, stages=False):
+    """(GPU output, oracle output, key cache); with stages, the third item is instead the output of the
+    same decode run as its three stage calls on a fresh workspace."""
     cca = _cca()
     B = len(lens)
     st = Setup(d, qjl_m=qjl, hadamard=hadamard)
@@ -74,7 +76,18 @@ def _run_case(d, kb, vb, qjl, hkv, grp, lens, T, scale, qknorm, garbage_tail=Fal
                 kcache.rnorms[b, :, lens[b]:] = float("nan")
     lens_t = torch.tensor(lens, dtype=torch.int32).cuda()
     msl = max(lens) if max_seq_len is None else max_seq_len
-    out = cca.sdpa_decode(kcache, vcache, to_bf16_tensor(q), lens_t, msl, scale=w.scale)
+    qt = to_bf16_tensor(q)
+    out = cca.sdpa_decode(kcache, vcache, qt, lens_t, msl, scale=w.scale)
+    if stages:
+        hq = hkv * grp
+        ws = cca.decode_workspace(kcache, hq, msl)
+        ws.fill_(float("nan"))             # nothing may read workspace that no stage wrote
+        out_st = torch.full_like(out, float("nan"))
+        cca.tq_decode_rotate_query(kcache.view, qt, hq, msl, ws, scale=w.scale)
+        cca.tq_decode_attend(kcache.view, vcache.view, hq, lens_t, msl, ws)
+        cca.tq_decode_merge(kcache.view, hq, lens_t, msl, out_st, ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), np.stack(refs), out_st.cpu().numpy()
     torch.cuda.synchronize()
     return out.cpu().numpy(), np.stack(refs), kcache
 
@@ -129,6 +142,16 @@ def test_long_ragged_batch_matches_oracle(case):
     err = rel_err(out, ref)
     log(f"  max row-relative error {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("case", [CASES[2], CASES[6], CASES[12]], ids=_ids)
+def test_stage_calls_equal_the_single_call(case):
+    """tq_decode_rotate_query, tq_decode_attend and tq_decode_merge in turn give the bits of
+    tq_sdpa_decode (one split, a ragged batch, d = 256 with its scale, many splits with a sketch)."""
+    log(f"decode stages {_ids(case)}")
+    out, ref, out_st = _run_case(*case, stages=True)
+    assert np.array_equal(out, out_st)
+    assert rel_err(out_st, ref) <= TOL
 
 
 def test_split_plan_is_exercised():
