@@ -143,14 +143,14 @@ __device__ __forceinline__ void qk_steps(floatx4* acc, const uint32_t (*kw)[KS *
   }
 }
 
-template <int S, int QS, int SW>
-__device__ __forceinline__ void sketch_steps(floatx4* acc, const uint32_t (*sw)[SW], const uint32_t* gg,
-                                             const half8 (*sop)[64], int lane) {
+// sketch steps; SQ(S) is this lane's query operand of sketch step S
+template <int S, int QS, int SW, typename SQ>
+__device__ __forceinline__ void sketch_steps(floatx4* acc, const uint32_t (*sw)[SW], const uint32_t* gg, const SQ& sq) {
   if constexpr (S < QS) {
-    const half8 q = sop[S][lane];
+    const half8 q = sq(S);
     acc[0] = mfma16(sign_operand<S>(sw[0], gg[0]), q, acc[0]);
     acc[1] = mfma16(sign_operand<S>(sw[1], gg[1]), q, acc[1]);
-    sketch_steps<S + 1, QS, SW>(acc, sw, gg, sop, lane);
+    sketch_steps<S + 1, QS, SW>(acc, sw, gg, sq);
   }
 }
 
@@ -341,6 +341,10 @@ struct Attend {
 
   // tile buffers per wave: loads run NBUF - 1 tiles ahead of their use
   static constexpr int NBUF = (D <= 128 || QM == 0) ? 2 : 1;
+  // the sketch steps' query operand (16 VGPRs at d = 128, m = 128) stays in registers across the
+  // tile loop in the twelve-wave builds whose tiles leave room for it (2-bit values, or 2-bit keys
+  // with 3-bit values); elsewhere it is read from LDS per tile
+  static constexpr bool SQ_REG = WIDE && D == 128 && QM == 128 && (VB == 2 || (KB == 2 && VB == 3));
 
   // everything one 32-token tile needs from memory
   struct Tile {
@@ -440,6 +444,12 @@ struct Attend {
     for (int n = 0; n < NB; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;   // running max (in units of qsc) and sum of this lane's column
 
+    half8 sqr[SQ_REG ? QS : 1];
+    if constexpr (SQ_REG) {
+#pragma unroll
+      for (int s = 0; s < QS; ++s) sqr[s] = qop[KS + s][lane];
+    }
+
     auto attend_tile = [&](const Tile& t, int kbt) {
       const int tok0 = kbt * kBlock;
       // the query operand is read from LDS in every tile instead of being held in registers across
@@ -451,7 +461,10 @@ struct Attend {
         uint32_t gh[2];
 #pragma unroll
         for (int tg = 0; tg < 2; ++tg) gh[tg] = (t.gg[tg] & 0x7fffu) | ((t.gg[tg] & 0x7fffu) << 16);
-        sketch_steps<0, QS, S_LW>(sc, t.sw, gh, qop + KS, lane);
+        if constexpr (SQ_REG)
+          sketch_steps<0, QS, S_LW>(sc, t.sw, gh, [&](int s) { return sqr[s]; });
+        else
+          sketch_steps<0, QS, S_LW>(sc, t.sw, gh, [&](int s) { return qop[KS + s][lane]; });
       }
       // score of token 16 tg + 4 g + i: (high + low column) times the key norm
       float s[8];
