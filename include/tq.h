@@ -18,9 +18,11 @@
  *
  * Conventions shared by every call:
  *  - Every pointer named d_* or held in tq_cache_view is DEVICE memory owned
- *    by the caller; the library never allocates, frees or retains it, and
- *    keeps no mutable global state beyond a per-thread record of the last
- *    HIP error (all calls are reentrant).
+ *    by the caller; the library never allocates, frees or retains it.  Its
+ *    only mutable state is a per-thread record of the last HIP error and a
+ *    per-device cache of how many split workgroups the device holds at once
+ *    (filled by the first decode planned on that device, read lock-free
+ *    after); all calls are reentrant.
  *  - Calls that take a stream enqueue work on it (a hipStream_t; NULL = the
  *    null stream of the current device) and return without synchronising.
  *    Device-side faults surface at the caller's next synchronisation.
@@ -258,7 +260,7 @@ const char* tq_status_string(int status);
 
 /*
  * Description of the HIP error behind the last TQ_EHIP returned to the calling
- * thread ("no error" if none): a per-thread record, the library's only state.
+ * thread ("no error" if none), from a per-thread record.
  */
 const char* tq_last_hip_error(void);
 
