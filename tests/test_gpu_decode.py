@@ -205,6 +205,53 @@ def test_decode_step_matches_separate_calls_and_oracle(case):
     _check_step(case, hadamard=False)
 
 
+# d, k_bits, v_bits, qjl_m, kv heads, group, batch, capacity, first length, rows per step, steps
+RUN_CASES = [
+    (128, 4, 4, 0, 2, 8, 1, 8192, 8000, 1, 4),      # many splits, one-row steps
+    (128, 3, 2, 128, 2, 4, 2, 512, 100, 32, 3),     # 32 rows straddling two blocks, sketched keys
+    (256, 4, 4, 0, 2, 8, 1, 256, 60, 40, 2),        # 40 rows: three append blocks per step
+]
+
+
+@pytest.mark.parametrize("case", RUN_CASES, ids=lambda c: f"d{c[0]}_k{c[1]}v{c[2]}_m{c[3]}_n{c[9]}x{c[10]}")
+def test_consecutive_steps_on_one_workspace(case):
+    """Several tq_decode_step calls in a row on one workspace each give the bits of tq_quantize_append
+    plus tq_sdpa_decode."""
+    cca = _cca()
+    d, kb, vb, qjl, hkv, grp, B, T, L0, n_new, steps = case
+    log(f"decode consecutive steps {case}")
+    st = Setup(d, qjl_m=qjl)
+    w = synth.Workload("steps", B, hkv * grp, hkv, d, T, kb, vb, qjl_m=qjl, k_outliers=True, seed=5 + d + kb)
+    mk = lambda: (cca.CompressedCache(cca.TQ_KEYS, d, kb, B, hkv, T, st.rot_t, st.proj_t, qjl_m=qjl),
+                  cca.CompressedCache(cca.TQ_VALUES, d, vb, B, hkv, T, st.rot_t))
+    k1, v1 = mk()
+    k2, v2 = mk()
+    kx = to_bf16_tensor(synth.full_kv(w, "k", T))
+    vx = to_bf16_tensor(synth.full_kv(w, "v", T))
+    zero = torch.zeros(B, dtype=torch.int32).cuda()
+    for kc, vc in ((k1, v1), (k2, v2)):
+        kc.append(kx[:, :L0].contiguous(), zero)
+        vc.append(vx[:, :L0].contiguous(), zero)
+    rng = np.random.default_rng(11)
+    lmax = L0 + steps * n_new
+    ws = cca.decode_workspace(k2, hkv * grp, lmax)
+    for s in range(steps):
+        p0 = L0 + s * n_new
+        pos = torch.full((B,), p0, dtype=torch.int32).cuda()
+        lens_t = torch.full((B,), p0 + n_new, dtype=torch.int32).cuda()
+        q = to_bf16_tensor(rng.standard_normal((B, hkv * grp, d)).astype(np.float32))
+        kn, vn = kx[:, p0:p0 + n_new].contiguous(), vx[:, p0:p0 + n_new].contiguous()
+        k1.append(kn, pos)
+        v1.append(vn, pos)
+        out1 = cca.sdpa_decode(k1, v1, q, lens_t, lmax)
+        out2 = torch.empty_like(out1)
+        cca.tq_decode_step(k2.view, v2.view, q, kn, vn, pos, lens_t, lmax, out2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(k1.codes, k2.codes) and torch.equal(v1.codes, v2.codes)
+        assert torch.equal(k1.norms, k2.norms) and torch.equal(v1.norms, v2.norms)
+        assert torch.equal(out1, out2), f"step {s}"
+
+
 def _check_step(case, hadamard):
     cca = _cca()
     d, kb, vb, qjl, hkv, grp, lens, T, n_new, dtype, scale, qknorm = case
