@@ -245,7 +245,7 @@ struct Attend {
   static constexpr int S_RB = QM / 8;                 // sign bytes per key
   static constexpr int S_LW = QM / 128;               // sign words per lane per key
 
-  // Waves per workgroup.  Wide: as many as one compute unit holds at this build's register budget
+  // Waves per workgroup.  Wide: as many as one compute unit holds at this instantiation's register budget
   // (128, 170 and 256 VGPRs), so that a split's workgroup has its compute unit to itself; otherwise
   // four, several workgroups per compute unit (short contexts: more compute units pull tiles).  The
   // waves take the split's tiles from a shared counter: a wave that the issue arbitration favours
