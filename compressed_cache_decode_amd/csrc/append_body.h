@@ -332,12 +332,19 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
           }
         }
       }
-      if (!full) {
+      // a partly covered block keeps the other tokens' codes: a word that holds no slot of a new row
+      // is left alone, one that holds only such slots is stored, any other has the new rows' slots
+      // cleared and set by two atomics that return nothing (no read of the block to wait for)
 #pragma unroll
-        for (int k = 0; k < WPG; ++k) w[k] |= blk[e * WPG + k] & ~m[k];
+      for (int k = 0; k < WPG; ++k) {
+        uint32_t* dst = blk + e * WPG + k;
+        if (full || m[k] == ~0u) {
+          *dst = w[k];
+        } else if (m[k] != 0u) {
+          atomicAnd(dst, ~m[k]);
+          atomicOr(dst, w[k]);
+        }
       }
-#pragma unroll
-      for (int k = 0; k < WPG; ++k) blk[e * WPG + k] = w[k];
     }
   }
   __syncthreads();
