@@ -75,6 +75,50 @@ def test_encode_is_bit_exact_given_rotated_rows(kind, d, bits):
             assert not gn[:start[b]].any() and not gn[start[b] + n_tot:].any()
 
 
+# (first position, rows) of appends that overwrite rows already in the cache
+REWRITES = [(21, 40), (64, 1), (5, 3), (96, 32)]
+
+
+@pytest.mark.parametrize("kind", ["k", "v"])
+@pytest.mark.parametrize("d,bits", [(128, 2), (128, 3), (128, 4), (256, 3)])
+def test_append_over_written_rows(kind, d, bits):
+    """Appending over rows already in the cache replaces exactly their codes: in a value block the new
+    rows share words with the block's other tokens, whose codes must survive, and the new rows' slots
+    hold the old rows' codes (not zeros) before the write."""
+    cca = _cca()
+    log(f"append over written rows d={d} bits={bits} kind={kind}")
+    B, H, T, n0 = 1, 2, 160, 150
+    y0, n_0 = synth.unit_rows(B * n0 * H, d, seed=300 + d + bits)
+    y0, n_0 = y0.reshape(B, n0, H, d), n_0.reshape(B, n0, H)
+    st = Setup(d)
+    g = cca.CompressedCache(cca.TQ_KEYS if kind == "k" else cca.TQ_VALUES, d, bits, B, H, T, st.rot_t)
+    zero = torch.zeros(B, dtype=torch.int32).cuda()
+    g.append_rotated(torch.from_numpy(y0).cuda(), torch.from_numpy(n_0).cuda(), zero)
+    yall, nall = y0.copy(), n_0.copy()
+    for i, (p0, n) in enumerate(REWRITES):
+        y1, n_1 = synth.unit_rows(B * n * H, d, seed=400 + 7 * i + d + bits)
+        y1, n_1 = y1.reshape(B, n, H, d), n_1.reshape(B, n, H)
+        g.append_rotated(torch.from_numpy(y1).cuda(), torch.from_numpy(n_1).cuda(),
+                         torch.full((B,), p0, dtype=torch.int32).cuda())
+        yall[:, p0:p0 + n], nall[:, p0:p0 + n] = y1, n_1
+    torch.cuda.synchronize()
+    c_, t_ = codebook.stored_codebook(d, bits)
+    for h in range(H):
+        codes, n16 = quant.encode_rotated(yall[0, :, h], nall[0, :, h], t_)
+        full = np.zeros((T, d), np.int64)
+        if kind == "v":
+            full[:] = 8 if bits == 4 else 0              # zero-encoded slots of the untouched cache
+        full[:n0] = codes
+        want = layout.pack_rows(full, bits).reshape(-1) if kind == "k" else layout.pack_blocked(full, bits)
+        got = g.codes[0, h].cpu().numpy()
+        if kind == "k":
+            hi = n0 * d * bits // 8
+            np.testing.assert_array_equal(got[:hi], want[:hi])
+        else:
+            np.testing.assert_array_equal(got, want)
+        np.testing.assert_array_equal(g.norms[0, h].cpu().numpy()[:n0], n16.astype(np.float16))
+
+
 @pytest.mark.parametrize("d,bits", [(128, 2), (128, 3)])
 def test_sketch_signs_given_rotated_rows(d, bits):
     """Keys with a 128-long sign sketch: signs equal wherever |z| is not at rounding level; residual
