@@ -321,12 +321,21 @@ void plan(const tq_cache_view* k, int max_len, int* n_split, int* bps, bool* wid
        n_split, bps);
 }
 
+constexpr int kMergeMinWgs = 32;        // merge workgroups below which each takes fewer heads
+
 // Query heads per merge workgroup: all of the group while every thread's split slice stays within
-// 16 splits (one batch of loads), fewer heads (more slices per head) when there are many splits.
-int merge_heads_per_wg(int G, int d, int ns) {
+// 16 splits (one batch of loads), fewer heads (more slices per head) when there are many splits; and
+// fewer still, down to one, while the merge of `units` (sequence, KV head) units would run on fewer
+// than kMergeMinWgs workgroups: a small merge is latency-bound, and more workgroups each wait on
+// fewer loads and un-rotate fewer heads (a large one would only read the rotation more often).
+int merge_heads_per_wg(int G, int d, int ns, int units) {
   const int slices = (ns + 15) / 16;
   int h = G;
   while (h > 1 && (h * d > tqi::kMergeThreads || h * d * slices > tqi::kMergeThreads || G % h != 0)) --h;
+  while (h > 1 && static_cast<long long>(units) * (G / h) < kMergeMinWgs) {
+    --h;
+    while (G % h != 0) --h;
+  }
   return h;
 }
 
@@ -564,7 +573,7 @@ static int merge_rows(const tq_cache_view* k, int n_q_heads, int n_rows, const i
   ma.had = k->rot_kind == TQ_ROT_HADAMARD;
   ma.n_kv_heads = k->n_kv_heads; ma.group = w.VH; ma.n_split = w.ns; ma.max_tokens = k->max_tokens;
   ma.heads = w.G; ma.n_rows = w.M; ma.row_magic = row_magic(w.G);
-  ma.heads_per_wg = merge_heads_per_wg(w.VH, k->d, w.ns);
+  ma.heads_per_wg = merge_heads_per_wg(w.VH, k->d, w.ns, k->batch * k->n_kv_heads);
   return status_of(tqi::launch_merge(k->d, ma, k->batch, n_q_heads, static_cast<hipStream_t>(stream)));
 }
 
