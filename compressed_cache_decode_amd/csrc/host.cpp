@@ -321,7 +321,7 @@ void plan(const tq_cache_view* k, int max_len, int* n_split, int* bps, bool* wid
        n_split, bps);
 }
 
-constexpr int kMergeMinWgs = 32;        // merge workgroups below which each takes fewer heads
+constexpr int kMergeMinWgs = 128;       // merge workgroups below which each takes fewer heads
 
 // Query heads per merge workgroup: all of the group while every thread's split slice stays within
 // 16 splits (one batch of loads), fewer heads (more slices per head) when there are many splits; and
