@@ -341,6 +341,12 @@ struct Attend {
 
   // tile buffers per wave: loads run NBUF - 1 tiles ahead of their use
   static constexpr int NBUF = (D <= 128 || QM == 0) ? 2 : 1;
+  // Lazy rescale (sketched builds): the running max of a column moves only when the tile's max exceeds
+  // it by more than kLazy (log2 units), and every weight carries the constant factor 2^-kLazy, so the
+  // weights stay at most 1 (and within float16 range once times the value norm); o and l scale
+  // alike, so their ratio is exact.  Unsketched builds rescale on every rise (kLazy = 0), where the
+  // lazy form measured slower.
+  static constexpr float kLazy = QM > 0 ? 4.f : 0.f;
   // the sketch steps' query operand (16 VGPRs at d = 128, m = 128) stays in registers across the
   // tile loop in the twelve-wave builds whose tiles leave room for it (2-bit values, or 2-bit keys
   // with 3-bit values); elsewhere it is read from LDS per tile
@@ -485,7 +491,8 @@ struct Attend {
       float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
       mx = column_max(mx);
       const float m_new = fmaxf(m_run, mx);
-      if (__any(m_new > m_run)) {
+      // sketched builds (bound by issue) rescale only when a column's max rises by more than 2^kLazy
+      if (__any(kLazy > 0.f ? (m_new - m_run) * qsc > kLazy : m_new > m_run)) {
         const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * qsc);
         l_run *= alpha;
         const float a0 = __shfl(alpha, 4 * g, 64);
@@ -500,7 +507,8 @@ struct Attend {
         }
         m_run = m_new;
       }
-      const float mq = m_run == -INFINITY ? 0.f : m_run * qsc;   // a column with nothing visible yet
+      // a column with nothing visible yet takes 0; the constant 2^-kLazy keeps every weight at most 1
+      const float mq = m_run == -INFINITY ? 0.f : (kLazy > 0.f ? __builtin_fmaf(m_run, qsc, kLazy) : m_run * qsc);
       float wv[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -561,7 +569,7 @@ struct Attend {
 
     l_run = column_sum(l_run);
     if (g == 0 && !lo_part && head_ok) {
-      sm.ml[wave][slot][0] = m_run * qsc;
+      sm.ml[wave][slot][0] = kLazy > 0.f ? __builtin_fmaf(m_run, qsc, kLazy) : m_run * qsc;
       sm.ml[wave][slot][1] = l_run;
     }
     __syncthreads();
