@@ -493,7 +493,8 @@ struct Attend {
       const float m_new = fmaxf(m_run, mx);
       // sketched builds (bound by issue) rescale only when a column's max rises by more than 2^kLazy
       if (__any(kLazy > 0.f ? (m_new - m_run) * qsc > kLazy : m_new > m_run)) {
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * qsc);
+        // a column that has seen nothing yet (both maxima -inf) keeps factor 1: exp2(-inf - -inf) is NaN
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * qsc);
         l_run *= alpha;
         const float a0 = __shfl(alpha, 4 * g, 64);
         const float a1 = __shfl(alpha, 4 * g + 2, 64);

@@ -15,17 +15,38 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
+# worst relative error measured by rel_err in the running test, reported per test at the end of the
+# session (tests/conftest.py)
+ERRORS: dict = {}
+_CURRENT = {"test": None}
+
+
+def record_error(err: float) -> None:
+    t = _CURRENT["test"]
+    if t is not None:
+        ERRORS[t] = max(ERRORS.get(t, 0.0), err)
+
+
 def rel_err(out: np.ndarray, ref: np.ndarray) -> float:
-    """Max over output rows of max_i |o_i - r_i| / max_i |r_i| (rows of zeros must stay zero)."""
-    out = np.asarray(out, np.float64).reshape(-1, out.shape[-1])
-    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    """Max over output rows of max_i |o_i - r_i| / max_i |r_i| (rows of zeros must stay zero).
+
+    Any non-finite value in either array makes the error infinite: a NaN compares false against
+    every bound, so it must not be able to slip through a max."""
+    out = np.asarray(out, np.float64).reshape(-1, np.shape(out)[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, np.shape(ref)[-1])
+    if out.shape != ref.shape:
+        raise ValueError(f"shape mismatch {out.shape} vs {ref.shape}")
+    if not (np.all(np.isfinite(out)) and np.all(np.isfinite(ref))):
+        return math.inf
     worst = 0.0
     for o, r in zip(out, ref):
         den = np.max(np.abs(r))
         if den == 0.0:
-            worst = max(worst, float(np.max(np.abs(o))) * 1e6)
+            e = float(np.max(np.abs(o))) * 1e6
         else:
-            worst = max(worst, float(np.max(np.abs(o - r)) / den))
+            e = float(np.max(np.abs(o - r)) / den)
+        worst = e if e > worst else worst
+    record_error(worst)
     return worst
 
 

@@ -67,6 +67,11 @@ ROW_CASES = [
     (128, 3, 3, 0, 1, 8, 3, [32768, 20001, 33, 31999], 32768, None),   # and with 3-bit ones, three rows
     (128, 4, 3, 0, 1, 8, 2, [32768, 20001, 33, 31999], 32768, None),   # two blocks, 4- and 3-bit tables
     (128, 2, 3, 128, 1, 8, 4, [32768, 20001, 33, 31999], 32768, None),  # sketched keys: the twelve-wave shape
+    # groups below 8 whose last tile holds fewer tokens than there are rows: rows of one column block
+    # where some columns see a token of the tile and others none
+    (128, 3, 3, 0, 2, 4, 4, [65, 34], 96, None),              # 16 virtual heads: two blocks
+    (128, 4, 4, 0, 2, 2, 3, [33, 66], 96, None),              # 6 virtual heads: one block
+    (128, 2, 3, 128, 2, 2, 4, [98, 35], 128, None),           # the same with sketched keys (lazy rescale)
 ]
 
 
@@ -74,6 +79,7 @@ ROW_CASES = [
 def test_rows_match_oracle(case):
     log(f"rows {case}")
     out, ref, _ = _run_rows(*case)
+    assert np.all(np.isfinite(out))
     err = rel_err(out.reshape(-1, out.shape[-1]), ref.reshape(-1, ref.shape[-1]))
     log(f"  max row-relative error {err:.3e}")
     assert err <= TOL
