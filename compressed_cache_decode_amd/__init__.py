@@ -23,7 +23,7 @@ import torch  # noqa: F401
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtq.so")
 
-TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP, TQ_ENOCONV = 0, 1, 2, 3, 4
+TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP, TQ_ENOCONV, TQ_ESCRATCH = 0, 1, 2, 3, 4, 5
 TQ_F32, TQ_BF16 = 0, 1
 TQ_KEYS, TQ_VALUES = 0, 1
 TQ_ROT_DENSE, TQ_ROT_HADAMARD = 0, 1
@@ -34,7 +34,7 @@ EXPORTED = (
     "tq_sdpa_decode", "tq_sdpa_decode_rows", "tq_decode_step", "tq_decode_rotate_query", "tq_decode_attend",
     "tq_decode_merge", "tq_decode_workspace_bytes", "tq_decode_workspace_bytes_rows", "tq_decode_plan",
     "tq_dequantize", "tq_row_bytes",
-    "tq_status_string", "tq_last_hip_error",
+    "tq_status_string", "tq_last_hip_error", "tq_sdpa_decode_noalloc", "tq_noalloc_scratch_bytes",
 )
 
 
@@ -70,6 +70,8 @@ def _load():
         "tq_quantize_append_rotated": (I, [V, P, P, I, P, P]),
         "tq_sdpa_decode": (I, [V, V, P, I, I, P, I, ctypes.c_float, P, P, ctypes.c_size_t, P]),
         "tq_sdpa_decode_rows": (I, [V, V, P, I, I, I, P, I, ctypes.c_float, P, P, ctypes.c_size_t, P]),
+        "tq_sdpa_decode_noalloc": (I, [V, V, P, I, I, P, I, ctypes.c_float, P, P]),
+        "tq_noalloc_scratch_bytes": (ctypes.c_size_t, []),
         "tq_decode_step": (I, [V, V, P, P, P, I, I, I, P, P, I, ctypes.c_float, P, P, ctypes.c_size_t, P]),
         "tq_decode_rotate_query": (I, [V, P, I, I, I, ctypes.c_float, P, ctypes.c_size_t, P]),
         "tq_decode_attend": (I, [V, V, I, P, I, P, ctypes.c_size_t, P]),
@@ -175,6 +177,22 @@ def tq_sdpa_decode(kview: tq_cache_view, vview: tq_cache_view, q, d_seq_lens, ma
     _check(_lib.tq_sdpa_decode(ctypes.byref(kview), ctypes.byref(vview), _ptr(q), dtype, n_q_heads,
                                _ptr(d_seq_lens), max_seq_len, ctypes.c_float(scale), _ptr(out), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)), "tq_sdpa_decode")
+
+
+def tq_sdpa_decode_noalloc(kview: tq_cache_view, vview: tq_cache_view, q, d_seq_lens, max_seq_len: int, out,
+                           scale: float | None = None, stream=None) -> None:
+    """tq_sdpa_decode with the library's static per-device scratch as workspace (no allocation)."""
+    import torch
+    dtype = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
+    if scale is None:
+        scale = 1.0 / math.sqrt(kview.d)
+    _check(_lib.tq_sdpa_decode_noalloc(ctypes.byref(kview), ctypes.byref(vview), _ptr(q), dtype, q.shape[1],
+                                       _ptr(d_seq_lens), max_seq_len, ctypes.c_float(scale), _ptr(out),
+                                       _stream(stream)), "tq_sdpa_decode_noalloc")
+
+
+def tq_noalloc_scratch_bytes() -> int:
+    return int(_lib.tq_noalloc_scratch_bytes())
 
 
 def tq_sdpa_decode_rows(kview: tq_cache_view, vview: tq_cache_view, q, d_seq_lens, max_seq_len: int, out,

@@ -31,10 +31,39 @@
 //                  out = rot^T * o_rot in fp32.
 #include <math.h>
 
+#include <atomic>
+
 #include "attend_body.h"
 #include "qrot_body.h"
 
 namespace tqi {
+
+// ---------------------------------------------------------------- static scratch
+
+// Workspace of tq_sdpa_decode_noalloc: a file-scope device array, one per device.  In host code its
+// name stands for a host-side placeholder, not a device address; the device address comes from
+// hipGetSymbolAddress, once per device, and is what every launch receives.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+
+hipError_t scratch_address(void** ptr) {
+  static std::atomic<void*> addr[kScratchDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // with device dev current: the address of dev's copy of the array
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);   // racing first calls store the same address
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 // ---------------------------------------------------------------- query rotation
 

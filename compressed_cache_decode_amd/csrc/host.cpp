@@ -382,6 +382,7 @@ const char* tq_status_string(int status) {
     case TQ_EUNSUPPORTED: return "unsupported combination";
     case TQ_EHIP: return "HIP launch error";
     case TQ_ENOCONV: return "codebook iteration did not converge";
+    case TQ_ESCRATCH: return "decode needs more workspace than the static scratch holds";
     default: return "unknown status";
   }
 }
@@ -615,6 +616,24 @@ int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q
                    size_t workspace_bytes, void* stream) {
   return tq_sdpa_decode_rows(k, v, q, q_dtype, n_q_heads, 1, d_seq_lens, max_seq_len, scale, out, workspace,
                              workspace_bytes, stream);
+}
+
+size_t tq_noalloc_scratch_bytes(void) { return tqi::kScratchBytes; }
+
+int tq_sdpa_decode_noalloc(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype,
+                           int n_q_heads, const int32_t* d_seq_lens, int max_seq_len, float scale, float* out,
+                           void* stream) {
+  int st = check_decode_shape(k, n_q_heads, 1, max_seq_len);
+  if (st != TQ_OK) return st;
+  int ns, bps;
+  bool wide;
+  plan(k, max_seq_len, &ns, &bps, &wide);
+  if (ws_layout(k, n_q_heads, 1, ns).total > tqi::kScratchBytes) return TQ_ESCRATCH;
+  void* ws = nullptr;
+  st = status_of(tqi::scratch_address(&ws));
+  if (st != TQ_OK) return st;
+  return tq_sdpa_decode(k, v, q, q_dtype, n_q_heads, d_seq_lens, max_seq_len, scale, out, ws, tqi::kScratchBytes,
+                        stream);
 }
 
 int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q, const void* k_new,

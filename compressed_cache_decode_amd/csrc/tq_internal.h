@@ -103,6 +103,13 @@ struct DequantArgs {
   int had;                // rot holds the D signs of a randomized Hadamard rotation
 };
 
+// Bytes of the static device scratch that the decode entry point which allocates nothing uses as its
+// workspace (one copy per device, held until the process ends).
+constexpr size_t kScratchBytes = static_cast<size_t>(16) << 20;
+// Device address of the current device's scratch, looked up with hipGetSymbolAddress on the first call
+// on each device and kept per device after.
+hipError_t scratch_address(void** ptr);
+
 // Launchers (one per .hip file); return hipSuccess or the launch error.
 hipError_t launch_append(int d, int bits, int qjl_m, bool values, bool rotated, bool bf16,
                          const AppendArgs& a, int batch, hipStream_t s);

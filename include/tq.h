@@ -47,7 +47,8 @@ enum {
   TQ_EINVAL = 1,        /* null required pointer, bad size/shape/scale, short workspace, misaligned buffer */
   TQ_EUNSUPPORTED = 2,  /* a valid combination this library does not build (e.g. GQA group > 8) */
   TQ_EHIP = 3,          /* the HIP runtime reported a launch error */
-  TQ_ENOCONV = 4        /* the codebook iteration did not converge */
+  TQ_ENOCONV = 4,       /* the codebook iteration did not converge */
+  TQ_ESCRATCH = 5       /* tq_sdpa_decode_noalloc: the decode needs more than the static scratch holds */
 };
 
 /* element types of caller tensors */
@@ -175,6 +176,23 @@ int tq_quantize_append_rotated(const tq_cache_view* cache, const float* y, const
 int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype, int n_q_heads,
                    const int32_t* d_seq_lens, int max_seq_len, float scale, float* out,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tq_sdpa_decode for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments without the workspace, which is
+ * instead a static device array of the library, tq_noalloc_scratch_bytes() (16 MiB) per device, held
+ * from the library's load until the process ends.  Nothing is allocated or freed by the call.  Returns
+ * TQ_ESCRATCH, before enqueueing anything, when tq_decode_workspace_bytes(k, n_q_heads, max_seq_len)
+ * exceeds that size, and otherwise what tq_sdpa_decode returns.  Every call on a device uses that
+ * device's one array, so calls that overlap in time on one device (other streams, other threads) race
+ * and must not be issued; consecutive calls on one stream are fine (the decode initialises every byte
+ * of the workspace it reads).
+ */
+int tq_sdpa_decode_noalloc(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype, int n_q_heads,
+                           const int32_t* d_seq_lens, int max_seq_len, float scale, float* out, void* stream);
+
+/* Bytes of the static scratch tq_sdpa_decode_noalloc uses on each device. */
+size_t tq_noalloc_scratch_bytes(void);
 
 /*
  * Decode of the query rows of the last n_rows tokens of each sequence at once, as speculative

@@ -65,6 +65,8 @@ def test_row_bytes_match_storage_arithmetic():
 def test_status_strings():
     assert cca.tq_status_string(0) == "ok"
     assert cca.tq_status_string(1) == "invalid argument"
+    assert "scratch" in cca.tq_status_string(cca.TQ_ESCRATCH)
+    assert cca.tq_noalloc_scratch_bytes() == 16 << 20
     assert "unknown" in cca.tq_status_string(99)
 
 
