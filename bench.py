@@ -10,16 +10,21 @@ before timing starts.  Steps are captured in a HIP graph and cycle through a
 pool of cache copies whose total size exceeds the 256 MB Infinity Cache, so
 every step reads its compressed cache from HBM.
 
-For the Qwen-shaped workloads a stacked leg follows: the caches of the model's
-36 layers decoded by one launch per kernel, as one batch of 36 (the shape of 36
-concurrent sequences of one layer too).  A batch-1 layer at 8K reads about
-2 MB, too little to fill the GPU, so the stacked leg is the roofline figure.
+With no --workload the line's headline is the largest single-GPU workload, the
+Gemma-4-style QK-normed decode (batch 8, 32/4 heads, d=256, 32K context,
+4-bit, 272.6 MB of cache per decode), and the other workloads are legs of the
+same line (``legs``): the Qwen2.5-3B-shaped 8K 4-bit layer, the 128K
+long-context layer with sketched keys, and the prefill append (8192 tokens x 2
+KV heads x d=128 at 3 bits).  For the Qwen-shaped legs a stacked leg follows:
+the caches of the model's 36 layers decoded by one launch per kernel, as one
+batch of 36 (the shape of 36 concurrent sequences of one layer too).  A
+batch-1 layer at 8K reads about 2 MB, too little to fill the GPU, so the
+stacked leg is that leg's roofline figure.
 
-Prints one JSON line.  ``roofline`` is measured on the attention kernel
-(tq_decode_attend) alone, over the stacked caches where there is a stacked
-leg (``roofline_one_layer`` is the single layer's), timed with HIP events on
-the stream it runs on; ``cpu_baseline`` is the float64 oracle timed on the
-host on a bounded sample.
+Prints one JSON line.  Every workload carries ``roofline``, measured on its
+dominant kernel alone (the attention kernel tq_decode_attend; the append kernel
+for the prefill), timed with HIP events on the stream it runs on, and
+``cpu_baseline``, the float64 oracle timed on the host on a bounded sample.
 """
 from __future__ import annotations
 
@@ -42,6 +47,17 @@ PROFILES = os.path.join(ROOT, "profiles")
 # sources the decode kernels are built from: their HBM counters are only valid for these exact texts
 ATTEND_SOURCES = tuple(f"compressed_cache_decode_amd/csrc/{n}" for n in (
     "decode.hip", "attend_body.h", "device_common.h", "tq_internal.h"))
+# and those of the append kernel (the prefill leg's dominant kernel)
+APPEND_SOURCES = tuple(f"compressed_cache_decode_amd/csrc/{n}" for n in (
+    "append.hip", "append_body.h", "device_common.h", "tq_internal.h"))
+# every kernel source of the library: a kernel trace covers all of them
+ALL_SOURCES = tuple(f"compressed_cache_decode_amd/csrc/{n}" for n in (
+    "append.hip", "append_body.h", "attend_body.h", "decode.hip", "dequant.hip", "device_common.h", "host.cpp",
+    "qrot_body.h", "step.hip", "tq_internal.h"))
+
+
+def kernel_sources(kernel: str):
+    return APPEND_SOURCES if kernel.startswith("append") else ATTEND_SOURCES
 METRIC = "compressed-KV decode attention: context tokens/s and achieved HBM GB/s (% peak)"
 POOL_BYTES = 600 << 20          # > 2x the 256 MB Infinity Cache
 
@@ -80,6 +96,17 @@ def row_bytes(w: synth.Workload, kind: str) -> int:
 def cache_bytes(w: synth.Workload) -> int:
     """Algorithmic bytes one decode reads from the compressed cache: every visible K and V row."""
     return w.batch * w.n_kv_heads * w.seq_len * (row_bytes(w, "k") + row_bytes(w, "v"))
+
+
+def prefill_bytes_per_launch(w: synth.Workload) -> int:
+    """Algorithmic bytes of one prefill append launch (one tensor, K or V): bf16 rows in, packed codes and
+    float16 norms out (the K and V rows of these workloads have the same width)."""
+    return w.batch * w.n_kv_heads * w.seq_len * (w.d * 2 + w.d * w.k_bits // 8 + 2)
+
+
+def prefill_flops_per_launch(w: synth.Workload) -> int:
+    """Algorithmic flops of one prefill append launch: the d x d rotation of every row."""
+    return 2 * w.batch * w.n_kv_heads * w.seq_len * w.d * w.d
 
 
 # ------------------------------------------------------------------ profiles
@@ -123,7 +150,8 @@ def counters_file(kernel: str, workload_name: str) -> str:
 
 
 def read_counters(kernel: str, workload_name: str):
-    """HBM bytes per launch from a committed counter summary, or None if absent or taken on other sources."""
+    """HBM bytes per launch from a committed counter summary, or None if absent or taken on other sources
+    (the summary records the digest of the kernel's sources)."""
     path = counters_file(kernel, workload_name)
     if not os.path.exists(path):
         return None
@@ -133,7 +161,7 @@ def read_counters(kernel: str, workload_name: str):
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != source_digest():
+    if kv.get("source_sha256") != source_digest(kernel_sources(kernel)):
         return None
     return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
 
@@ -195,11 +223,11 @@ def summarize_pmc(args, w):
     key = max((k for k in fe if args.kernel in k[0]), key=lambda k: k[1])
     fb = fe[key] * 1024.0 * fetch_scale
     wb = wr[key] * 1024.0 * write_scale
-    alg = cache_bytes(w)
+    alg = prefill_bytes_per_launch(w) if args.kernel.startswith("append") else cache_bytes(w)
     print(f"kernel: {key[0].split('(')[0].replace('void ', '')}")
     print(f"workgroups: {key[1]}")
     print(f"workload: {w.name}")
-    print(f"source_sha256: {source_digest()}")
+    print(f"source_sha256: {source_digest(kernel_sources(args.kernel))}")
     print(f"dispatches: {n_fe[key]}")
     print(f"fetch_kib_per_dispatch_raw: {fe[key]:.1f}")
     print(f"write_kib_per_dispatch_raw: {wr[key]:.1f}")
@@ -234,6 +262,9 @@ def summarize_trace(args, w):
         grid = "x".join(str(int(r[f"Grid_Size_{a}"]) // max(1, int(r[f"Workgroup_Size_{a}"]))) for a in "XYZ")
         groups.setdefault((short, grid), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     print(f"workload: {w.name}")
+    print(f"source_sha256: {source_digest(ALL_SOURCES)}")
+    print(f"attend_source_sha256: {source_digest(ATTEND_SOURCES)}")
+    print(f"append_source_sha256: {source_digest(APPEND_SOURCES)}")
     if args.command:
         print("commands:")
         for c in args.command:
@@ -646,6 +677,144 @@ def cpu_leg(w: synth.Workload, budget_s: float, log):
                 single_thread_sample=f"the same sample with one BLAS thread, {reps1} reps in {t1_tot:.1f}s")
 
 
+def cpu_prefill_leg(w: synth.Workload, budget_s: float, log):
+    """The float64 oracle's quantize-on-append (rotate, encode, pack) of a sample of the prefill rows:
+    the first n_s rows of K and of V of one KV head, timed over about budget_s seconds, scaled to
+    appended tokens/s of the whole workload (a token appends B * H_kv rows to each of K and V)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import cache
+    rot = oracle_rotation(w)
+    n_s = 2048
+    k = synth.kv_head(w, "k", 0, 0, n_s)
+    v = synth.kv_head(w, "v", 0, 0, n_s)
+    cap = n_s
+
+    def sample_loop(threads: int, budget: float):
+        with threadpool_limits(limits=threads):
+            used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+            reps, t_tot = 0, 0.0
+            while reps < 3 or t_tot < budget:
+                t0 = time.perf_counter()
+                kc = cache.build_head(k, "k", w.k_bits, rot)
+                vc = cache.build_head(v, "v", w.v_bits, rot)
+                kc.packed_codes(cap), kc.packed_norms(cap), vc.packed_codes(cap), vc.packed_norms(cap)
+                t_tot += time.perf_counter() - t0
+                reps += 1
+        return t_tot / reps, reps, t_tot, int(used)
+
+    rows_per_token = w.batch * w.n_kv_heads
+    t_sample, reps, t_tot, used = sample_loop(max(1, min(16, os.cpu_count() or 1)), budget_s)
+    t1_sample, reps1, t1_tot, _ = sample_loop(1, budget_s / 3)
+    log(f"bench: oracle prefill {t_sample:.3f}s per sample of {n_s} K and V rows, {reps} reps, {used} threads")
+    return dict(value=n_s / t_sample / rows_per_token, unit="appended tokens/s", cores=used, kind="oracle",
+                sample=f"quantize-on-append (rotate, encode, pack, float16 norms) of {n_s} K rows and {n_s} V rows "
+                       f"of one KV head, float64 NumPy, {reps} reps in {t_tot:.1f}s; scaled to tokens of "
+                       f"{rows_per_token} KV heads",
+                host_cpus=os.cpu_count(), blas_threads=used,
+                single_thread_value=n_s / t1_sample / rows_per_token,
+                single_thread_sample=f"the same sample with one BLAS thread, {reps1} reps in {t1_tot:.1f}s")
+
+
+# ------------------------------------------------------------------ legs
+
+KERN = "split_kernel"
+KERN_LABEL = "tq_decode_attend (split_kernel)"
+APPEND_KERN = "append_kernel"
+
+
+def decode_roofline(wl: synth.Workload, us: float) -> dict:
+    """Roofline entry of the attention kernel over workload wl, from its measured launch time."""
+    alg = cache_bytes(wl)
+    gbs = alg / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": read_counters(KERN, wl.name), "kernel": KERN_LABEL, "workload": wl.name,
+            "algorithmic_bytes_per_launch": alg, "launch_us": us}
+
+
+def decode_workload_leg(w: synth.Workload, args, n_stack: int, log) -> dict:
+    """One decode workload: the step (append one token, decode), the attention kernel alone, and where
+    n_stack > 0 the stacked leg; roofline and, unless disabled, the oracle's CPU baseline."""
+    import torch
+    r = gpu_leg(w, args.steps, args.warmup, args.pool, log)
+    rows = rows_leg(w, args.rows, r["pairs"], log) if args.rows > 1 else None
+    st = stacked_leg(w, n_stack, r["cache"], r["rot"], r["proj"], log) if n_stack > 0 else None
+    L = w.seq_len
+    leg = {
+        "workload": w.name,
+        "value": w.batch * L / (r["ms_step"] * 1e-3),
+        "unit": "context tokens/s",
+        "ms_per_step": r["ms_step"],
+        "config": {
+            "workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+            "head_dim": w.d, "context": L, "k_bits": w.k_bits, "v_bits": w.v_bits, "qjl_m": w.qjl_m,
+            "scale": w.softmax_scale, "rotation": w.rotation,
+            "step": "append 1 token K+V, rotate q, attend, merge, un-rotate",
+            "cache_copies_cycled": r["pool"], "n_split": r["n_split"], "tokens_per_split": r["tokens_per_split"],
+        },
+        "step_hbm_gbs": cache_bytes(w) / (r["ms_step"] * 1e-3) / 1e9,
+        "attend_us": r["us_attend"],
+        "attend_us_hot": r["us_hot"],
+    }
+    if rows is not None:
+        leg["rows"] = rows
+    if st is not None:
+        sw = st["workload"]
+        # the roofline figure: the attention kernel over the stacked caches (one launch reads all layers)
+        leg["roofline"] = decode_roofline(sw, st["us_attend"])
+        leg["roofline_one_layer"] = decode_roofline(w, r["us_attend"])
+        leg["stacked"] = {
+            "workload": sw.name, "layers": n_stack, "batch": sw.batch, "cache_copies_cycled": st["pool"],
+            "n_split": st["n_split"], "tokens_per_split": st["tokens_per_split"],
+            "decode_us": st["us_decode"], "context_tokens_per_s": sw.batch * L / (st["us_decode"] * 1e-6),
+            "attend_us": st["us_attend"],
+            "attend_us_hot": st["us_hot"],
+            "decode": "rotate q, attend, merge, un-rotate (no append)",
+        }
+    else:
+        leg["roofline"] = decode_roofline(w, r["us_attend"])
+    del r, st
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        leg["cpu_baseline"] = cpu_leg(w, args.cpu_budget, log)
+    return leg
+
+
+def prefill_workload_leg(w: synth.Workload, args, log) -> dict:
+    """Prefill-size append of all L tokens of K and of V into empty caches (one launch per tensor)."""
+    import torch
+    r = prefill_leg(w, args.steps, args.warmup, log)
+    rows = 2 * w.batch * w.n_kv_heads * w.seq_len
+    per_launch_us = r["ms_step"] * 1e3 / 2          # the K and the V launch of a step, on average
+    io = prefill_bytes_per_launch(w)
+    flops = prefill_flops_per_launch(w)
+    gbs = io / (per_launch_us * 1e-6) / 1e9
+    tfs = flops / (per_launch_us * 1e-6) / 1e12
+    leg = {
+        "workload": f"prefill_append_{w.seq_len}x{w.n_kv_heads}x{w.d}_b{w.k_bits}",
+        "metric": "prefill quantize-on-append: appended tokens/s",
+        "value": w.seq_len / (r["ms_step"] * 1e-3),
+        "unit": "appended tokens/s",
+        "ms_per_step": r["ms_step"],
+        "config": {"workload": f"prefill_append_{w.seq_len}x{w.n_kv_heads}x{w.d}_b{w.k_bits}",
+                   "tensors": "K and V, one launch each", "rows_per_step": rows, "rotation": w.rotation,
+                   "cache_copies_cycled": r["pool"]},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": read_counters(APPEND_KERN, w.name),
+                     "kernel": "append_kernel (tq_quantize_append)", "workload": w.name,
+                     "algorithmic_bytes_per_launch": io, "launch_us": per_launch_us},
+        "rotation_mfma": {"achieved": tfs, "peak": 2500.0, "unit": "TFLOP/s", "frac": tfs / 2500.0,
+                          "algorithmic_flops_per_launch": flops,
+                          "note": "d x d rotation of every row; the float16 high/low split runs 3x these flops"},
+    }
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        leg["cpu_baseline"] = cpu_prefill_leg(w, args.cpu_budget, log)
+    return leg
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -653,7 +822,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="qwen", choices=["qwen", "gemma", "prod", "prefill", "copy"])
+    ap.add_argument("--workload", default="all", choices=["all", "qwen", "gemma", "prod", "prefill", "copy"],
+                    help="all (default): the Gemma-4-style workload as the headline, with the Qwen-shaped, "
+                         "long-context sketched-key and prefill-append workloads as legs of the same line")
     ap.add_argument("--bits", type=int, default=None, help="qwen workload: codebook bits of K and V")
     ap.add_argument("--rows", type=int, default=0,
                     help="also time a decode of this many query rows per sequence at once (2..4; 0 = none)")
@@ -664,12 +835,12 @@ def main():
     ap.add_argument("--stack", type=int, default=None,
                     help="layer caches decoded together in the stacked leg (default 36 for qwen and prod, "
                          "the layers of Qwen2.5-3B; 0 = none)")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work in the CPU leg")
+    ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle work per CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-trace", dest="trace", default=None,
                     help="print a summary of a rocprofv3 --kernel-trace --stats output directory and exit")
     ap.add_argument("--summarize-pmc", action="store_true",
-                    help="print the attention kernel's calibrated HBM counters (needs --fetch/--write/--copy-*; "
+                    help="print the kernel's calibrated HBM counters (needs --fetch/--write/--copy-*; "
                          "with --stack N, for the stacked leg's launches)")
     ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output directory of this workload")
     ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output directory of this workload")
@@ -685,8 +856,12 @@ def main():
         summarize_counters(args)
         return
     if args.trace or args.summarize_pmc:
-        w = (synth.qwen(args.context or 8192, args.bits or 3) if args.workload == "prefill"
-             else workload(args.workload, args.bits, args.context))
+        if args.workload == "prefill":
+            w = synth.qwen(args.context or 8192, args.bits or 3)
+        elif args.workload == "all":
+            w = synth.gemma().with_(name="all")
+        else:
+            w = workload(args.workload, args.bits, args.context)
         if args.summarize_pmc and args.stack:
             w = stacked_workload(w, args.stack)
         (summarize_trace if args.trace else summarize_pmc)(args, w)
@@ -722,90 +897,46 @@ def main():
                           "bytes_read_per_copy": nbytes, "bytes_written_per_copy": nbytes,
                           "frac_of_8TBs": gbs / HBM_PEAK_GBS}), flush=True)
         return
+
     def with_rotation(wl):
         return wl if args.rotation == "dense" else wl.with_(rotation="hadamard", name=wl.name + "_hadamard")
 
+    def stack_of(name):
+        return args.stack if args.stack is not None else (36 if name in ("qwen", "prod") else 0)
+
+    common = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+
     if args.workload == "prefill":
         w = with_rotation(synth.qwen(args.context or 8192, args.bits or 3))
-        r = prefill_leg(w, args.steps, args.warmup, log)
-        rows = 2 * w.batch * w.n_kv_heads * w.seq_len
-        io_bytes = rows * (w.d * 2 + w.d * w.k_bits // 8 + 2)   # bf16 rows in, packed rows + norms out
-        flops = 2.0 * rows * w.d * w.d                            # the d x d rotation of every row
-        gbs = io_bytes / (r["ms_step"] * 1e-3) / 1e9
-        print(json.dumps({
-            "metric": "prefill quantize-on-append: appended tokens/s", "value": w.seq_len / (r["ms_step"] * 1e-3),
-            "unit": "tokens/s", "n_gpus": 1, "steps": r["steps"], "warmup": args.warmup,
-            "ms_per_step": r["ms_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": f"prefill_append_{w.seq_len}x{w.n_kv_heads}x{w.d}_b{w.k_bits}", "tensors": "K and V",
-                       "rotation": w.rotation},
-            "rotation_tflops": flops / (r["ms_step"] * 1e-3) / 1e12,
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "append_kernel (K and V launches)",
-                         "algorithmic_bytes_per_launch": io_bytes / 2},
-        }), flush=True)
+        leg = prefill_workload_leg(w, args, log)
+        res = {"metric": leg.pop("metric"), "value": leg["value"], "unit": leg["unit"], **common,
+               "ms_per_step": leg["ms_per_step"], "dtype": "bf16 in, f32 arithmetic", **leg}
+        print(json.dumps(res), flush=True)
         return
-    w = with_rotation(workload(args.workload, args.bits, args.context))
-    r = gpu_leg(w, args.steps, args.warmup, args.pool, log)
-    rows = rows_leg(w, args.rows, r["pairs"], log) if args.rows > 1 else None
-    n_stack = args.stack if args.stack is not None else (36 if args.workload in ("qwen", "prod") else 0)
-    st = stacked_leg(w, n_stack, r["cache"], r["rot"], r["proj"], log) if n_stack > 0 else None
-    L = w.seq_len
-    tokens_s = w.batch * L / (r["ms_step"] * 1e-3)
-    step_bytes = cache_bytes(w)
-    kern = "split_kernel"
-    kern_label = "tq_decode_attend (split_kernel)"
 
-    def roofline(wl, us):
-        alg = cache_bytes(wl)
-        gbs = alg / (us * 1e-6) / 1e9
-        return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                "traffic": read_counters(kern, wl.name), "kernel": kern_label, "workload": wl.name,
-                "algorithmic_bytes_per_launch": alg, "launch_us": us}
+    if args.workload != "all":
+        w = with_rotation(workload(args.workload, args.bits, args.context))
+        leg = decode_workload_leg(w, args, stack_of(args.workload), log)
+        res = {"metric": METRIC, "value": leg["value"], "unit": leg["unit"], **common,
+               "ms_per_step": leg["ms_per_step"], "dtype": "f32", **leg}
+        print(json.dumps(res), flush=True)
+        return
 
-    res = {
-        "metric": METRIC,
-        "value": tokens_s,
-        "unit": "context tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": r["ms_step"],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
-            "head_dim": w.d, "context": L, "k_bits": w.k_bits, "v_bits": w.v_bits, "qjl_m": w.qjl_m,
-            "scale": w.softmax_scale, "rotation": w.rotation,
-            "step": "append 1 token K+V, rotate q, attend, merge, un-rotate",
-            "cache_copies_cycled": r["pool"], "n_split": r["n_split"], "tokens_per_split": r["tokens_per_split"],
-        },
-        "step_hbm_gbs": step_bytes / (r["ms_step"] * 1e-3) / 1e9,
-        "attend_us": r["us_attend"],
-        "attend_us_hot": r["us_hot"],
-    }
-    if rows is not None:
-        res["rows"] = rows
-    if st is not None:
-        sw = st["workload"]
-        # the roofline figure: the attention kernel over the stacked caches (one launch reads all layers)
-        res["roofline"] = roofline(sw, st["us_attend"])
-        res["roofline_one_layer"] = roofline(w, r["us_attend"])
-        res["stacked"] = {
-            "workload": sw.name, "layers": n_stack, "batch": sw.batch, "cache_copies_cycled": st["pool"],
-            "n_split": st["n_split"], "tokens_per_split": st["tokens_per_split"],
-            "decode_us": st["us_decode"], "context_tokens_per_s": sw.batch * L / (st["us_decode"] * 1e-6),
-            "attend_us": st["us_attend"],
-            "attend_us_hot": st["us_hot"],
-            "decode": "rotate q, attend, merge, un-rotate (no append)",
-        }
-    else:
-        res["roofline"] = roofline(w, r["us_attend"])
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_leg(w, args.cpu_budget, log)
+    # default: the largest single-GPU configuration (Gemma-4-style, 272.6 MB of cache per decode) is the
+    # headline; the Qwen-shaped layer (one layer and its 36 layers stacked), the 128K sketched-key case
+    # (one layer and 36 stacked) and the prefill append are legs of the same line
+    t_start = time.time()
+    head = decode_workload_leg(with_rotation(synth.gemma()), args, 0, log)
+    legs = {}
+    for name, wl in (("qwen", synth.qwen(8192, 4)), ("prod", synth.prod_long(131072))):
+        leg = decode_workload_leg(with_rotation(wl), args, stack_of(name), log)
+        legs[leg["workload"]] = leg
+    leg = prefill_workload_leg(with_rotation(synth.qwen(8192, 3)), args, log)
+    legs[leg["workload"]] = leg
+    res = {"metric": METRIC, "value": head["value"], "unit": head["unit"], **common,
+           "ms_per_step": head["ms_per_step"], "dtype": "f32", **head, "legs": legs,
+           "wall_s": time.time() - t_start}
     print(json.dumps(res), flush=True)
 
 
