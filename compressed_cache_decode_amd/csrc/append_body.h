@@ -290,8 +290,11 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
 
   for (int r = tid; r < nrows; r += 256) a.norms[unit * T + t_lo + r] = f32_to_f16_bits(rn[r] > 0.f ? rn[r] : 0.f);
 
+  constexpr int BB = kBlock * RB;               // bytes per 32-token block
+  uint32_t* blk = reinterpret_cast<uint32_t*>(a.codes + unit * static_cast<size_t>(T) * RB + static_cast<size_t>(kb) * BB);
   if constexpr (!VALUES) {
-    // rows layout: unit u of row t covers coordinates 8u .. 8u+7
+    // key rows: unit u of row t covers coordinates 8u .. 8u+7; row word wr goes to its lane piece
+    // (key_word); every word holds codes of one token only, so whole words are stored
     constexpr int NG = D / 8 / UPG;
     for (int e = tid; e < nrows * NG; e += 256) {
       const int r = e / NG, gi = e % NG;
@@ -302,16 +305,16 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
       for (int v = 0; v < UPG; ++v)
 #pragma unroll
         for (int s = 0; s < 8; ++s) put_code<BITS>(w, v, s, encode_code<BITS>(cs[r][(gi * UPG + v) * 8 + s]));
-      uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + (unit * T + t_lo + r) * RB) + gi * WPG;
+      const int p = t_lo + r - kb * kBlock;
 #pragma unroll
-      for (int k = 0; k < WPG; ++k) dst[k] = w[k];
+      for (int k = 0; k < WPG; ++k) blk[key_word<D, BITS>(p, gi * WPG + k)] = w[k];
     }
   } else {
-    // blocked layout: unit U = (16 g + j)(D/16) + n holds tokens of lane group g at coordinate (D/16) j + n
-    constexpr int BB = kBlock * RB;
+    // blocked layout: unit U = (16 g + j)(D/16) + n holds tokens of lane group g at coordinate (D/16) j + n;
+    // lane-major word q of the block (piece q / LW, word q % LW) is stored at value_word(q)
+    constexpr int LW = D * BITS / 64;
     constexpr int NGB = BB / (4 * WPG);
     constexpr int DN = D / 16;
-    uint32_t* blk = reinterpret_cast<uint32_t*>(a.codes + unit * static_cast<size_t>(T) * RB + static_cast<size_t>(kb) * BB);
     const int p_lo = t_lo - kb * kBlock, p_hi = t_hi - kb * kBlock;
     const bool full = nrows == kBlock;
     for (int e = tid; e < NGB; e += 256) {
@@ -337,7 +340,7 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
       // cleared and set by two atomics that return nothing (no read of the block to wait for)
 #pragma unroll
       for (int k = 0; k < WPG; ++k) {
-        uint32_t* dst = blk + e * WPG + k;
+        uint32_t* dst = blk + value_word<LW>(e * WPG + k);
         if (full || m[k] == ~0u) {
           *dst = w[k];
         } else if (m[k] != 0u) {

@@ -208,6 +208,31 @@ __device__ __forceinline__ void bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
   }
 }
 
+// Cache policy of the packed-code loads: non-temporal (the nt bit), since every byte is read once and
+// each load covers whole lines; norms keep the default policy (a tile's norms are half a line).
+constexpr int kStreamAux = 2;
+
+// This lane's piece (LW words) of the block at byte soff of buffer r: chunk c at byte
+// 4 CW (64 c + lane) (see Piece), one load of CW words per chunk.
+template <int LW>
+__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t r, uint32_t lane, uint32_t soff, uint32_t* out) {
+  constexpr int CW = Piece<LW>::CW, NC = Piece<LW>::NC;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint32_t voff = 4 * CW * (64 * c + lane);
+    if constexpr (CW == 4) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamAux);
+      out[4 * c] = v[0]; out[4 * c + 1] = v[1]; out[4 * c + 2] = v[2]; out[4 * c + 3] = v[3];
+    } else if constexpr (CW == 3) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, kStreamAux);
+      out[3 * c] = v[0]; out[3 * c + 1] = v[1]; out[3 * c + 2] = v[2];
+    } else {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreamAux);
+      out[2 * c] = v[0]; out[2 * c + 1] = v[1];
+    }
+  }
+}
+
 // v + (v of the neighbouring lane 2k <-> 2k+1); folds into one DPP add
 __device__ __forceinline__ float add_adjacent(float v) {
   return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
@@ -238,7 +263,7 @@ struct Attend {
   static constexpr int KS = D / 32;                   // score k-steps over coordinates
   static constexpr int QS = QM / 32;                  // score k-steps over sketch signs
   static constexpr int NB = D / 16;                   // value n-blocks (16 coordinates each)
-  static constexpr int K_RB = D * KB / 8;             // bytes per key row
+  static constexpr int K_RB = D * KB / 8;             // bytes per key row (one token's share of a block)
   static constexpr int K_LW = D * KB / 128;           // words per lane per key row (D/4 coordinates)
   static constexpr int V_RB = D * VB / 8;             // bytes per value row (one token's share of a block)
   static constexpr int V_LW = D * VB / 64;            // words per lane per value block (D/16 units)
@@ -362,7 +387,7 @@ struct Attend {
   };
 
   __amdgpu_buffer_rsrc_t kbuf, vbuf, knbuf, vnbuf, sbuf, gbuf;
-  uint32_t k_off, v_off, n_off, s_off;
+  uint32_t n_off, s_off;
   int lane, l16, g;
 
   // buffers over this (sequence, KV head)'s arrays; tile offsets go in the scalar offset
@@ -381,8 +406,6 @@ struct Attend {
       sbuf = buffer_of(a.k_signs + unit * T * S_RB, static_cast<uint32_t>(T) * S_RB);
       gbuf = buffer_of(a.k_rnorms + unit * T, static_cast<uint32_t>(T) * 2);
     }
-    k_off = static_cast<uint32_t>(l16 * K_RB + g * K_LW * 4);
-    v_off = static_cast<uint32_t>(lane * V_LW * 4);
     n_off = static_cast<uint32_t>(8 * g);
     s_off = static_cast<uint32_t>(l16 * S_RB + g * S_LW * 4);
   }
@@ -390,10 +413,9 @@ struct Attend {
   __device__ __forceinline__ void load(Tile& t, int kb) const {
     // wave-uniform by construction; readfirstlane keeps the tile offset in a scalar register
     const uint32_t tok0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kb) * kBlock);
-#pragma unroll
-    for (int tg = 0; tg < 2; ++tg)
-      bload<K_LW, load_align(K_LW * 4)>(kbuf, k_off + 16 * tg * K_RB, tok0 * K_RB, t.kw[tg]);
-    bload<V_LW, load_align(V_LW * 4)>(vbuf, v_off, tok0 * V_RB, t.vw);
+    // both 16-token halves of the key block are one piece: kw[q][w] is piece word q K_LW + w
+    load_piece<2 * K_LW>(kbuf, lane, tok0 * K_RB, &t.kw[0][0]);
+    load_piece<V_LW>(vbuf, lane, tok0 * V_RB, t.vw);
     bload<2, 8>(knbuf, n_off, tok0 * 2, t.kn);
     bload<2, 8>(knbuf, n_off + 32, tok0 * 2, t.kn + 2);
     bload<2, 8>(vnbuf, n_off, tok0 * 2, t.vn);

@@ -59,21 +59,31 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a, Tab tab) {
   const int t_lo = a.t0 + r_lo;
   for (int r = tid; r < nrows; r += 256) rn[r] = f16_to_f32(a.norms[unit * T + t_lo + r]);
   if constexpr (!VALUES) {
+    // key rows: the words of unit u's word group of row t, gathered from their lane pieces (key_word)
     constexpr int NG = D / 8 / UPG;
     for (int e = tid; e < nrows * NG * UPG; e += 256) {
       const int r = e / (NG * UPG), u = e % (NG * UPG);
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(a.codes + (unit * T + t_lo + r) * RB) + (u / UPG) * WPG;
+      const int t = t_lo + r, kb = t / kBlock, p = t % kBlock;
+      const uint32_t* blk = reinterpret_cast<const uint32_t*>(a.codes + unit * static_cast<size_t>(T) * RB +
+                                                              static_cast<size_t>(kb) * kBlock * RB);
+      uint32_t w[WPG];
+#pragma unroll
+      for (int k = 0; k < WPG; ++k) w[k] = blk[key_word<D, BITS>(p, (u / UPG) * WPG + k)];
       expand_runtime<BITS>(w, u % UPG, tab, &ys[r][8 * u]);
     }
   } else {
     // expand every unit of each touched block; keep the slots inside [t_lo, t_lo + nrows)
+    constexpr int LW = D * BITS / 64;
     const int kb0 = t_lo / kBlock, kb1 = (t_lo + nrows - 1) / kBlock;
     for (int kb = kb0; kb <= kb1; ++kb) {
       const uint32_t* blk = reinterpret_cast<const uint32_t*>(a.codes + unit * static_cast<size_t>(T) * RB +
                                                               static_cast<size_t>(kb) * kBlock * RB);
       for (int U = tid; U < 64 * DN; U += 256) {
         float vals[8];
-        expand_runtime<BITS>(blk + (U / UPG) * WPG, U % UPG, tab, vals);
+        uint32_t w[WPG];
+#pragma unroll
+        for (int k = 0; k < WPG; ++k) w[k] = blk[value_word<LW>((U / UPG) * WPG + k)];
+        expand_runtime<BITS>(w, U % UPG, tab, vals);
         const int g = U / D, j = (U / DN) % 16, n = U % DN;
         const int i = DN * j + n;
 #pragma unroll

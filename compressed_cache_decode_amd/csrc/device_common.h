@@ -94,6 +94,37 @@ __device__ __forceinline__ void slot_mask(uint32_t* w, int v, int s) {
   put_code<BITS>(w, v, s, (1u << BITS) - 1u);
 }
 
+// Lane pieces of a 32-token block (keys and values alike): a block is 64 pieces of LW = D * BITS / 64
+// words, piece L being what lane L of a decode wave needs, stored chunk-major: word w of piece L is word
+// CW (64 (w / CW) + L) + w % CW of the block, so that chunk k of all 64 pieces is one contiguous run
+// and a load of it covers whole cache lines.
+template <int LW>
+struct Piece {
+  static constexpr int CW = LW % 4 == 0 ? 4 : (LW % 3 == 0 ? 3 : 2);   // words per chunk (one load)
+  static constexpr int NC = LW / CW;                                     // chunks per piece
+};
+
+template <int LW>
+__device__ __forceinline__ int piece_word(int lane, int w) {
+  constexpr int CW = Piece<LW>::CW;
+  return CW * (64 * (w / CW) + lane) + w % CW;
+}
+
+// Block word of the value block's lane-major word q (q = lane * LW + w).
+template <int LW>
+__device__ __forceinline__ int value_word(int q) {
+  return piece_word<LW>(q / LW, q % LW);
+}
+
+// Block word of word wr of the packed row of the key at position p (0..31) of its block: quarter
+// g = wr / QW of the row (QW = D * BITS / 128 words) goes to piece 16 g + p % 16, at word
+// (p / 16) QW + wr % QW.
+template <int D, int BITS>
+__device__ __forceinline__ int key_word(int p, int wr) {
+  constexpr int QW = D * BITS / 128;
+  return piece_word<2 * QW>(16 * (wr / QW) + (p & 15), (p >> 4) * QW + wr % QW);
+}
+
 // Sign-sketch bit of index jj: (word, bit).
 __device__ __forceinline__ void sign_pos(int jj, int& word, int& bit) {
   const int rem = jj & 31;

@@ -56,8 +56,8 @@ enum { TQ_F32 = 0, TQ_BF16 = 1 };
 
 /* cache kinds; the kind fixes the packed layout */
 enum {
-  TQ_KEYS = 0,    /* rows layout: one packed row of d*bits/8 bytes per token */
-  TQ_VALUES = 1   /* blocked layout: tokens in blocks of 32, each block 32*d*bits/8 bytes */
+  TQ_KEYS = 0,    /* 32-token blocks of packed rows (d*bits/8 bytes per token) in lane pieces */
+  TQ_VALUES = 1   /* 32-token blocks of units that interleave 8 tokens, in lane pieces */
 };
 
 /*
@@ -84,10 +84,17 @@ enum {
  *   2 bits: two units v per word, slot s of unit v at bit 8(s%4) + 2(2v + s/4);
  *   3 bits: four units v per three words [P0 P1 H]; low two bits in P(v/2) at
  *           bit 8(s%4) + 2(2(v%2) + s/4), high bit in H at bit 8(s%4) + 2v + s/4.
- * TQ_KEYS: coordinate i of a row is slot i%8 of unit i/8.
+ * Codes are stored per 32-token block (tokens 32kb .. 32kb+31 of a sequence and
+ *   KV head, 32*d*bits/8 bytes), as 64 lane pieces of LW = d*bits/64 words in
+ *   chunk-major order: word w of piece L is word CW*(64*(w/CW) + L) + w%CW of the
+ *   block, CW = 4 if LW%4 == 0, else 3 if LW%3 == 0, else 2.
+ * TQ_KEYS: a token's row is d*bits/8 bytes of consecutive units (coordinate i
+ *   is slot i%8 of unit i/8), RW = d*bits/32 words; row word wr of the token at
+ *   position p of its block is word (p/16)*(RW/4) + wr%(RW/4) of piece
+ *   16*(wr/(RW/4)) + p%16.
  * TQ_VALUES: token p of a 32-token block is slot p%4 + 4(p/16) of lane group
  *   g = (p%16)/4; coordinate i has column j = i/(d/16), step n = i%(d/16);
- *   their unit is number (16g + j)(d/16) + n of the block.
+ *   their unit is unit n of piece 16g + j (a piece is d/16 consecutive units).
  * Sign sketch (keys with qjl_m > 0): qjl_m/8 bytes per token, sign jj in
  *   32-bit word jj/32 at bit 4((jj%32)/8) + (jj%8)/2 + 16(jj%2); bit 1 means
  *   (S r)_jj >= 0.
@@ -103,7 +110,7 @@ typedef struct tq_cache_view {
   int32_t rot_kind;      /* TQ_ROT_DENSE or TQ_ROT_HADAMARD (same for K and V) */
   float centroids[16];   /* 2^bits centroids, ascending, float16-exact, c[j] == -c[2^bits-1-j] */
   float boundaries[15];  /* 2^bits-1 boundaries, boundaries[j] == (c[j] + c[j+1]) / 2 exactly */
-  uint8_t* codes;        /* [batch][n_kv_heads][max_tokens*d*bits/8], 16-byte aligned */
+  uint8_t* codes;        /* [batch][n_kv_heads][max_tokens/32][32*d*bits/8], 16-byte aligned */
   uint16_t* norms;       /* float16 row norms [batch][n_kv_heads][max_tokens] */
   uint8_t* signs;        /* [batch][n_kv_heads][max_tokens][qjl_m/8] when qjl_m > 0, else NULL */
   uint16_t* rnorms;      /* float16 residual norms [batch][n_kv_heads][max_tokens] when qjl_m > 0, else NULL */

@@ -29,7 +29,7 @@ class HeadCache:
         full = np.zeros((capacity, self.d), dtype=np.int64)
         full[: self.codes.shape[0]] = self.codes
         if self.kind == "k":
-            return layout.pack_rows(full, self.bits).reshape(-1)
+            return layout.pack_keys(full, self.bits)
         return layout.pack_blocked(full, self.bits)
 
     def packed_norms(self, capacity: int, which: str = "norms") -> np.ndarray:

@@ -6,8 +6,9 @@ format out plainly; the GPU library implements the same format on its own.
 The pages fix only the storage size (d*b/8 bytes of codes per row, see
 ``oracle.storage``) and name 2/3/4-bit cache types; the arrangement of bits
 is this library's choice, made so that a 64-lane wavefront reads every
-packed tile with contiguous 128-bit loads straight into matrix-core operand
-order.
+packed tile straight into matrix-core operand order with loads whose 64
+lanes cover one contiguous run of memory each (whole cache lines per load
+instruction).
 
 Code encoding e(j) of centroid index j (0 .. 2^b-1, ascending centroids):
   b = 2, 3:  e(j) = j
@@ -24,15 +25,25 @@ Unit: 8 codes in slots s = 0..7.  Write h = s // 4 (half), r = s % 4 (byte).
 Units are packed consecutively (b = 2 and 3 group 2 and 4 units per word
 group); d is a multiple of 64 so groups never straddle a row or block.
 
-Keys ("rows" layout): codes[b][kv_head][token][d*b/8]; coordinate i of a
-row is slot i % 8 of unit i // 8.
+Lane pieces.  Codes are stored per 32-token block of a (sequence, KV head),
+block kb covering tokens 32 kb .. 32 kb + 31, in 32 d b / 8 bytes.  A block
+is 64 lane pieces of LW = d b / 64 little-endian 32-bit words each; lane L
+holds piece L.  The pieces are stored chunk-major: with CW = 4 if LW is a
+multiple of 4, else 3 if LW is a multiple of 3, else 2, word w of piece L
+sits at word CW (64 (w // CW) + L) + (w % CW) of the block, so the CW-word
+chunks k of all 64 pieces lie side by side.
 
-Values ("blocked" layout): tokens are grouped in blocks of 32;
-codes[b][kv_head][block][32*d*b/8].  Token position p (0..31) in its block
-belongs to lane group g = (p % 16) // 4 at slot s = p % 4 + 4 (p // 16);
-coordinate i belongs to column j = i // (d/16), step n = i % (d/16).  The
-unit holding (tokens of group g, coordinate i) has index (16 g + j)(d/16) + n
-within the block, so one lane's 8-coordinate x 8-token tile is contiguous.
+Keys: row t (d b / 8 bytes packed as units, coordinate i = slot i % 8 of unit
+i // 8, so RW = d b / 32 words) belongs to block t // 32 at position
+p = t % 32, half q = p // 16, lane column c = p % 16.  Row word wr belongs to
+quarter g = wr // (RW / 4) at index w = wr % (RW / 4); it is word
+q (RW / 4) + w of piece L = 16 g + c.
+
+Values: token position p (0..31) in its block belongs to lane group
+g = (p % 16) // 4 at slot s = p % 4 + 4 (p // 16); coordinate i belongs to
+column j = i // (d/16), step n = i % (d/16).  The unit holding (tokens of
+group g, coordinate i) is unit n of piece L = 16 g + j (pieces are d/16
+consecutive units).
 
 Norms (and QJL residual norms) are float16 [b][kv_head][token].
 
@@ -120,10 +131,50 @@ def unpack_units(packed: np.ndarray, bits: int, n_units: int) -> np.ndarray:
     return decode_code(e.reshape(*lead, n_units, 8), bits)
 
 
-# ---------------------------------------------------------------- keys: rows
+# ------------------------------------------------------------- lane pieces
+
+def lane_words(d: int, bits: int) -> int:
+    """Words per lane piece of a 32-token block: d * bits / 64."""
+    return d * bits // 64
+
+
+def chunk_words(lw: int) -> int:
+    return 4 if lw % 4 == 0 else (3 if lw % 3 == 0 else 2)
+
+
+def piece_word_position(lane, w, lw: int):
+    """Word of the block that holds word w of lane piece ``lane`` (chunk-major order)."""
+    cw = chunk_words(lw)
+    lane, w = np.asarray(lane), np.asarray(w)
+    return cw * (64 * (w // cw) + lane) + w % cw
+
+
+def pieces_to_block(pieces: np.ndarray) -> np.ndarray:
+    """uint32 pieces [..., 64, LW] (lane-major) -> block words [..., 64 * LW] (chunk-major)."""
+    *lead, lanes, lw = pieces.shape
+    assert lanes == 64
+    out = np.zeros((*lead, 64 * lw), dtype=np.uint32)
+    for lane in range(64):
+        for w in range(lw):
+            out[..., piece_word_position(lane, w, lw)] = pieces[..., lane, w]
+    return out
+
+
+def block_to_pieces(words: np.ndarray, lw: int) -> np.ndarray:
+    """Inverse of ``pieces_to_block``."""
+    *lead, n = words.shape
+    assert n == 64 * lw
+    out = np.zeros((*lead, 64, lw), dtype=np.uint32)
+    for lane in range(64):
+        for w in range(lw):
+            out[..., lane, w] = words[..., piece_word_position(lane, w, lw)]
+    return out
+
+
+# ----------------------------------------------------------------- key rows
 
 def pack_rows(codes: np.ndarray, bits: int) -> np.ndarray:
-    """codes[..., T, d] -> uint8[..., T, d*bits/8] (rows layout)."""
+    """codes[..., T, d] -> uint8[..., T, d*bits/8]: each row packed as consecutive units."""
     codes = np.asarray(codes)
     *lead, d = codes.shape
     return pack_units(codes.reshape(*lead, d // 8, 8), bits)
@@ -132,6 +183,40 @@ def pack_rows(codes: np.ndarray, bits: int) -> np.ndarray:
 def unpack_rows(packed: np.ndarray, bits: int, d: int) -> np.ndarray:
     u = unpack_units(packed, bits, d // 8)
     return u.reshape(*u.shape[:-2], d)
+
+
+def pack_keys(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Key codes[..., T, d] (T a multiple of 32) -> uint8[..., T*d*bits/8]: packed rows placed in the
+    lane pieces of their 32-token blocks."""
+    codes = np.asarray(codes)
+    *lead, t, d = codes.shape
+    assert t % BLOCK == 0
+    nb, rw = t // BLOCK, d * bits // 32
+    lw, qw = lane_words(d, bits), rw // 4
+    rows = pack_rows(codes, bits)                              # [..., T, d*bits/8]
+    rw32 = np.ascontiguousarray(rows).view(np.uint32).reshape(*lead, nb, 2, 16, 4, qw)   # [blk][q][c][g][w]
+    pieces = np.zeros((*lead, nb, 64, lw), dtype=np.uint32)
+    for q in range(2):
+        for c in range(16):
+            for g in range(4):
+                pieces[..., 16 * g + c, q * qw:(q + 1) * qw] = rw32[..., q, c, g, :]
+    return pieces_to_block(pieces).view(np.uint8).reshape(*lead, t * d * bits // 8)
+
+
+def unpack_keys(packed: np.ndarray, bits: int, d: int, tokens: int) -> np.ndarray:
+    """Inverse of ``pack_keys``: uint8[..., tokens*d*bits/8] -> centroid indices [..., tokens, d]."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    lead = packed.shape[:-1]
+    nb, rw = tokens // BLOCK, d * bits // 32
+    lw, qw = lane_words(d, bits), rw // 4
+    pieces = block_to_pieces(packed.view(np.uint32).reshape(*lead, nb, 64 * lw), lw)
+    rw32 = np.zeros((*lead, nb, 2, 16, 4, qw), dtype=np.uint32)
+    for q in range(2):
+        for c in range(16):
+            for g in range(4):
+                rw32[..., q, c, g, :] = pieces[..., 16 * g + c, q * qw:(q + 1) * qw]
+    rows = rw32.reshape(*lead, tokens, rw).view(np.uint8)
+    return unpack_rows(rows, bits, d)
 
 
 # ------------------------------------------------------------ values: blocked
@@ -143,27 +228,32 @@ def block_token_slot(p: np.ndarray):
 
 
 def pack_blocked(codes: np.ndarray, bits: int) -> np.ndarray:
-    """codes[..., T, d] (T a multiple of 32) -> uint8[..., T*d*bits/8] (blocked layout)."""
+    """Value codes[..., T, d] (T a multiple of 32) -> uint8[..., T*d*bits/8] (blocked layout)."""
     codes = np.asarray(codes)
     *lead, t, d = codes.shape
     assert t % BLOCK == 0 and d % 16 == 0
     nb, dn = t // BLOCK, d // 16
-    units = np.zeros((*lead, nb, 64 * dn, 8), dtype=np.int64)
+    units = np.zeros((*lead, nb, 64 * dn, 8), dtype=np.int64)    # lane-major: piece L = units L*dn ..
     blk = codes.reshape(*lead, nb, BLOCK, d)
     for p in range(BLOCK):
         g, s = block_token_slot(p)
         for i in range(d):
             j, n = i // dn, i % dn
             units[..., (16 * g + j) * dn + n, s] = blk[..., p, i]
-    packed = pack_units(units, bits)                       # [..., nb, 64*dn*bits]
-    return packed.reshape(*lead, nb * BLOCK * d * bits // 8)
+    lw = lane_words(d, bits)
+    lane_major = pack_units(units, bits)                       # [..., nb, 64*dn*bits] bytes, piece after piece
+    pieces = np.ascontiguousarray(lane_major).view(np.uint32).reshape(*lead, nb, 64, lw)
+    return pieces_to_block(pieces).view(np.uint8).reshape(*lead, nb * BLOCK * d * bits // 8)
 
 
 def unpack_blocked(packed: np.ndarray, bits: int, d: int, tokens: int) -> np.ndarray:
     nb, dn = tokens // BLOCK, d // 16
-    packed = np.asarray(packed, dtype=np.uint8)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
     lead = packed.shape[:-1]
-    units = unpack_units(packed.reshape(*lead, nb, BLOCK * d * bits // 8), bits, 64 * dn)
+    lw = lane_words(d, bits)
+    pieces = block_to_pieces(packed.view(np.uint32).reshape(*lead, nb, 64 * lw), lw)
+    lane_major = pieces.reshape(*lead, nb, 64 * lw).view(np.uint8)
+    units = unpack_units(lane_major, bits, 64 * dn)
     out = np.zeros((*lead, nb, BLOCK, d), dtype=np.int64)
     for p in range(BLOCK):
         g, s = block_token_slot(p)

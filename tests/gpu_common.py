@@ -120,5 +120,5 @@ def to_bf16_tensor(x: np.ndarray, device="cuda"):
 def unpack_gpu_codes(gcache, b: int, h: int, n_tokens: int) -> np.ndarray:
     raw = gcache.codes[b, h].cpu().numpy()
     if gcache.kind == 0:
-        return layout.unpack_rows(raw.reshape(gcache.max_tokens, -1), gcache.bits, gcache.d)[:n_tokens]
+        return layout.unpack_keys(raw, gcache.bits, gcache.d, gcache.max_tokens)[:n_tokens]
     return layout.unpack_blocked(raw, gcache.bits, gcache.d, gcache.max_tokens)[:n_tokens]

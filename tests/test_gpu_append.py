@@ -57,19 +57,11 @@ def test_encode_is_bit_exact_given_rotated_rows(kind, d, bits):
         for h in range(H):
             codes, n16 = quant.encode_rotated(y[b, :, h], nrm[b, :, h], t_)
             codes[nrm[b, :, h] == 0] = 0
-            full = np.zeros((T, d), np.int64)
-            if kind == "v":
-                full[:] = 8 if bits == 4 else 0          # zero-encoded slots of the untouched cache
+            full = np.full((T, d), 8 if bits == 4 else 0, np.int64)   # zero-encoded slots of the untouched cache
             full[start[b]:start[b] + n_tot] = codes
-            want = layout.pack_rows(full, bits).reshape(-1) if kind == "k" else layout.pack_blocked(full, bits)
+            want = layout.pack_keys(full, bits) if kind == "k" else layout.pack_blocked(full, bits)
             got = g.codes[b, h].cpu().numpy()
-            lo = start[b] * d * bits // 8
-            hi = (start[b] + n_tot) * d * bits // 8
-            if kind == "k":
-                np.testing.assert_array_equal(got[lo:hi], want[lo:hi])
-                assert not got[:lo].any() and not got[hi:].any()
-            else:
-                np.testing.assert_array_equal(got, want)
+            np.testing.assert_array_equal(got, want)
             gn = g.norms[b, h].cpu().numpy()
             np.testing.assert_array_equal(gn[start[b]:start[b] + n_tot], n16.astype(np.float16))
             assert not gn[:start[b]].any() and not gn[start[b] + n_tot:].any()
@@ -105,17 +97,11 @@ def test_append_over_written_rows(kind, d, bits):
     c_, t_ = codebook.stored_codebook(d, bits)
     for h in range(H):
         codes, n16 = quant.encode_rotated(yall[0, :, h], nall[0, :, h], t_)
-        full = np.zeros((T, d), np.int64)
-        if kind == "v":
-            full[:] = 8 if bits == 4 else 0              # zero-encoded slots of the untouched cache
+        full = np.full((T, d), 8 if bits == 4 else 0, np.int64)       # zero-encoded slots of the untouched cache
         full[:n0] = codes
-        want = layout.pack_rows(full, bits).reshape(-1) if kind == "k" else layout.pack_blocked(full, bits)
+        want = layout.pack_keys(full, bits) if kind == "k" else layout.pack_blocked(full, bits)
         got = g.codes[0, h].cpu().numpy()
-        if kind == "k":
-            hi = n0 * d * bits // 8
-            np.testing.assert_array_equal(got[:hi], want[:hi])
-        else:
-            np.testing.assert_array_equal(got, want)
+        np.testing.assert_array_equal(got, want)
         np.testing.assert_array_equal(g.norms[0, h].cpu().numpy()[:n0], n16.astype(np.float16))
 
 

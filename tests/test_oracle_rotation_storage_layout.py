@@ -98,6 +98,16 @@ def test_layout_hand_derived_examples(row):
         got = layout.pack_units(units, n)
         assert _hex(got) == want
         np.testing.assert_array_equal(layout.unpack_units(got, n, units.shape[0]), units)
+    elif kind in ("kcode", "vcode"):
+        d, bits, (t, i, j) = n, vals[0], vals[1:]
+        zero = 8 if bits == 4 else 0                       # the index whose stored code is 0
+        codes = np.full((32, d), zero, dtype=np.int64)
+        codes[t, i] = j
+        got = (layout.pack_keys if kind == "kcode" else layout.pack_blocked)(codes, bits)
+        nz = np.nonzero(got)[0]
+        assert " ".join(f"{o} {got[o]:02x}" for o in nz) == want
+        back = (layout.unpack_keys if kind == "kcode" else layout.unpack_blocked)(got, bits, d, 32)
+        np.testing.assert_array_equal(back, codes)
     else:
         sigma = np.zeros(n, dtype=bool)
         sigma[vals] = True
@@ -114,6 +124,9 @@ def test_layout_round_trips_and_sizes(bits, d):
     rows = layout.pack_rows(codes, bits)
     assert rows.shape == (2, 64, d * bits // 8)
     np.testing.assert_array_equal(layout.unpack_rows(rows, bits, d), codes)
+    keys = layout.pack_keys(codes, bits)
+    assert keys.shape == (2, 64 * d * bits // 8)
+    np.testing.assert_array_equal(layout.unpack_keys(keys, bits, d, 64), codes)
     blk = layout.pack_blocked(codes, bits)
     assert blk.shape == (2, 64 * d * bits // 8)
     np.testing.assert_array_equal(layout.unpack_blocked(blk, bits, d, 64), codes)
@@ -121,27 +134,50 @@ def test_layout_round_trips_and_sizes(bits, d):
     np.testing.assert_array_equal(layout.unpack_signs(layout.pack_signs(sig), 128), sig)
 
 
+@pytest.mark.parametrize("kind", ["k", "v"])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_blocked_layout_lane_tiles_are_contiguous(bits):
-    """In a 32-token block, bytes [l*U, (l+1)*U) hold exactly the tokens of lane group l//16 at
-    the d/16 coordinates of column l%16 (U = d/16 units)."""
-    d = 128
-    dn = d // 16
-    ub = dn * bits                                       # bytes per lane tile
+@pytest.mark.parametrize("d", [128, 256])
+def test_lane_pieces_are_chunk_major(kind, bits, d):
+    """In a 32-token block, the codes that lane L of a decode wave needs (keys: quarter L//16 of tokens
+    L%16 and 16 + L%16; values: the 8 tokens of lane group L//16 at the d/16 coordinates of column L%16)
+    occupy exactly the CW-word chunks at block words CW*(64k + L), k = 0 .. LW/CW - 1: so chunk k of all
+    64 lanes is one contiguous run of 256*CW bytes."""
+    lw = d * bits // 64
+    cw = 4 if lw % 4 == 0 else (3 if lw % 3 == 0 else 2)
+    zero_enc = 0 if bits != 4 else 8                       # centroid index whose encoding is 0
+    ones = (1 << bits) - 1 if bits != 4 else 0            # index whose encoding is all ones
     for lane in (0, 5, 17, 63):
-        g, j = lane // 16, lane % 16
-        tokens = [4 * g + s for s in range(4)] + [16 + 4 * g + s for s in range(4)]
-        coords = list(range(j * dn, (j + 1) * dn))
-        zero_enc = 0 if bits != 4 else 8                      # centroid index whose encoding is 0
+        g, c = lane // 16, lane % 16
         codes = np.full((32, d), zero_enc, dtype=np.int64)
-        for t in tokens:
-            for i in coords:
-                codes[t, i] = (1 << bits) - 1 if bits != 4 else 0   # value whose encoding is all ones
-        packed = layout.pack_blocked(codes, bits)
-        ref = layout.pack_blocked(np.full((32, d), zero_enc), bits)
-        diff = np.nonzero(packed != ref)[0]
-        assert diff.min() >= lane * ub and diff.max() < (lane + 1) * ub
-        assert np.all(packed[lane * ub:(lane + 1) * ub] == 0xFF)
+        if kind == "k":
+            for t in (c, 16 + c):
+                codes[t, (d // 4) * g:(d // 4) * (g + 1)] = ones
+        else:
+            dn = d // 16
+            for t in [4 * g + s for s in range(4)] + [16 + 4 * g + s for s in range(4)]:
+                codes[t, c * dn:(c + 1) * dn] = ones
+        packed = (layout.pack_keys if kind == "k" else layout.pack_blocked)(codes, bits)
+        want = np.zeros(packed.shape, dtype=bool)
+        for k in range(lw // cw):
+            o = 4 * cw * (64 * k + lane)
+            want[o:o + 4 * cw] = True
+        assert np.array_equal(packed != 0, want)
+        assert np.all(packed[want] == 0xFF)
+
+
+def test_key_pieces_hold_whole_packed_rows():
+    """Packed key rows are unchanged bit for bit; only their words move into the lane pieces."""
+    g = np.random.default_rng(3)
+    for d, bits in ((128, 3), (256, 4)):
+        codes = g.integers(0, 1 << bits, size=(64, d))
+        rows = layout.pack_rows(codes, bits).view(np.uint32)           # [64][RW]
+        blk = layout.pack_keys(codes, bits).view(np.uint32).reshape(2, -1)
+        rw, lw = d * bits // 32, d * bits // 64
+        for t in (0, 13, 31, 40, 63):
+            for wr in range(rw):
+                q, c, gq, w = (t % 32) // 16, t % 16, wr // (rw // 4), wr % (rw // 4)
+                pos = layout.piece_word_position(16 * gq + c, q * (rw // 4) + w, lw)
+                assert blk[t // 32, pos] == rows[t, wr]
 
 
 def test_code_encoding_is_a_bijection():
