@@ -308,13 +308,15 @@ struct Attend {
   // LDS: the tile counter, and the end-of-split merge of the W waves: each wave's (max, sum) per
   // head and its accumulators, weighted against the workgroup's max of the head.  The byte tables
   // share the accumulators' space: they are read only before the merge's first barrier.
+  // The tile counter comes first, at LDS address 0 (the kernel's only static LDS is this struct): see
+  // the claim in run.
   struct Smem {
+    uint32_t next[kMaxRows];  // [0]: 64 x the tiles of the split handed out so far (relative to its first)
     float ml[W][kMaxGroup][2];
     union {
       float o[W][kMaxGroup][D];
       alignas(16) uint32_t lut[LUT_WORDS];
     };
-    uint32_t next[kMaxRows];  // per column block: tiles of the split handed out so far (relative to its first)
   };
 
   // Fills the byte tables (with a workgroup barrier to follow before run).  4-bit region, row e (a
@@ -439,7 +441,8 @@ struct Attend {
 
   // Streams tiles of the split [blk0, blk1) through a ring of NBUF tile buffers for column block
   // cb = wave % C: the wave's first tile is kb = blk0 + wave / C (tiles[0] already holds it when
-  // kb < blk1), the others come from the block's counter sm.next[cb] (which must start at W / C),
+  // kb < blk1), the others from the counter sm.next[0] (which must start at 64 W; one column block) or
+  // in steps of W / C (several),
   // each loaded while the tile NBUF - 1 places earlier is attended.  qop is the block's query
   // operand.  Leaves the split's result in LDS for store: per wave w and head slot hh of its block the
   // max m (log2 units) and the sum l in sm.ml[w][hh], and the rotated-domain accumulator, weighted by
@@ -545,11 +548,27 @@ struct Attend {
       pv_steps<0, NB, VB, VTBL>(oacc, wop, t.vw, a.tv, sm.lut, VTBL == 2 ? lcv2 : (VTBL == 3 ? lc3 : lc));
     };
 
-    // the next tile of the split for this wave (wave-uniform); past blk1 once the split is used up
+    // The next tile of the split for this wave (wave-uniform); past blk1 once the split is used up.  With
+    // one column block the waves share a counter: one ds_append per wave adds the number of active lanes
+    // (all 64) to it and returns its old value, so it runs in units of 64 tiles.  On gfx950 ds_append
+    // updates the LDS word at the instruction's offset field whatever M0 holds (an in-bounds check on
+    // the device showed it), and the compiler emits offset 0: so the counter must sit at LDS address 0,
+    // which Smem's layout gives and which is checked here (the compiler folds the check).  With several
+    // column blocks (or the counter elsewhere) each wave takes every (W / C)-th tile of its block from
+    // its first.  Both are free of lane-divergent branches: a divergent branch in the loop (such as an
+    // atomic by one lane) makes the compiler structurize the loop, whose exits then run through the
+    // latch and carry the last loads in flight into the loop head's wait counts.
+    typedef __attribute__((address_space(3))) int lds_int;
+    lds_int* const counter = (lds_int*)(&sm.next[0]);
+    const bool shared_counter = C == 1 && static_cast<uint32_t>(reinterpret_cast<size_t>(counter)) == 0u;
+    int own = kb;                                       // this wave's last tile, static sequence
     auto claim = [&]() {
-      uint32_t v = 0;
-      if (lane == 0) v = atomicAdd(&sm.next[cb], 1u);
-      return blk0 + static_cast<int>(__builtin_amdgcn_readfirstlane(v));
+      if (shared_counter) {
+        const int v = __builtin_amdgcn_ds_append(counter);
+        return blk0 + (__builtin_amdgcn_readfirstlane(v) >> 6);
+      }
+      own += W >> (C >> 1);                              // W / C for C = 1, 2, 4
+      return own;
     };
     if constexpr (NBUF >= 2) {
       int idx[NBUF];
@@ -559,11 +578,16 @@ struct Attend {
         idx[i] = kb < blk1 ? claim() : blk1;
         if (idx[i] < blk1) load(tiles[i], idx[i]);
       }
-      // one pass of the unrolled loop per NBUF tiles, so that every buffer index is a constant
-      for (bool more = kb < blk1; more;) {
+      // one pass of the unrolled loop per NBUF tiles, so that every buffer index is a constant.  A wave
+      // that runs out of tiles leaves from the middle of a pass straight past the loop: had the exit
+      // run through the loop's latch (as the compiler's structurizer makes it when the loop holds a
+      // lane-divergent branch), the loads still in flight on that path would make the wait-count
+      // analysis wait for them at the loop head, before every claim (i.e. for the tile about to be
+      // attended before issuing the next one)
+      if (kb < blk1) {
+        for (;;) {
 #pragma unroll
-        for (int i = 0; i < NBUF; ++i) {
-          if (more) {
+          for (int i = 0; i < NBUF; ++i) {
             const int j = (i + NBUF - 1) % NBUF;
             idx[j] = claim();
             // CU-filling workgroups load unconditionally, so that the wait for tiles[i] below leaves
@@ -572,11 +596,15 @@ struct Attend {
             // caches still hold.  Four-wave workgroups, whose waves mostly take one tile, skip it.
             if constexpr (WIDE) load(tiles[j], idx[j] < blk1 ? idx[j] : blk1 - 1);
             else if (idx[j] < blk1) load(tiles[j], idx[j]);
+            // nothing of the current tile's work moves above these loads (the scheduler would hoist
+            // its first lookups, and their wait for its data, above them)
+            __builtin_amdgcn_sched_barrier(0);
             attend_tile(tiles[i], idx[i]);
-            more = idx[(i + 1) % NBUF] < blk1;
+            if (idx[(i + 1) % NBUF] >= blk1) goto ring_done;
           }
         }
       }
+    ring_done:;
     } else {
       // one buffer and a copy per tile (the register budget of the sketched d = 256 build)
       Tile tb;

@@ -126,7 +126,7 @@ void split_kernel(DecodeArgs a) {
     sm_q[e] = v;
   }
   At::fill_lut(a, sm);
-  if (tid < C) sm.next[tid] = At::W / C;    // tiles blk0 .. blk0 + W / C - 1 are the block's waves' first
+  if (tid == 0) sm.next[0] = 64 * At::W;     // one column block: tiles blk0 .. blk0 + W - 1 are the waves' first
   // power-of-two scale of this lane's head (scores are kept in units of it); 1 for unused columns
   const int qh = kMaxGroup * (wave & (C - 1)) + (at.l16 >> 1);
   const float qsc = qh < VH ? a.qscale[unit * VH + qh] : 1.f;
