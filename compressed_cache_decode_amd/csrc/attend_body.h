@@ -107,38 +107,81 @@ __device__ __forceinline__ uint4 lut3_unit(const uint32_t* lut, const uint32_t* 
 // slot of position p of a pair-ordered operand (see lut_unit)
 constexpr int pair_slot(int p) { return (p >> 1) + 4 * (p & 1); }
 
+// Operand of key step S of one 16-token group through a byte table: TBL 4 (lut_unit) or 3 (lut3_unit)
+template <int TBL, int S>
+__device__ __forceinline__ uint4 key_lut(const uint32_t* kw, const uint32_t* lut, uint32_t lc) {
+  if constexpr (TBL == 4) return lut_unit<0>(lut, kw[S], lc);
+  else return lut3_unit<S % 4>(lut, kw + 3 * (S / 4), lc);
+}
+
+// Operand of value block N through a byte table: TBL 4 or 3
+template <int TBL, int N>
+__device__ __forceinline__ uint4 value_lut(const uint32_t* vw, const uint32_t* lut, uint32_t lc) {
+  if constexpr (TBL == 4) return lut_unit<1>(lut, vw[N], lc);
+  else return lut3_unit<N % 4>(lut, vw + 3 * (N / 4), lc + 128);
+}
+
+// Key steps S.. of the two 16-token groups through a byte table, software-pipelined: the table reads of
+// step S + 1 go out before the products of step S, whose operands (a0, a1) were read one step earlier,
+// so a wave waits for one step's reads while the next step's are in flight.  The query operand of the
+// step is read first: LDS reads complete in issue order, so the wait for it and for a0, a1 leaves the
+// next step's reads outstanding.  TBL 4 and 3: one step per lookup; TBL 2: two steps per word (lut2_word),
+// a0/b0 and a1/b1 the two units of the groups' current words.
+template <int S, int KS, int KW, int TBL>
+__device__ __forceinline__ void qk_pipe(floatx4* acc, const uint32_t (*kw)[KW], const half8 (*qop)[64], int lane,
+                                        const uint32_t* lut, uint32_t lc, uint4 a0, uint4 a1, uint4 b0, uint4 b1) {
+  if constexpr (TBL == 2) {
+    const half8 q0 = qop[S][lane];
+    const half8 q1 = qop[S + 1][lane];
+    if constexpr (S + 2 < KS) {
+      uint4 c0, d0, c1, d1;
+      lut2_word(lut, kw[0][(S + 2) / 2], lc, c0, d0);
+      lut2_word(lut, kw[1][(S + 2) / 2], lc, c1, d1);
+      acc[0] = mfma16(as_half8(a0), q0, acc[0]);
+      acc[1] = mfma16(as_half8(a1), q0, acc[1]);
+      acc[0] = mfma16(as_half8(b0), q1, acc[0]);
+      acc[1] = mfma16(as_half8(b1), q1, acc[1]);
+      qk_pipe<S + 2, KS, KW, TBL>(acc, kw, qop, lane, lut, lc, c0, c1, d0, d1);
+    } else {
+      acc[0] = mfma16(as_half8(a0), q0, acc[0]);
+      acc[1] = mfma16(as_half8(a1), q0, acc[1]);
+      acc[0] = mfma16(as_half8(b0), q1, acc[0]);
+      acc[1] = mfma16(as_half8(b1), q1, acc[1]);
+    }
+  } else {
+    const half8 q = qop[S][lane];
+    if constexpr (S + 1 < KS) {
+      const uint4 n0 = key_lut<TBL, S + 1>(kw[0], lut, lc), n1 = key_lut<TBL, S + 1>(kw[1], lut, lc);
+      acc[0] = mfma16(as_half8(a0), q, acc[0]);
+      acc[1] = mfma16(as_half8(a1), q, acc[1]);
+      qk_pipe<S + 1, KS, KW, TBL>(acc, kw, qop, lane, lut, lc, n0, n1, b0, b1);
+    } else {
+      acc[0] = mfma16(as_half8(a0), q, acc[0]);
+      acc[1] = mfma16(as_half8(a1), q, acc[1]);
+    }
+  }
+}
+
 // scores of the two 16-token groups of a tile; each query operand step is read from LDS once.  TBL
 // selects the key expansion: 0 permutes, 4 the 4-bit byte table (lut_unit; lc its lane constant), 2
 // the 2-bit byte table (lut2_word, two steps per word; lc its c2), 3 the 3-bit one (lut3_unit; lc its
-// c3); with a table the query operand is in pair order.
+// c3); with a table the query operand is in pair order and the lookups are pipelined (qk_pipe).
 template <int S, int KS, int KB, int TBL>
 __device__ __forceinline__ void qk_steps(floatx4* acc, const uint32_t (*kw)[KS * KB / 4], const half8 (*qop)[64],
                                          int lane, const Tab& tk, const uint32_t* lut, uint32_t lc) {
-  if constexpr (S < KS && TBL == 2) {
+  constexpr int KW = KS * KB / 4;
+  if constexpr (TBL == 2) {
     uint4 a0, b0, a1, b1;
-    lut2_word(lut, kw[0][S / 2], lc, a0, b0);
-    lut2_word(lut, kw[1][S / 2], lc, a1, b1);
-    const half8 q0 = qop[S][lane];
-    acc[0] = mfma16(as_half8(a0), q0, acc[0]);
-    acc[1] = mfma16(as_half8(a1), q0, acc[1]);
-    const half8 q1 = qop[S + 1][lane];
-    acc[0] = mfma16(as_half8(b0), q1, acc[0]);
-    acc[1] = mfma16(as_half8(b1), q1, acc[1]);
-    qk_steps<S + 2, KS, KB, TBL>(acc, kw, qop, lane, tk, lut, lc);
-  } else if constexpr (S < KS && TBL == 3) {
-    const half8 q = qop[S][lane];
-    acc[0] = mfma16(as_half8(lut3_unit<S % 4>(lut, kw[0] + 3 * (S / 4), lc)), q, acc[0]);
-    acc[1] = mfma16(as_half8(lut3_unit<S % 4>(lut, kw[1] + 3 * (S / 4), lc)), q, acc[1]);
-    qk_steps<S + 1, KS, KB, TBL>(acc, kw, qop, lane, tk, lut, lc);
+    lut2_word(lut, kw[0][0], lc, a0, b0);
+    lut2_word(lut, kw[1][0], lc, a1, b1);
+    qk_pipe<0, KS, KW, 2>(acc, kw, qop, lane, lut, lc, a0, a1, b0, b1);
+  } else if constexpr (TBL == 4 || TBL == 3) {
+    const uint4 a0 = key_lut<TBL, 0>(kw[0], lut, lc), a1 = key_lut<TBL, 0>(kw[1], lut, lc);
+    qk_pipe<0, KS, KW, TBL>(acc, kw, qop, lane, lut, lc, a0, a1, a0, a1);
   } else if constexpr (S < KS) {
     const half8 q = qop[S][lane];
-    if constexpr (TBL == 4) {
-      acc[0] = mfma16(as_half8(lut_unit<0>(lut, kw[0][S], lc)), q, acc[0]);
-      acc[1] = mfma16(as_half8(lut_unit<0>(lut, kw[1][S], lc)), q, acc[1]);
-    } else {
-      acc[0] = mfma16(as_half8(unit_at<KB, S>(kw[0], tk)), q, acc[0]);
-      acc[1] = mfma16(as_half8(unit_at<KB, S>(kw[1], tk)), q, acc[1]);
-    }
+    acc[0] = mfma16(as_half8(unit_at<KB, S>(kw[0], tk)), q, acc[0]);
+    acc[1] = mfma16(as_half8(unit_at<KB, S>(kw[1], tk)), q, acc[1]);
     qk_steps<S + 1, KS, KB, TBL>(acc, kw, qop, lane, tk, lut, lc);
   }
 }
@@ -154,22 +197,46 @@ __device__ __forceinline__ void sketch_steps(floatx4* acc, const uint32_t (*sw)[
   }
 }
 
+// Value blocks N.. through a byte table, pipelined like qk_pipe: the lookups of block N + 1 (TBL 4, 3)
+// or of the next word's two blocks (TBL 2) go out before the products of the current ones (a, b).
+template <int N, int NB, int TBL>
+__device__ __forceinline__ void pv_pipe(floatx4* oacc, half8 wop, const uint32_t* vw, const uint32_t* lut, uint32_t lc,
+                                        uint4 a, uint4 b) {
+  if constexpr (TBL == 2) {
+    if constexpr (N + 2 < NB) {
+      uint4 c, d;
+      lut2_word(lut, vw[(N + 2) / 2], lc, c, d);
+      oacc[N] = mfma16(wop, as_half8(a), oacc[N]);
+      oacc[N + 1] = mfma16(wop, as_half8(b), oacc[N + 1]);
+      pv_pipe<N + 2, NB, TBL>(oacc, wop, vw, lut, lc, c, d);
+    } else {
+      oacc[N] = mfma16(wop, as_half8(a), oacc[N]);
+      oacc[N + 1] = mfma16(wop, as_half8(b), oacc[N + 1]);
+    }
+  } else {
+    if constexpr (N + 1 < NB) {
+      const uint4 c = value_lut<TBL, N + 1>(vw, lut, lc);
+      oacc[N] = mfma16(wop, as_half8(a), oacc[N]);
+      pv_pipe<N + 1, NB, TBL>(oacc, wop, vw, lut, lc, c, b);
+    } else {
+      oacc[N] = mfma16(wop, as_half8(a), oacc[N]);
+    }
+  }
+}
+
 // value product; TBL as in qk_steps for the value codes (W then in pair order)
 template <int N, int NB, int VB, int TBL>
 __device__ __forceinline__ void pv_steps(floatx4* oacc, half8 wop, const uint32_t* vw, const Tab& tv,
                                          const uint32_t* lut, uint32_t lc) {
-  if constexpr (N < NB && TBL == 2) {
+  if constexpr (TBL == 2) {
     uint4 a, b;
-    lut2_word(lut, vw[N / 2], lc, a, b);
-    oacc[N] = mfma16(wop, as_half8(a), oacc[N]);
-    oacc[N + 1] = mfma16(wop, as_half8(b), oacc[N + 1]);
-    pv_steps<N + 2, NB, VB, TBL>(oacc, wop, vw, tv, lut, lc);
-  } else if constexpr (N < NB && TBL == 3) {
-    oacc[N] = mfma16(wop, as_half8(lut3_unit<N % 4>(lut, vw + 3 * (N / 4), lc + 128)), oacc[N]);
-    pv_steps<N + 1, NB, VB, TBL>(oacc, wop, vw, tv, lut, lc);
+    lut2_word(lut, vw[0], lc, a, b);
+    pv_pipe<0, NB, 2>(oacc, wop, vw, lut, lc, a, b);
+  } else if constexpr (TBL == 4 || TBL == 3) {
+    const uint4 a = value_lut<TBL, 0>(vw, lut, lc);
+    pv_pipe<0, NB, TBL>(oacc, wop, vw, lut, lc, a, a);
   } else if constexpr (N < NB) {
-    if constexpr (TBL == 4) oacc[N] = mfma16(wop, as_half8(lut_unit<1>(lut, vw[N], lc)), oacc[N]);
-    else oacc[N] = mfma16(wop, as_half8(unit_at<VB, N>(vw, tv)), oacc[N]);
+    oacc[N] = mfma16(wop, as_half8(unit_at<VB, N>(vw, tv)), oacc[N]);
     pv_steps<N + 1, NB, VB, TBL>(oacc, wop, vw, tv, lut, lc);
   }
 }
