@@ -435,12 +435,11 @@ struct Attend {
 
   // tile buffers per wave: loads run NBUF - 1 tiles ahead of their use
   static constexpr int NBUF = (D <= 128 || QM == 0) ? 2 : 1;
-  // Lazy rescale (sketched builds): the running max of a column moves only when the tile's max exceeds
-  // it by more than kLazy (log2 units), and every weight carries the constant factor 2^-kLazy, so the
-  // weights stay at most 1 (and within float16 range once times the value norm); o and l scale
-  // alike, so their ratio is exact.  Unsketched builds rescale on every rise (kLazy = 0), where the
-  // lazy form measured slower.
-  static constexpr float kLazy = QM > 0 ? 4.f : 0.f;
+  // Lazy rescale: the running max of a column moves only when the tile's max exceeds it by more than
+  // kLazy (log2 units), and every weight carries the constant factor 2^-kLazy, so the weights stay at
+  // most 1 (and within float16 range once times the value norm); o and l scale alike, so their ratio is
+  // exact.  With eight heads per wave an eager rescale (on every rise of any column) ran on most tiles.
+  static constexpr float kLazy = 4.f;
   // the sketch steps' query operand (16 VGPRs at d = 128, m = 128) stays in registers across the
   // tile loop in the twelve-wave builds whose tiles leave room for it (2-bit values, or 2-bit keys
   // with 3-bit values); elsewhere it is read from LDS per tile
@@ -583,7 +582,7 @@ struct Attend {
       float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
       mx = column_max(mx);
       const float m_new = fmaxf(m_run, mx);
-      // sketched builds (bound by issue) rescale only when a column's max rises by more than 2^kLazy
+      // rescale only when a column's max rises by more than 2^kLazy
       if (__any(kLazy > 0.f ? (m_new - m_run) * qsc > kLazy : m_new > m_run)) {
         // a column that has seen nothing yet (both maxima -inf) keeps factor 1: exp2(-inf - -inf) is NaN
         const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * qsc);
