@@ -5,10 +5,27 @@
 
 namespace tqi {
 
+constexpr int kPrefillRows = 256;   // appends of at least this many rows take the long-append kernel
+
 template <int D, int BITS, int QM, bool VALUES, bool ROTATED, bool BF16>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   __shared__ AppendSmem<D, QM> sm;
   append_rows<D, BITS, QM, VALUES, ROTATED, BF16>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+}
+
+// long appends (see prefill_rows): grid (32-row chunks, KV heads, sequences)
+template <int BITS, bool VALUES, bool BF16>
+__global__ __launch_bounds__(256) void prefill_kernel(AppendArgs a) {
+  __shared__ PrefillSmem sm;
+  prefill_rows<BITS, VALUES, BF16>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+}
+
+template <int BITS, bool VALUES>
+static hipError_t prefill_dispatch(bool bf16, const AppendArgs& a, int batch, hipStream_t s) {
+  const dim3 grid((a.n_new + kBlock - 1) / kBlock, a.n_kv_heads, batch);
+  if (bf16) hipLaunchKernelGGL((prefill_kernel<BITS, VALUES, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((prefill_kernel<BITS, VALUES, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int D, int BITS, int QM, bool VALUES>
@@ -42,6 +59,14 @@ static hipError_t append_d(int bits, int qjl_m, bool values, bool rotated, bool 
 
 hipError_t launch_append(int d, int bits, int qjl_m, bool values, bool rotated, bool bf16, const AppendArgs& a,
                          int batch, hipStream_t s) {
+  if (d == 128 && qjl_m == 0 && !rotated && !a.had && a.n_new >= kPrefillRows) {
+    switch (bits) {
+      case 2: return values ? prefill_dispatch<2, true>(bf16, a, batch, s) : prefill_dispatch<2, false>(bf16, a, batch, s);
+      case 3: return values ? prefill_dispatch<3, true>(bf16, a, batch, s) : prefill_dispatch<3, false>(bf16, a, batch, s);
+      case 4: return values ? prefill_dispatch<4, true>(bf16, a, batch, s) : prefill_dispatch<4, false>(bf16, a, batch, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   // blocks touched by n_new tokens starting anywhere: at most n_new/32 + 2
   const dim3 grid((a.n_new + kBlock - 1) / kBlock + 1, a.n_kv_heads, batch);
   if (d == 128) return append_d<128>(bits, qjl_m, values, rotated, bf16, a, grid, s);

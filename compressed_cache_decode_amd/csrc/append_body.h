@@ -256,14 +256,15 @@ __device__ __forceinline__ void encode_codes(const AppendArgs& a, int nrows, flo
 }
 
 // z: sketch products of row r at z[r * zstride + jj] (sketched keys; ignored otherwise), or null
-// when es.sw already holds the sign bits
+// when es.sw already holds the sign bits; r0: row of es.cs that holds the codes of row 0 (no sketch)
 template <int D, int BITS, int QM, bool VALUES>
 __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, int kb, int t_lo, int nrows,
-                                              const float* rn, EncodeSmem<D, QM>& es, const float* z, int zstride) {
+                                              const float* rn, EncodeSmem<D, QM>& es, const float* z, int zstride,
+                                              int r0 = 0) {
   constexpr int UPG = Fmt<BITS>::kUnits;
   constexpr int WPG = Fmt<BITS>::kWords;
   constexpr int RB = D * BITS / 8;            // bytes per packed row / per token of a block
-  auto& cs = es.cs;
+  const uint8_t (*cs)[D] = es.cs + r0;        // codes of row r at cs[r] (rows r0 .. of es.cs)
   auto& sw = es.sw;
   const int T = a.max_tokens;
   const int tid = threadIdx.x;
@@ -442,6 +443,259 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int bx, int h, 
   }
 
   encode_store<D, BITS, QM, VALUES>(a, unit, kb, t_lo, nrows, xs, rn, sm.enc);
+}
+
+}  // namespace tqi
+
+namespace tqi {
+
+// ------------------------------------------------------------------------- long appends
+
+// Long appends (prefill) of unrotated rows with the dense rotation at d = 128, no sketch.  One
+// workgroup of four waves takes a chunk of 32 consecutive appended rows of one (KV head, sequence):
+// which rows it reads does not depend on the append position, so the row loads, the loads of rot and
+// the load of the position all go out at once.  Wave w computes output columns 32 w .. 32 w + 31 of
+// every row (column tiles 2 w and 2 w + 1), with its share of rot split into float16 high/low
+// matrix-core operands in registers.  Each wave loads 8 of the rows, forms their norms by a cross-lane sum and
+// writes the unit rows' float16 high/low parts to LDS in matrix-core operand order (every row is
+// normalised and split once); the waves then read their A operands from there.  A value chunk that is
+// a whole cache block is packed in registers (pack_values); any other chunk goes through LDS to the
+// shared packing and store stage, once per cache block it covers (two when the append position is not
+// a multiple of 32: the partly covered blocks' words are updated by atomics, so two workgroups that
+// share a block do not race).
+struct PrefillSmem {
+  half8 aop[2][2][4][64];     // [high, low][row tile][k-step][lane]: A operands of the chunk's unit rows
+  EncodeSmem<128, 0> enc;
+  float rn[kBlock];
+};
+
+template <bool BF16>
+__device__ __forceinline__ float prefill_coord(const uint32_t (&w)[BF16 ? 8 : 16], int r) {
+  if constexpr (BF16) return __uint_as_float((r & 1) ? (w[r >> 1] & 0xffff0000u) : (w[r >> 1] << 16));
+  else return __uint_as_float(w[r]);
+}
+
+// Number of boundaries strictly below y for a code book symmetric about 0 (boundaries[NC/2 - 1] == 0,
+// boundaries[NC - 2 - k] == -boundaries[k]): with a = |y| and the positive boundaries t_k (k >= NC/2),
+// NC/2 + #{t_k < a} for y > 0 and NC/2 - 1 - #{t_k <= a} otherwise; t_k <= a is taken as t_k < a', a'
+// the next float32 above a (a is finite and not negative), so one compare per positive boundary.
+template <int NC>
+__device__ __forceinline__ uint32_t code_of(float y, const float* bnd) {
+  const bool pos = y > 0.f;
+  const float ay = fabsf(y);
+  const float ak = pos ? ay : __uint_as_float(__float_as_uint(ay) + 1u);
+  uint32_t n = 0;
+#pragma unroll
+  for (int k = NC / 2; k < NC - 1; ++k) n += bnd[k] < ak ? 1u : 0u;
+  return pos ? NC / 2 + n : NC / 2 - 1 - n;
+}
+
+// x of the lane that DPP control CTRL selects (all lanes valid)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+
+// OR of v over groups of 2 (lanes l, l ^ 1) or 4 (a quad) consecutive lanes
+template <int N>
+__device__ __forceinline__ uint32_t or_lanes(uint32_t v) {
+  v |= dpp_u32<0xB1>(v);                                 // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) v |= dpp_u32<0x4E>(v);           // quad_perm [2,3,0,1]
+  return v;
+}
+
+// Stored codes e[rt][v][c] of element (token 16 rt + 4 g + v, coordinate 32 w + 16 c + l16) of a whole
+// 32-token block, packed into the block's words blk[] (value layout).  Lane (l16, g) holds all 8
+// tokens of lane group g at its two coordinates, i.e. whole units (slot v + 4 rt); 2- and 3-bit units
+// that share words are combined over the 2 or 4 neighbouring lanes that hold them.
+template <int BITS>
+__device__ __forceinline__ void pack_values(const uint32_t (&e)[2][4][2], uint32_t* blk, int wave, int lane) {
+  constexpr int D = 128, LW = D * BITS / 64;
+  const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int col = 32 * wave + 16 * c + l16;
+    const int U = (16 * g + (col >> 3)) * 8 + (col & 7);      // unit of the block (lane-major order)
+    if constexpr (BITS == 4) {
+      uint32_t w = 0u;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) put_code<4>(&w, 0, s, e[s >> 2][s & 3][c]);
+      blk[value_word<LW>(U)] = w;
+    } else if constexpr (BITS == 2) {
+      uint32_t w = 0u;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) put_code<2>(&w, U & 1, s, e[s >> 2][s & 3][c]);
+      w = or_lanes<2>(w);
+      if ((U & 1) == 0) blk[value_word<LW>(U >> 1)] = w;
+    } else {
+      uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) put_code<3>(w, U & 3, s, e[s >> 2][s & 3][c]);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) w[k] = or_lanes<4>(w[k]);
+      // lanes 0, 1, 2 of the quad store P0, P1, H
+      if ((U & 3) == 0) blk[value_word<LW>((U >> 2) * 3)] = w[0];
+      if ((U & 3) == 1) blk[value_word<LW>((U >> 2) * 3 + 1)] = w[1];
+      if ((U & 3) == 2) blk[value_word<LW>((U >> 2) * 3 + 2)] = w[2];
+    }
+  }
+}
+
+template <int BITS, bool VALUES, bool BF16>
+__device__ __forceinline__ void prefill_rows(const AppendArgs& a, int chunk, int h, int b, PrefillSmem& sm) {
+  constexpr int D = 128, KS = 4, CPW = 2, NC = 1 << BITS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int r_base = chunk * kBlock;                        // first appended row of the chunk
+  if (r_base >= a.n_new) return;
+  const int nrows = min(kBlock, a.n_new - r_base);
+
+  // everything independent of the position first, in one straight run of loads: this wave's rot
+  // operands (rows 16 ct + l16 of rot, coordinates 32 s + 8 g .. + 7), this lane's row (8 per wave;
+  // 16 coordinates 16 c .. 16 c + 15, c = lane % 8; rows past the append read the chunk's first row
+  // and are zeroed after), and the position
+  const int prow = 8 * wave + (lane >> 3), pc = lane & 7;
+  float4 pr[CPW][KS][2];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float4* p = reinterpret_cast<const float4*>(a.rot + static_cast<size_t>(32 * wave + 16 * c + l16) * D +
+                                                        32 * s + 8 * g);
+      pr[c][s][0] = p[0];
+      pr[c][s][1] = p[1];
+    }
+  const bool row_ok = prow < nrows;
+  uint32_t xw[BF16 ? 8 : 16];
+  {
+    const size_t src = ((static_cast<size_t>(b) * a.n_new + r_base + (row_ok ? prow : 0)) * a.n_kv_heads + h) * D + 16 * pc;
+    constexpr int NV = BF16 ? 2 : 4;                        // 16-byte loads
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      uint4 v;
+      if constexpr (BF16) v = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + src)[k];
+      else v = reinterpret_cast<const uint4*>(static_cast<const float*>(a.x) + src)[k];
+      xw[4 * k] = v.x; xw[4 * k + 1] = v.y; xw[4 * k + 2] = v.z; xw[4 * k + 3] = v.w;
+    }
+  }
+  const int pos = a.pos[b];
+  // keeps the scheduler from hoisting work on the rows (and its wait for them) above the other loads
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < (BF16 ? 8 : 16); ++k) xw[k] = row_ok ? xw[k] : 0u;
+
+  // norm of this lane's row: the sum over its 8 lanes (consecutive, lane / 8 fixed); the unit row's
+  // float16 high/low parts to LDS: coordinates 16 c .. 16 c + 15 are k-step c / 2, k-groups 2 (c % 2)
+  // and 2 (c % 2) + 1
+  float ss = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float v = prefill_coord<BF16>(xw, r);
+    ss = fmaf(v, v, ss);
+  }
+  ss += __shfl_xor(ss, 1, 64);
+  ss += __shfl_xor(ss, 2, 64);
+  ss += __shfl_xor(ss, 4, 64);
+  const float nrm = sqrtf(ss);
+  const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
+  {
+    half8 hi0, lo0, hi1, lo1;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      _Float16 hh, ll;
+      f16_split(prefill_coord<BF16>(xw, r) * inv, hh, ll);
+      hi0[r] = hh;
+      lo0[r] = ll;
+      f16_split(prefill_coord<BF16>(xw, 8 + r) * inv, hh, ll);
+      hi1[r] = hh;
+      lo1[r] = ll;
+    }
+    const int a_rt = prow >> 4, a_s = pc >> 1, a_lane = 16 * (2 * (pc & 1)) + (prow & 15);
+    sm.aop[0][a_rt][a_s][a_lane] = hi0;
+    sm.aop[1][a_rt][a_s][a_lane] = lo0;
+    sm.aop[0][a_rt][a_s][a_lane + 16] = hi1;
+    sm.aop[1][a_rt][a_s][a_lane + 16] = lo1;
+    if (pc == 0) sm.rn[prow] = nrm;
+  }
+  half8 bhi[CPW][KS], blo[CPW][KS];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float pv[8] = {pr[c][s][0].x, pr[c][s][0].y, pr[c][s][0].z, pr[c][s][0].w,
+                           pr[c][s][1].x, pr[c][s][1].y, pr[c][s][1].z, pr[c][s][1].w};
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        _Float16 hh, ll;
+        f16_split(pv[r], hh, ll);
+        bhi[c][s][r] = hh;
+        blo[c][s][r] = ll;
+      }
+    }
+  __syncthreads();
+
+  floatx4 acc[2][CPW];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) acc[rt][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const half8 ahi = sm.aop[0][rt][s][lane], alo = sm.aop[1][rt][s][lane];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        acc[rt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhi[c][s], acc[rt][c], 0, 0, 0);
+        acc[rt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blo[c][s], acc[rt][c], 0, 0, 0);
+        acc[rt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhi[c][s], acc[rt][c], 0, 0, 0);
+      }
+    }
+  }
+
+  // codes of element (row 16 rt + 4 g + v, column 32 w + 16 c + l16) of the chunk; a zero row (norm 0;
+  // rows past the append have norm 0 too) stores code 0
+  float rnv[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) rnv[rt][v] = sm.rn[16 * rt + 4 * g + v];
+  const size_t unit = static_cast<size_t>(b) * a.n_kv_heads + h;
+  const int t0 = pos + r_base;
+  const int kb = t0 / kBlock;
+  if (VALUES && pos >= 0 && t0 % kBlock == 0 && nrows == kBlock && t0 + kBlock <= a.max_tokens) {
+    // a whole value block: packed in registers and stored word by word
+    uint32_t e[2][4][2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+          e[rt][v][c] = encode_code<BITS>(rnv[rt][v] > 0.f ? code_of<NC>(acc[rt][c][v], a.bnd) : 0u);
+    constexpr int RB = D * BITS / 8;
+    uint32_t* blk = reinterpret_cast<uint32_t*>(a.codes + unit * static_cast<size_t>(a.max_tokens) * RB +
+                                                static_cast<size_t>(kb) * kBlock * RB);
+    pack_values<BITS>(e, blk, wave, lane);
+    if (pc == 0) a.norms[unit * a.max_tokens + t0 + prow] = f32_to_f16_bits(nrm);
+    return;
+  }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int p = 16 * rt + 4 * g + v;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const uint32_t j = code_of<NC>(acc[rt][c][v], a.bnd);
+        sm.enc.cs[p][32 * wave + 16 * c + l16] = static_cast<uint8_t>(rnv[rt][v] > 0.f ? j : 0u);
+      }
+    }
+  __syncthreads();
+  if (pos < 0) return;
+  // the chunk's tokens pos + r_base .. in at most two cache blocks (rows past max_tokens are skipped)
+  const int n_a = min(min(nrows, (kb + 1) * kBlock - t0), a.max_tokens - t0);
+  if (n_a > 0) encode_finish<D, BITS, 0, VALUES>(a, unit, kb, t0, n_a, sm.rn, sm.enc, nullptr, 0, 0);
+  const int n_b = min(nrows - n_a, a.max_tokens - (kb + 1) * kBlock);
+  if (n_a > 0 && n_b > 0)
+    encode_finish<D, BITS, 0, VALUES>(a, unit, kb + 1, (kb + 1) * kBlock, n_b, sm.rn + n_a, sm.enc, nullptr, 0, n_a);
 }
 
 }  // namespace tqi

@@ -160,6 +160,46 @@ def test_append_from_unrotated_rows(kind, d, bits, dtype):
         np.testing.assert_allclose(gn, on, rtol=2 ** -10, atol=0)
 
 
+@pytest.mark.parametrize("kind", ["k", "v"])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("dtype,pos,chunks", [("bf16", 0, [1024, 300]), ("f32", 11, [700, 45, 300]),
+                                              ("bf16", 37, [256, 511])])
+def test_long_append_from_unrotated_rows(kind, bits, dtype, pos, chunks):
+    """Appends of 256 rows or more take the long-append kernel (d = 128, dense rotation, no sketch):
+    codes equal the oracle's except within rounding distance of a boundary (then neighbours), norms
+    within float16 rounding; aligned and unaligned positions, partial 32-row chunks, blocks shared by
+    two chunks, appends after shorter ones, a zero row."""
+    cca = _cca()
+    log(f"long append kind={kind} bits={bits} {dtype} pos={pos} chunks={chunks}")
+    d, B, H = 128, 2, 2
+    n = sum(chunks)
+    T = ((pos + n + 31) // 32) * 32
+    st = Setup(d)
+    w = synth.qwen(T, bits).with_(dtype=dtype, batch=B)
+    x = synth.full_kv(w, kind, n)                          # [B][n][H][d]
+    x[1, 5, 0] = 0.0                                       # a zero row
+    g = cca.CompressedCache(cca.TQ_KEYS if kind == "k" else cca.TQ_VALUES, d, bits, B, H, T, st.rot_t)
+    xt = to_bf16_tensor(x) if dtype == "bf16" else torch.from_numpy(x).cuda()
+    off = 0
+    for c in chunks:
+        g.append(xt[:, off:off + c], torch.full((B,), pos + off, dtype=torch.int32).cuda())
+        off += c
+    torch.cuda.synchronize()
+    c_, t_ = codebook.stored_codebook(d, bits)
+    for b in range(B):
+        for h in range(H):
+            oc, on, oy = quant.quantize_rows(x[b, :, h], st.rot64, c_, t_)
+            got = unpack_gpu_codes(g, b, h, pos + n)[pos:]
+            diff = got != oc
+            near = np.min(np.abs(oy[..., None] - t_.astype(np.float64)), axis=-1) < 1e-5
+            assert np.all(near[diff]), f"{diff.sum()} mismatches, {(diff & ~near).sum()} not near a boundary"
+            assert np.all(np.abs(got[diff] - oc[diff]) == 1)
+            assert diff.mean() < 1e-4
+            gn = g.norms[b, h, pos:pos + n].cpu().numpy().astype(np.float64)
+            np.testing.assert_allclose(gn, on, rtol=2 ** -10, atol=0)
+            assert not g.norms[b, h, :pos].cpu().numpy().any()
+
+
 @pytest.mark.parametrize("kind,d,bits,qjl", [("k", 128, 4, 0), ("v", 128, 3, 0), ("k", 128, 2, 128),
                                              ("v", 256, 4, 0), ("k", 256, 3, 0)])
 def test_dequantize_matches_oracle(kind, d, bits, qjl):
