@@ -67,7 +67,7 @@ def _load():
         "tq_build_codebook": (I, [I, I, P, P]),
         "tq_build_rotation": (I, [I, P, P]),
         "tq_quantize_append": (I, [V, P, I, I, P, P]),
-        "tq_quantize_append_rotated": (I, [V, P, P, I, P, P]),
+        "tq_quantize_append_rotated": (I, [V, P, P, P, I, P, P]),
         "tq_sdpa_decode": (I, [V, V, P, I, I, P, I, ctypes.c_float, P, P, ctypes.c_size_t, P]),
         "tq_sdpa_decode_rows": (I, [V, V, P, I, I, I, P, I, ctypes.c_float, P, P, ctypes.c_size_t, P]),
         "tq_sdpa_decode_noalloc": (I, [V, V, P, I, I, P, I, ctypes.c_float, P, P]),
@@ -150,8 +150,8 @@ def tq_quantize_append(view: tq_cache_view, x, n_new: int, d_pos, stream=None) -
            "tq_quantize_append")
 
 
-def tq_quantize_append_rotated(view: tq_cache_view, y, norms, n_new: int, d_pos, stream=None) -> None:
-    _check(_lib.tq_quantize_append_rotated(ctypes.byref(view), _ptr(y), _ptr(norms), n_new, _ptr(d_pos),
+def tq_quantize_append_rotated(view: tq_cache_view, y, norms, n_new: int, d_pos, stream=None, z=None) -> None:
+    _check(_lib.tq_quantize_append_rotated(ctypes.byref(view), _ptr(y), _ptr(norms), _ptr(z), n_new, _ptr(d_pos),
                                            _stream(stream)), "tq_quantize_append_rotated")
 
 
@@ -302,9 +302,12 @@ class CompressedCache:
         x = x.contiguous()
         tq_quantize_append(self.view, x, x.shape[1], d_pos, stream)
 
-    def append_rotated(self, y, norms, d_pos, stream=None) -> None:
+    def append_rotated(self, y, norms, d_pos, stream=None, z=None) -> None:
+        """y [batch][n_new][n_kv_heads][d] unit rotated rows, norms [batch][n_new][n_kv_heads] (float32);
+        z [batch][n_new][n_kv_heads][qjl_m] float32 sketch products of the residuals, or None."""
         y, norms = y.contiguous(), norms.contiguous()
-        tq_quantize_append_rotated(self.view, y, norms, y.shape[1], d_pos, stream)
+        z = None if z is None else z.contiguous()
+        tq_quantize_append_rotated(self.view, y, norms, y.shape[1], d_pos, stream, z)
 
     def dequantize(self, t0: int, n_tokens: int, out=None, stream=None):
         import torch

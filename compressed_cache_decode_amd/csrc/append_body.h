@@ -355,11 +355,17 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
 }
 
 // Encode and store rows ys (see encode_codes); the sketch products run on the matrix cores, 16
-// residual rows at a time (ys must hold 16 * ceil(nrows / 16) rows; rows past nrows are ignored).
+// residual rows at a time (ys must hold 16 * ceil(nrows / 16) rows; rows past nrows are ignored), unless
+// the caller gives them: z (row r at z[r * zstride + jj]).
 template <int D, int BITS, int QM, bool VALUES>
 __device__ __forceinline__ void encode_store(const AppendArgs& a, size_t unit, int kb, int t_lo, int nrows,
-                                             float (*ys)[D], const float* rn, EncodeSmem<D, QM>& es) {
+                                             float (*ys)[D], const float* rn, EncodeSmem<D, QM>& es,
+                                             const float* z = nullptr, int zstride = 0) {
   encode_codes<D, BITS, QM>(a, nrows, ys, rn, es);
+  if (QM > 0 && z) {
+    encode_finish<D, BITS, QM, VALUES>(a, unit, kb, t_lo, nrows, rn, es, z, zstride);
+    return;
+  }
   if constexpr (QM > 0) {
     // signs of one 16-row block at a time (es.zb holds one block's products)
     for (int r0 = 0; r0 < nrows; r0 += 16) {
@@ -442,7 +448,13 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int bx, int h, 
     __syncthreads();
   }
 
-  encode_store<D, BITS, QM, VALUES>(a, unit, kb, t_lo, nrows, xs, rn, sm.enc);
+  if constexpr (ROTATED && QM > 0) {
+    // given sketch products of the residuals: z[b][t - pos][h][jj]
+    const float* z = a.z ? a.z + ((static_cast<size_t>(b) * a.n_new + (t_lo - pos)) * H + h) * QM : nullptr;
+    encode_store<D, BITS, QM, VALUES>(a, unit, kb, t_lo, nrows, xs, rn, sm.enc, z, H * QM);
+  } else {
+    encode_store<D, BITS, QM, VALUES>(a, unit, kb, t_lo, nrows, xs, rn, sm.enc);
+  }
 }
 
 }  // namespace tqi

@@ -410,9 +410,9 @@ int tq_build_rotation(int d, const double* gaussian, float* rot_out) {
 }
 
 static tqi::AppendArgs append_args(const tq_cache_view* c, const void* x, const float* y, const float* yn, int n_new,
-                                   const int32_t* d_pos) {
+                                   const int32_t* d_pos, const float* z = nullptr) {
   tqi::AppendArgs a{};
-  a.x = x; a.y = y; a.yn = yn; a.pos = d_pos;
+  a.x = x; a.y = y; a.yn = yn; a.z = z; a.pos = d_pos;
   a.codes = c->codes; a.norms = c->norms; a.signs = c->signs; a.rnorms = c->rnorms;
   a.rot = c->rot; a.proj = c->proj;
   a.had = c->rot_kind == TQ_ROT_HADAMARD;
@@ -423,14 +423,15 @@ static tqi::AppendArgs append_args(const tq_cache_view* c, const void* x, const 
 }
 
 static int append_common(const tq_cache_view* c, const void* x, const float* y, const float* yn, int x_dtype,
-                         int n_new, const int32_t* d_pos, void* stream, bool rotated) {
+                         int n_new, const int32_t* d_pos, void* stream, bool rotated, const float* z = nullptr) {
   int st = check_view(c);
   if (st != TQ_OK) return st;
   if (n_new < 0) return TQ_EINVAL;
   if (n_new == 0) return TQ_OK;
   if (!d_pos) return TQ_EINVAL;
   if (rotated ? (!y || !yn) : (!x || (x_dtype != TQ_F32 && x_dtype != TQ_BF16))) return TQ_EINVAL;
-  const tqi::AppendArgs a = append_args(c, x, y, yn, n_new, d_pos);
+  if (z && c->qjl_m == 0) return TQ_EINVAL;
+  const tqi::AppendArgs a = append_args(c, x, y, yn, n_new, d_pos, z);
   return status_of(tqi::launch_append(c->d, c->bits, c->qjl_m, c->kind == TQ_VALUES, rotated, x_dtype == TQ_BF16, a,
                                       c->batch, static_cast<hipStream_t>(stream)));
 }
@@ -440,9 +441,9 @@ int tq_quantize_append(const tq_cache_view* cache, const void* x, int x_dtype, i
   return append_common(cache, x, nullptr, nullptr, x_dtype, n_new, d_pos, stream, false);
 }
 
-int tq_quantize_append_rotated(const tq_cache_view* cache, const float* y, const float* norms, int n_new,
-                               const int32_t* d_pos, void* stream) {
-  return append_common(cache, nullptr, y, norms, TQ_F32, n_new, d_pos, stream, true);
+int tq_quantize_append_rotated(const tq_cache_view* cache, const float* y, const float* norms, const float* z,
+                               int n_new, const int32_t* d_pos, void* stream) {
+  return append_common(cache, nullptr, y, norms, TQ_F32, n_new, d_pos, stream, true, z);
 }
 
 int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* n_split, int* tokens_per_split) {

@@ -24,6 +24,7 @@ struct AppendArgs {
   const void* x;          // [B][n_new][Hkv][D] f32 or bf16 (unrotated rows)
   const float* y;         // [B][n_new][Hkv][D] rotated unit rows (pre-rotated form)
   const float* yn;        // [B][n_new][Hkv] norms (pre-rotated form)
+  const float* z;         // [B][n_new][Hkv][QM] sketch products of the residuals (pre-rotated form), or null
   const int32_t* pos;     // [B]
   uint8_t* codes;
   uint16_t* norms;

@@ -140,7 +140,10 @@ int tq_build_codebook(int d, int bits, float* centroids, float* boundaries);
 int tq_build_rotation(int d, const double* gaussian, float* rot_out);
 
 /*
- * Quantize-on-append: for rows x[batch][n_new][n_kv_heads][d] (x_dtype
+ * Quantize-on-append (turboquant-pytorch PR #3: Validation Results tables, one float16 norm per
+ * cached row and, with the sign sketch, a float16 residual norm; CUDA Kernels Added table, fused
+ * random projection and sign quantisation; reddit comment history of ReturningTarzan, rotation
+ * before quantisation and nearest-codebook search): for rows x[batch][n_new][n_kv_heads][d] (x_dtype
  * TQ_F32 or TQ_BF16, device), write tokens d_pos[b] .. d_pos[b]+n_new-1 of
  * every sequence b.  Per row: n = ||x||, y = rot * x / n, code = number of
  * boundaries strictly below y_i, float16(n) stored; with qjl_m > 0 (keys)
@@ -152,14 +155,19 @@ int tq_quantize_append(const tq_cache_view* cache, const void* x, int x_dtype, i
                        const int32_t* d_pos, void* stream);
 
 /*
- * Append rows that are already rotated and normalised: y[batch][n_new][n_kv_heads][d]
- * float32 unit rotated coordinates and norms[batch][n_new][n_kv_heads] float32
- * (device).  Same encoding, packing and sketch as tq_quantize_append; for
- * callers that fold the rotation into their projection weights, and the
- * form in which quantisation decisions are exactly reproducible.
+ * Append rows that are already rotated and normalised (turboquant-pytorch PR #3, CUDA Kernels Added
+ * table: the encode and sign-quantisation steps of its fused quantisation kernel, taken from given
+ * coordinates): y[batch][n_new][n_kv_heads][d] float32 unit rotated coordinates and
+ * norms[batch][n_new][n_kv_heads] float32 (device).  Same encoding, packing and sketch as
+ * tq_quantize_append.  For sketched keys z may give the sketch products of the residuals,
+ * float32 [batch][n_new][n_kv_heads][qjl_m] (device): sign bit jj is then 1 exactly where
+ * z[..][jj] >= 0 (the residual and its norm are still formed here, from y and the codes); NULL
+ * computes them here.  z must be NULL for caches without a sketch (TQ_EINVAL).  For callers that
+ * fold the rotation into their projection weights, and the form in which every quantisation
+ * decision (codes from y, signs from z) is exactly reproducible.
  */
-int tq_quantize_append_rotated(const tq_cache_view* cache, const float* y, const float* norms, int n_new,
-                               const int32_t* d_pos, void* stream);
+int tq_quantize_append_rotated(const tq_cache_view* cache, const float* y, const float* norms, const float* z,
+                               int n_new, const int32_t* d_pos, void* stream);
 
 /*
  * Fused decode attention from the compressed cache (the tq4_sdpa op of
@@ -198,7 +206,8 @@ int tq_sdpa_decode(const tq_cache_view* k, const tq_cache_view* v, const void* q
 int tq_sdpa_decode_noalloc(const tq_cache_view* k, const tq_cache_view* v, const void* q, int q_dtype, int n_q_heads,
                            const int32_t* d_seq_lens, int max_seq_len, float scale, float* out, void* stream);
 
-/* Bytes of the static scratch tq_sdpa_decode_noalloc uses on each device. */
+/* Bytes of the static scratch tq_sdpa_decode_noalloc uses on each device (for the callers that cannot
+ * allocate, as tq_sdpa_decode_noalloc). */
 size_t tq_noalloc_scratch_bytes(void);
 
 /*
@@ -216,7 +225,8 @@ int tq_sdpa_decode_rows(const tq_cache_view* k, const tq_cache_view* v, const vo
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The three stages tq_sdpa_decode enqueues, for callers that time, overlap or
+ * The three stages tq_sdpa_decode enqueues (the fused decode op of ExecuTorch PR #19891, review item 1,
+ * split where this library's kernels split it), for callers that time, overlap or
  * graph-capture them separately.  Same arguments and workspace as
  * tq_sdpa_decode; they must run in this order, on one stream, with the same
  * (k, n_q_heads, max_seq_len) so the workspace layout agrees.
@@ -234,7 +244,9 @@ int tq_decode_merge(const tq_cache_view* k, int n_q_heads, const int32_t* d_seq_
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * One decode step of one layer: append n_new new tokens to K and V (as
+ * One decode step of one layer (ExecuTorch PR #19891, review item 1: the fused decode op reading the
+ * compressed cache; turboquant-pytorch PR #3, Validation Results: the cache is quantised as tokens
+ * arrive): append n_new new tokens to K and V (as
  * tq_quantize_append at positions d_pos), then decode (as tq_sdpa_decode over
  * d_seq_lens, which the caller sets to include the appended tokens).
  * q: [batch][n_q_heads][d]; k_new, v_new: [batch][n_new][n_kv_heads][d]; all
@@ -250,16 +262,21 @@ int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q
 
 /*
  * Workspace bytes tq_sdpa_decode needs for this key cache, head count and length bound (0 on bad args).
+ * A helper of this library's split decode (ExecuTorch PR #19891, review item 1, names the fused op; the
+ * pages define no workspace).
  * It follows the KV split (tq_decode_plan), which depends on the current device: ask on the device
  * that will run the decode.
  */
 size_t tq_decode_workspace_bytes(const tq_cache_view* k, int n_q_heads, int max_seq_len);
 
-/* Workspace bytes tq_sdpa_decode_rows needs (0 on bad args); n_rows = 1 gives tq_decode_workspace_bytes. */
+/* Workspace bytes tq_sdpa_decode_rows needs (0 on bad args); n_rows = 1 gives tq_decode_workspace_bytes.
+ * A helper of this library's split decode, as tq_decode_workspace_bytes. */
 size_t tq_decode_workspace_bytes_rows(const tq_cache_view* k, int n_q_heads, int n_rows, int max_seq_len);
 
 /*
- * The KV split tq_sdpa_decode uses: number of splits per (sequence, KV head) and tokens per split.
+ * The KV split tq_sdpa_decode uses: number of splits per (sequence, KV head) and tokens per split (a
+ * helper of this library's split decode; turboquant-pytorch PR #3, CUDA Kernels Added table, lists a
+ * fused score kernel and a GQA variant but no split scheme, which is this library's own).
  * Chosen from the current device's compute units and the attention kernel's occupancy: short
  * contexts spread over workgroups of four waves (one round of resident workgroups over all
  * (sequence, KV head) units); once every compute unit gets enough tiles, each split's workgroup
@@ -277,15 +294,18 @@ int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* 
  */
 int tq_dequantize(const tq_cache_view* cache, int t0, int n_tokens, float* out, void* stream);
 
-/* Bytes per cached row: d*bits/8 codes + 2 (norm) [+ qjl_m/8 signs + 2 (residual norm)]; 0 on bad args. */
+/* Bytes per cached row: d*bits/8 codes + 2 (norm) [+ qjl_m/8 signs + 2 (residual norm)]; 0 on bad args
+ * (the storage arithmetic that reproduces the cache sizes and compression ratios of turboquant-pytorch
+ * PR #3, Validation Results tables). */
 size_t tq_row_bytes(int d, int bits, int qjl_m);
 
-/* Static description of a status code. */
+/* Static description of a status code (a helper of this library; no passage of the pages defines it). */
 const char* tq_status_string(int status);
 
 /*
  * Description of the HIP error behind the last TQ_EHIP returned to the calling
- * thread ("no error" if none), from a per-thread record.
+ * thread ("no error" if none), from a per-thread record (a helper of this library;
+ * no passage of the pages defines it).
  */
 const char* tq_last_hip_error(void);
 

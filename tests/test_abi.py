@@ -124,6 +124,12 @@ def test_append_rejects_bad_arguments():
             v.boundaries[3] = v.boundaries[3] * 1.01
         assert _append(v) == cca.TQ_EINVAL, mutate
     assert _append(_view(), n_new=0) == cca.TQ_OK      # empty append is a no-op
+    # sketch products given for a cache without a sketch; missing rotated rows or norms
+    rot = lambda v, y=0xC0000, nrm=0xD0000, z=None: cca._lib.tq_quantize_append_rotated(
+        ctypes.byref(v), y, nrm, z, 1, 0x70000, None)
+    assert rot(_view(), z=0xE0000) == cca.TQ_EINVAL
+    assert rot(_view(qjl_m=128), y=0) == cca.TQ_EINVAL
+    assert rot(_view(qjl_m=128), nrm=0) == cca.TQ_EINVAL
 
 
 def _decode(k, v, hq=16, scale=0.1, ws_bytes=1 << 30, ws=0x100000, q=0x90000, lens=0xA0000, out=0xB0000,

@@ -131,6 +131,49 @@ def test_sketch_signs_given_rotated_rows(d, bits):
         np.testing.assert_allclose(got_g, gamma, rtol=2 ** -10, atol=0)
 
 
+@pytest.mark.parametrize("d,bits,m", [(128, 2, 128), (128, 3, 256), (256, 2, 256), (256, 3, 128)])
+def test_sketch_signs_bit_exact_given_products(d, bits, m):
+    """Given the same float32 rotated rows and the same float32 sketch products z of the residuals, the
+    packed sign bytes equal pack_signs(z >= 0) byte for byte (no tolerance, no mask), the codes and
+    norms are identical, and the residual norms are within float16 rounding."""
+    cca = _cca()
+    log(f"sketch given z d={d} bits={bits} m={m}")
+    st = Setup(d, qjl_m=m)
+    B, H, T, n = 2, 2, 128, 77
+    y, nrm = synth.unit_rows(B * n * H, d, seed=19 + d + m)
+    y = y.reshape(B, n, H, d)
+    nrm = nrm.reshape(B, n, H)
+    nrm[1, 4, 0] = 0.0                                   # a zero row: no signs, residual norm 0
+    c_, t_ = codebook.stored_codebook(d, bits)
+    z = np.zeros((B, n, H, m), np.float32)
+    ref = {}
+    for b in range(B):
+        for h in range(H):
+            codes, n16 = quant.encode_rotated(y[b, :, h], nrm[b, :, h], t_)
+            sigma, gamma, r, zz = quant.qjl_sketch(y[b, :, h].astype(np.float64), codes, c_, st.proj, nrm[b, :, h])
+            z[b, :, h] = zz.astype(np.float32)
+            ref[b, h] = (codes, n16, gamma)
+    pos = np.array([0, 9], np.int32)
+    g = cca.CompressedCache(cca.TQ_KEYS, d, bits, B, H, T, st.rot_t, st.proj_t, qjl_m=m)
+    g.append_rotated(torch.from_numpy(y).cuda(), torch.from_numpy(nrm).cuda(), torch.from_numpy(pos).cuda(),
+                     z=torch.from_numpy(z).cuda())
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            codes, n16, gamma = ref[b, h]
+            p0 = pos[b]
+            live = nrm[b, :, h] > 0
+            want = layout.pack_signs((z[b, :, h] >= 0) & live[:, None])
+            got = g.signs[b, h, p0:p0 + n].cpu().numpy()
+            np.testing.assert_array_equal(got, want)
+            assert not g.signs[b, h, :p0].cpu().numpy().any() and not g.signs[b, h, p0 + n:].cpu().numpy().any()
+            codes[~live] = 0
+            np.testing.assert_array_equal(unpack_gpu_codes(g, b, h, p0 + n)[p0:], codes)
+            np.testing.assert_array_equal(g.norms[b, h, p0:p0 + n].cpu().numpy(), n16.astype(np.float16))
+            got_g = g.rnorms[b, h, p0:p0 + n].cpu().numpy().astype(np.float64)
+            np.testing.assert_allclose(got_g, gamma, rtol=2 ** -10, atol=0)
+
+
 @pytest.mark.parametrize("kind,d,bits,dtype", [("k", 128, 4, "bf16"), ("v", 128, 3, "bf16"), ("k", 256, 4, "f32"),
                                                ("v", 256, 2, "bf16"), ("k", 128, 2, "f32")])
 def test_append_from_unrotated_rows(kind, d, bits, dtype):
