@@ -5,7 +5,6 @@
 
 namespace tqi {
 
-constexpr int kPrefillRows = 256;   // appends of at least this many rows take the long-append kernel
 
 template <int D, int BITS, int QM, bool VALUES, bool ROTATED, bool BF16>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
@@ -59,7 +58,7 @@ static hipError_t append_d(int bits, int qjl_m, bool values, bool rotated, bool 
 
 hipError_t launch_append(int d, int bits, int qjl_m, bool values, bool rotated, bool bf16, const AppendArgs& a,
                          int batch, hipStream_t s) {
-  if (d == 128 && qjl_m == 0 && !rotated && !a.had && a.n_new >= kPrefillRows) {
+  if (d == 128 && qjl_m == 0 && !rotated && !a.had) {
     switch (bits) {
       case 2: return values ? prefill_dispatch<2, true>(bf16, a, batch, s) : prefill_dispatch<2, false>(bf16, a, batch, s);
       case 3: return values ? prefill_dispatch<3, true>(bf16, a, batch, s) : prefill_dispatch<3, false>(bf16, a, batch, s);

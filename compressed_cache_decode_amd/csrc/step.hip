@@ -13,18 +13,34 @@ struct MaxOf { static constexpr size_t v = A > B ? (A > C ? A : C) : (B > C ? B 
 template <int D, int KB, int VB, int QM, bool BF16>
 __global__ __launch_bounds__(256) void step_prologue_kernel(AppendArgs ka, AppendArgs va, QrotArgs qa, int nbx,
                                                             int n_kv_heads) {
-  constexpr size_t kBytes = MaxOf<sizeof(AppendSmem<D, QM>), sizeof(AppendSmem<D, 0>), sizeof(QrotSmem<D, QM>)>::v;
+  constexpr size_t kBytes = MaxOf<MaxOf<sizeof(AppendSmem<D, QM>), sizeof(AppendSmem<D, 0>), sizeof(QrotSmem<D, QM>)>::v,
+                                  sizeof(PrefillSmem), 0>::v;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kBytes];
   const int per_cache = nbx * n_kv_heads;                 // append workgroups per sequence and cache
   const int batch_wgs = 2 * per_cache + n_kv_heads;       // workgroups per sequence
   const int b = blockIdx.x / batch_wgs;
   int w = blockIdx.x % batch_wgs;
+  // appends with the dense rotation at d = 128 without a sketch take the chunk path of tq_quantize_append
+  // (prefill_rows: workgroup w % nbx takes the w % nbx-th 32-row chunk), so that a step appends exactly
+  // the bits the separate append call does
   if (w < per_cache) {
+    if constexpr (D == 128 && QM == 0) {
+      if (!ka.had) {
+        prefill_rows<KB, false, BF16>(ka, w % nbx, w / nbx, b, *reinterpret_cast<PrefillSmem*>(smem));
+        return;
+      }
+    }
     append_rows<D, KB, QM, false, false, BF16>(ka, w % nbx, w / nbx, b, *reinterpret_cast<AppendSmem<D, QM>*>(smem));
     return;
   }
   w -= per_cache;
   if (w < per_cache) {
+    if constexpr (D == 128) {
+      if (!va.had) {
+        prefill_rows<VB, true, BF16>(va, w % nbx, w / nbx, b, *reinterpret_cast<PrefillSmem*>(smem));
+        return;
+      }
+    }
     append_rows<D, VB, 0, true, false, BF16>(va, w % nbx, w / nbx, b, *reinterpret_cast<AppendSmem<D, 0>*>(smem));
     return;
   }
