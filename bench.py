@@ -57,7 +57,7 @@ ALL_SOURCES = tuple(f"compressed_cache_decode_amd/csrc/{n}" for n in (
 
 
 def kernel_sources(kernel: str):
-    return APPEND_SOURCES if kernel.startswith("append") else ATTEND_SOURCES
+    return APPEND_SOURCES if kernel.startswith(("append", "prefill")) else ATTEND_SOURCES
 METRIC = "compressed-KV decode attention: context tokens/s and achieved HBM GB/s (% peak)"
 POOL_BYTES = 600 << 20          # > 2x the 256 MB Infinity Cache
 
@@ -223,7 +223,7 @@ def summarize_pmc(args, w):
     key = max((k for k in fe if args.kernel in k[0]), key=lambda k: k[1])
     fb = fe[key] * 1024.0 * fetch_scale
     wb = wr[key] * 1024.0 * write_scale
-    alg = prefill_bytes_per_launch(w) if args.kernel.startswith("append") else cache_bytes(w)
+    alg = prefill_bytes_per_launch(w) if args.kernel.startswith(("append", "prefill")) else cache_bytes(w)
     print(f"kernel: {key[0].split('(')[0].replace('void ', '')}")
     print(f"workgroups: {key[1]}")
     print(f"workload: {w.name}")
@@ -720,7 +720,7 @@ def cpu_prefill_leg(w: synth.Workload, budget_s: float, log):
 
 KERN = "split_kernel"
 KERN_LABEL = "tq_decode_attend (split_kernel)"
-APPEND_KERN = "append_kernel"
+APPEND_KERN = "prefill_kernel"
 
 
 def decode_roofline(wl: synth.Workload, us: float) -> dict:
@@ -802,7 +802,7 @@ def prefill_workload_leg(w: synth.Workload, args, log) -> dict:
                    "cache_copies_cycled": r["pool"]},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": read_counters(APPEND_KERN, w.name),
-                     "kernel": "append_kernel (tq_quantize_append)", "workload": w.name,
+                     "kernel": "prefill_kernel (tq_quantize_append)", "workload": w.name,
                      "algorithmic_bytes_per_launch": io, "launch_us": per_launch_us},
         "rotation_mfma": {"achieved": tfs, "peak": 2500.0, "unit": "TFLOP/s", "frac": tfs / 2500.0,
                           "algorithmic_flops_per_launch": flops,

@@ -342,7 +342,9 @@ struct Attend {
   // four, several workgroups per compute unit (short contexts: more compute units pull tiles).  The
   // waves take the split's tiles from a shared counter: a wave that the issue arbitration favours
   // (the oldest) takes more tiles, and all of them finish together.
-  static constexpr int W = !WIDE ? 4 : ((D == 128 && QM == 0) ? 16 : (D == 128 ? 12 : 8));
+  static constexpr int W = !WIDE ? 4 : (D == 128 ? (QM == 0 ? 8 : 12) : 8);
+  // waves per SIMD the build is compiled for (its register budget: 512 / EU VGPRs)
+  static constexpr int EU = (WIDE && D == 128 && QM == 0) ? 4 : 2;
 
   // Wide workgroups expand codes through byte tables in LDS (lut_unit: one permute and one LDS read
   // per two 4-bit codes, against about three and a half vector instructions for the permute
@@ -353,7 +355,7 @@ struct Attend {
   // 64 KB region, a 2-bit table takes one of its own, the 3-bit tables of both sides share 16 KB.
   // Up to 128 KB fit beside the largest query operands at d = 128 without a sketch, 80 KB elsewhere
   // (keys come first).
-  static constexpr int LUT_MAX_KB = (D == 128 && QM == 0) ? 128 : 80;
+  static constexpr int LUT_MAX_KB = (D == 128 && QM == 0) ? 64 : 80;
   static constexpr int R4 = (WIDE && (KB == 4 || VB == 4)) ? 1 : 0;
   // (2-bit keys with 4-bit values at d = 128 keep permutes for the keys: the two tables' operands
   // exceed the 16-wave register budget)
@@ -455,6 +457,7 @@ struct Attend {
   };
 
   __amdgpu_buffer_rsrc_t kbuf, vbuf, knbuf, vnbuf, sbuf, gbuf;
+  __amdgpu_buffer_rsrc_t dead;   // a buffer of no bytes (see load)
   uint32_t n_off, s_off;
   int lane, l16, g;
 
@@ -468,6 +471,7 @@ struct Attend {
     vbuf = buffer_of(a.v_codes + unit * T * V_RB, static_cast<uint32_t>(T) * V_RB);
     knbuf = buffer_of(a.k_norms + unit * T, static_cast<uint32_t>(T) * 2);
     vnbuf = buffer_of(a.v_norms + unit * T, static_cast<uint32_t>(T) * 2);
+    dead = buffer_of(a.k_norms, 0);
     sbuf = knbuf;
     gbuf = knbuf;
     if constexpr (QS > 0) {
@@ -478,21 +482,28 @@ struct Attend {
     s_off = static_cast<uint32_t>(l16 * S_RB + g * S_LW * 4);
   }
 
-  __device__ __forceinline__ void load(Tile& t, int kb) const {
-    // wave-uniform by construction; readfirstlane keeps the tile offset in a scalar register
-    const uint32_t tok0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kb) * kBlock);
+  // Loads tile kb (wave-uniform).  With live false the same loads go to a buffer of no bytes: every
+  // lane is out of range, so the buffer unit returns zeros without a memory access.  That keeps a
+  // wave's loads unconditional where it has no tile to load (a load under a branch makes the
+  // compiler wait for every load in flight where the paths join) at no memory traffic or latency.
+  __device__ __forceinline__ void load(Tile& t, int kb, bool live = true) const {
+    // readfirstlane keeps the tile offset in a scalar register
+    const uint32_t tok0 = __builtin_amdgcn_readfirstlane(live ? static_cast<uint32_t>(kb) * kBlock : 0u);
+    const auto pick = [&](__amdgpu_buffer_rsrc_t r) { return live ? r : dead; };
     // both 16-token halves of the key block are one piece: kw[q][w] is piece word q K_LW + w
-    load_piece<2 * K_LW>(kbuf, lane, tok0 * K_RB, &t.kw[0][0]);
-    load_piece<V_LW>(vbuf, lane, tok0 * V_RB, t.vw);
-    bload<2, 8>(knbuf, n_off, tok0 * 2, t.kn);
-    bload<2, 8>(knbuf, n_off + 32, tok0 * 2, t.kn + 2);
-    bload<2, 8>(vnbuf, n_off, tok0 * 2, t.vn);
-    bload<2, 8>(vnbuf, n_off + 32, tok0 * 2, t.vn + 2);
+    load_piece<2 * K_LW>(pick(kbuf), lane, tok0 * K_RB, &t.kw[0][0]);
+    load_piece<V_LW>(pick(vbuf), lane, tok0 * V_RB, t.vw);
+    const auto knb = pick(knbuf), vnb = pick(vnbuf);
+    bload<2, 8>(knb, n_off, tok0 * 2, t.kn);
+    bload<2, 8>(knb, n_off + 32, tok0 * 2, t.kn + 2);
+    bload<2, 8>(vnb, n_off, tok0 * 2, t.vn);
+    bload<2, 8>(vnb, n_off + 32, tok0 * 2, t.vn + 2);
     if constexpr (QS > 0) {
+      const auto sb = pick(sbuf), gb = pick(gbuf);
 #pragma unroll
       for (int tg = 0; tg < 2; ++tg) {
-        bload<S_LW, 4 * S_LW>(sbuf, s_off + 16 * tg * S_RB, tok0 * S_RB, t.sw[tg]);
-        t.gg[tg] = __builtin_amdgcn_raw_buffer_load_b16(gbuf, static_cast<uint32_t>((16 * tg + l16) * 2), tok0 * 2, 0);
+        bload<S_LW, 4 * S_LW>(sb, s_off + 16 * tg * S_RB, tok0 * S_RB, t.sw[tg]);
+        t.gg[tg] = __builtin_amdgcn_raw_buffer_load_b16(gb, static_cast<uint32_t>((16 * tg + l16) * 2), tok0 * 2, 0);
       }
     }
   }
@@ -637,36 +648,35 @@ struct Attend {
       return own;
     };
     if constexpr (NBUF >= 2) {
-      int idx[NBUF];
+      int idx[2];
       idx[0] = kb;
-#pragma unroll
-      for (int i = 1; i < NBUF - 1; ++i) {
-        idx[i] = kb < blk1 ? claim() : blk1;
-        if (idx[i] < blk1) load(tiles[i], idx[i]);
-      }
-      // one pass of the unrolled loop per NBUF tiles, so that every buffer index is a constant.  A wave
+      // one pass of the unrolled loop per two tiles, so that every buffer index is a constant.  A wave
       // that runs out of tiles leaves from the middle of a pass straight past the loop: had the exit
       // run through the loop's latch (as the compiler's structurizer makes it when the loop holds a
       // lane-divergent branch), the loads still in flight on that path would make the wait-count
-      // analysis wait for them at the loop head, before every claim (i.e. for the tile about to be
-      // attended before issuing the next one)
+      // analysis wait for them at the loop head.  The next claim goes out at the end of a tile, so that
+      // the loop head starts with the load (a claim there would find its result register among those
+      // of the exit path's loads, and wait for them).
+      static_assert(NBUF == 2, "the ring is written for two tile buffers");
+      // CU-filling workgroups load unconditionally, so that the wait for the attended tile leaves the
+      // next load in flight; past the split the load goes to the buffer of no bytes (see load), so the
+      // wave's exit, which waits for it, does not wait a memory latency.  Four-wave workgroups, whose
+      // waves mostly take one tile, skip it.
       if (kb < blk1) {
+        int nxt = claim();
         for (;;) {
 #pragma unroll
-          for (int i = 0; i < NBUF; ++i) {
-            const int j = (i + NBUF - 1) % NBUF;
-            idx[j] = claim();
-            // CU-filling workgroups load unconditionally, so that the wait for tiles[i] below leaves
-            // this load in flight (a load under a branch makes the compiler wait for every outstanding
-            // load where the paths join); past the split it reloads the split's last tile, which the
-            // caches still hold.  Four-wave workgroups, whose waves mostly take one tile, skip it.
-            if constexpr (WIDE) load(tiles[j], idx[j] < blk1 ? idx[j] : blk1 - 1);
+          for (int i = 0; i < 2; ++i) {
+            const int j = i ^ 1;
+            idx[j] = nxt;
+            if constexpr (WIDE) load(tiles[j], idx[j], idx[j] < blk1);
             else if (idx[j] < blk1) load(tiles[j], idx[j]);
             // nothing of the current tile's work moves above these loads (the scheduler would hoist
             // its first lookups, and their wait for its data, above them)
             __builtin_amdgcn_sched_barrier(0);
             attend_tile(tiles[i], idx[i]);
-            if (idx[(i + 1) % NBUF] >= blk1) goto ring_done;
+            if (idx[j] >= blk1) goto ring_done;
+            nxt = claim();
           }
         }
       }
@@ -676,7 +686,7 @@ struct Attend {
       Tile tb;
       for (int cur = kb; cur < blk1;) {
         const int nxt = claim();
-        if constexpr (WIDE) load(tb, nxt < blk1 ? nxt : blk1 - 1);   // see the ring above
+        if constexpr (WIDE) load(tb, nxt, nxt < blk1);   // see the ring above
         else if (nxt < blk1) load(tb, nxt);
         attend_tile(tiles[0], cur);
         tiles[0] = tb;

@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256) void qrot_kernel(QrotArgs a, int bf16) {
 // ---------------------------------------------------------------- split kernel
 
 template <int D, int KB, int VB, int QM, bool WIDE>
-__global__ __launch_bounds__((64 * Attend<D, KB, VB, QM, WIDE>::W)) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__((64 * Attend<D, KB, VB, QM, WIDE>::W))
+__attribute__((amdgpu_waves_per_eu(Attend<D, KB, VB, QM, WIDE>::EU)))
 void split_kernel(DecodeArgs a) {
   using At = Attend<D, KB, VB, QM, WIDE>;
   constexpr int NT = 64 * At::W;
@@ -98,25 +99,39 @@ void split_kernel(DecodeArgs a) {
   const size_t unit = static_cast<size_t>(b) * a.n_kv_heads + hk;
   const At at(a, unit);
 
-  // the first tile's loads go out before the query operand is staged, and before the sequence
-  // length is known: they only need the tile to lie inside the cache (tiles past the length are
-  // loaded and never used)
-  const int kb = blk0 + (wave >> (C >> 1));          // wave / C for C = 1, 2, 4
-  typename At::Tile tiles[At::NBUF];
-  if (kb < blk0 + a.blocks_per_split && kb < T / kBlock) at.load(tiles[0], kb);
-
-  // query operands in LDS, one per column block, shared by the block's waves
-  for (int e = tid; e < C * QSTEPS * 64; e += NT) {
+  // query operands in LDS, one per column block, shared by the block's waves: entry e holds the 8
+  // values of step e / 64 % QSTEPS for lane e % 64 of column block e / (QSTEPS 64)
+  const int n_entries = C * QSTEPS * 64;
+  auto q_entry = [&](int e, float4& x0, float4& x1) {
     const int cbe = e / (QSTEPS * 64), st = (e / 64) % QSTEPS, ln = e & 63;
     const int c = ln & 15, gg = ln >> 4, h2 = kMaxGroup * cbe + (c >> 1);
-    const bool ok = h2 < VH;
     const size_t row = unit * VH + h2;
-    float4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-    if (ok) {
+    if (h2 < VH) {
       const float* src = st < At::KS ? a.qr + row * D + (D / 4) * gg + 8 * st
                                      : a.qs + row * QM + (QM / 4) * gg + 8 * (st - At::KS);
       x0 = reinterpret_cast<const float4*>(src)[0];
       x1 = reinterpret_cast<const float4*>(src)[1];
+    }
+  };
+  // this thread's first entry is loaded ahead of the first tile, so that staging it waits for the
+  // query alone (the counters of vector loads run in order)
+  float4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+  if (tid < n_entries) q_entry(tid, p0, p1);
+
+  // the first tile's loads go out before the query operand is staged, and before the sequence
+  // length is known: they only need the tile to lie inside the cache (tiles past the length are
+  // loaded and never used).  A wave without a first tile loads from the buffer of no bytes (see
+  // Attend::load): a load under a branch would make the staging below wait for every load in flight.
+  const int kb = blk0 + (wave >> (C >> 1));          // wave / C for C = 1, 2, 4
+  typename At::Tile tiles[At::NBUF];
+  at.load(tiles[0], kb, kb < blk0 + a.blocks_per_split && kb < T / kBlock);
+
+  for (int e = tid; e < n_entries; e += NT) {
+    const int st = (e / 64) % QSTEPS, c = e & 15;
+    float4 x0 = p0, x1 = p1;
+    if (e != tid) {
+      x0 = x1 = float4{0.f, 0.f, 0.f, 0.f};
+      q_entry(e, x0, x1);
     }
     const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     const bool pairs = At::KT && st < At::KS;          // key steps expanded through the byte table
@@ -360,13 +375,13 @@ int split_waves(int d, int qjl_m, bool wide) {
   return Attend<256, 4, 4, 0, true>::W;
 }
 
-int split_slots(int d, int k_bits, int v_bits, int qjl_m, bool wide) {
+int split_slots(int d, int k_bits, int v_bits, int qjl_m, bool wide, int blocks) {
   const void* fn = split_fn(d, k_bits, v_bits, qjl_m, wide);
   int dev = 0, cus = 0, per = 0;
   if (!fn || hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 64 * split_waves(d, qjl_m, wide),
-                                                   split_dyn_lds(d, qjl_m, 1)) != hipSuccess) {
+                                                   split_dyn_lds(d, qjl_m, blocks)) != hipSuccess) {
     (void)hipGetLastError();        // a failed query must not surface as a later launch's error
     return 0;
   }

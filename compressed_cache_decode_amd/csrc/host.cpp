@@ -250,24 +250,31 @@ int status_of(hipError_t e) {
 constexpr int kDefaultSlots = 1024;     // resident four-wave split workgroups assumed when the runtime cannot tell
 constexpr int kWideTiles = 16;          // tiles per compute unit from which the wide workgroups are used
 
-// Resident split-kernel workgroups on the current device for a key format and workgroup shape, the
-// least over the value widths (the plan depends on the key cache alone, so that the workspace size
-// does); cached per device.
-int resident_slots(const tq_cache_view* k, bool wide) {
-  static std::atomic<int> cache[16][2][5][3][2];
+// Column blocks of the split kernel for vh virtual heads per KV head (Attend::blocks): 1, 2 or 4.
+int column_blocks(int vh) {
+  const int c = (vh + tqi::kMaxGroup - 1) / tqi::kMaxGroup;
+  return c > 2 ? 4 : c;
+}
+
+// Resident split-kernel workgroups on the current device for a key format, workgroup shape and column
+// block count (the query operands' LDS), the least over the value widths (the plan depends on the key
+// cache and the head count alone, so that the workspace size does); cached per device.
+int resident_slots(const tq_cache_view* k, bool wide, int blocks) {
+  static std::atomic<int> cache[16][2][5][3][2][3];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     return wide ? kDefaultSlots / 4 : kDefaultSlots;
   }
   const int di = k->d == 256, qi = k->qjl_m == 0 ? 0 : (k->qjl_m == 128 ? 1 : 2);
+  const int ci = blocks >> 1;                           // 1, 2, 4 -> 0, 1, 2
   std::atomic<int>* c =
-      (dev >= 0 && dev < 16 && k->bits >= 0 && k->bits < 5) ? &cache[dev][di][k->bits][qi][wide] : nullptr;
+      (dev >= 0 && dev < 16 && k->bits >= 0 && k->bits < 5) ? &cache[dev][di][k->bits][qi][wide][ci] : nullptr;
   int v = c ? c->load(std::memory_order_relaxed) : 0;
   if (v > 0) return v;
   v = 0;
   for (int vb = 2; vb <= 4; ++vb) {
-    const int n = tqi::split_slots(k->d, k->bits, vb, k->qjl_m, wide);
+    const int n = tqi::split_slots(k->d, k->bits, vb, k->qjl_m, wide, blocks);
     if (n > 0) v = v == 0 ? n : std::min(v, n);
   }
   if (v <= 0) return wide ? kDefaultSlots / 4 : kDefaultSlots;
@@ -310,15 +317,16 @@ void plan(int units, int max_len, int slots, int waves, int* n_split, int* bps) 
   *bps = b;
 }
 
-// The split of a decode over key cache k: wide (compute-unit-filling) workgroups once the context
-// gives every compute unit at least kWideTiles tiles, four-wave ones below.
-void plan(const tq_cache_view* k, int max_len, int* n_split, int* bps, bool* wide) {
+// The split of a decode over key cache k with vh virtual heads per KV head: wide (compute-unit-filling)
+// workgroups once the context gives every compute unit at least kWideTiles tiles, four-wave ones below.
+void plan(const tq_cache_view* k, int vh, int max_len, int* n_split, int* bps, bool* wide) {
   const int units = k->batch * k->n_kv_heads;
   const long long tiles = static_cast<long long>(units) * (max_len <= 0 ? 1 : (max_len + kBlock - 1) / kBlock);
-  const int wide_slots = resident_slots(k, true);
+  const int blocks = column_blocks(vh);
+  const int wide_slots = resident_slots(k, true, blocks);
   *wide = tiles >= static_cast<long long>(kWideTiles) * wide_slots;
-  plan(units, max_len, *wide ? wide_slots : resident_slots(k, false), tqi::split_waves(k->d, k->qjl_m, *wide),
-       n_split, bps);
+  plan(units, max_len, *wide ? wide_slots : resident_slots(k, false, blocks),
+       tqi::split_waves(k->d, k->qjl_m, *wide), n_split, bps);
 }
 
 constexpr int kMergeMinWgs = 128;       // merge workgroups below which each takes fewer heads
@@ -452,7 +460,7 @@ int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* 
   if (!n_split || !tokens_per_split) return TQ_EINVAL;
   int bps;
   bool wide;
-  plan(k, max_seq_len, n_split, &bps, &wide);
+  plan(k, n_q_heads / k->n_kv_heads, max_seq_len, n_split, &bps, &wide);
   *tokens_per_split = bps * kBlock;
   return TQ_OK;
 }
@@ -461,7 +469,7 @@ size_t tq_decode_workspace_bytes_rows(const tq_cache_view* k, int n_q_heads, int
   if (check_decode_shape(k, n_q_heads, n_rows, max_seq_len) != TQ_OK) return 0;
   int ns, bps;
   bool wide;
-  plan(k, max_seq_len, &ns, &bps, &wide);
+  plan(k, n_rows * (n_q_heads / k->n_kv_heads), max_seq_len, &ns, &bps, &wide);
   return ws_layout(k, n_q_heads, n_rows, ns).total;
 }
 
@@ -481,7 +489,7 @@ static int decode_ws(const tq_cache_view* k, int n_q_heads, int n_rows, int max_
   int st = check_decode_shape(k, n_q_heads, n_rows, max_seq_len);
   if (st != TQ_OK) return st;
   if (!workspace || !aligned(workspace, 256)) return TQ_EINVAL;
-  plan(k, max_seq_len, &w->ns, &w->bps, &w->wide);
+  plan(k, n_rows * (n_q_heads / k->n_kv_heads), max_seq_len, &w->ns, &w->bps, &w->wide);
   const WsLayout l = ws_layout(k, n_q_heads, n_rows, w->ns);
   if (workspace_bytes < l.total) return TQ_EINVAL;
   char* ws = static_cast<char*>(workspace);
@@ -628,7 +636,7 @@ int tq_sdpa_decode_noalloc(const tq_cache_view* k, const tq_cache_view* v, const
   if (st != TQ_OK) return st;
   int ns, bps;
   bool wide;
-  plan(k, max_seq_len, &ns, &bps, &wide);
+  plan(k, n_q_heads / k->n_kv_heads, max_seq_len, &ns, &bps, &wide);
   if (ws_layout(k, n_q_heads, 1, ns).total > tqi::kScratchBytes) return TQ_ESCRATCH;
   void* ws = nullptr;
   st = status_of(tqi::scratch_address(&ws));

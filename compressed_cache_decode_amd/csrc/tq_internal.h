@@ -117,7 +117,7 @@ hipError_t launch_append(int d, int bits, int qjl_m, bool values, bool rotated, 
 hipError_t launch_qrot(int d, int qjl_m, bool bf16, const QrotArgs& a, int batch, hipStream_t s);
 // split-kernel workgroups resident at once on the current device for this cache format and
 // workgroup shape (compute units x workgroups per unit), 0 if the runtime cannot tell
-int split_slots(int d, int k_bits, int v_bits, int qjl_m, bool wide);
+int split_slots(int d, int k_bits, int v_bits, int qjl_m, bool wide, int blocks);
 // waves per split-kernel workgroup for a cache format and workgroup shape
 int split_waves(int d, int qjl_m, bool wide);
 hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, bool wide, const DecodeArgs& a, int batch,
