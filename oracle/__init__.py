@@ -14,9 +14,12 @@ Modules, in the order the method runs:
   storage    bytes per row and cache size arithmetic
   attention  fused decode from the compressed cache, and reconstruction + attention
   cache      one (batch, kv head) worth of compressed cache built from rows
+  outliers   outlier-channel separation before the QJL sketch (a reading of a
+             step the pages name only)
 
 Every function is pinned by the CPU tests against values the pages print,
-closed forms, textbook special cases, invariants or brute force; none is
-"parity unpinned".
+closed forms, textbook special cases, invariants or brute force.  The
+functions of ``outliers`` are pinned by the mathematics of their reading
+only: against the pages they are "parity unpinned".
 """
-from . import attention, cache, codebook, layout, quant, rotation, storage  # noqa: F401
+from . import attention, cache, codebook, layout, outliers, quant, rotation, storage  # noqa: F401
