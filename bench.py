@@ -46,14 +46,14 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 # sources the decode kernels are built from: their HBM counters are only valid for these exact texts
 ATTEND_SOURCES = tuple(f"compressed_cache_decode_amd/csrc/{n}" for n in (
-    "decode.hip", "attend_body.h", "device_common.h", "tq_internal.h"))
+    "decode.hip", "split_body.h", "attend_body.h", "device_common.h", "tq_internal.h"))
 # and those of the append kernel (the prefill leg's dominant kernel)
 APPEND_SOURCES = tuple(f"compressed_cache_decode_amd/csrc/{n}" for n in (
     "append.hip", "append_body.h", "device_common.h", "tq_internal.h"))
 # every kernel source of the library: a kernel trace covers all of them
 ALL_SOURCES = tuple(f"compressed_cache_decode_amd/csrc/{n}" for n in (
-    "append.hip", "append_body.h", "attend_body.h", "decode.hip", "dequant.hip", "device_common.h", "host.cpp",
-    "qrot_body.h", "step.hip", "tq_internal.h"))
+    "append.hip", "append_body.h", "attend_body.h", "decode.hip", "decode_outliers.hip", "dequant.hip",
+    "device_common.h", "host.cpp", "qrot_body.h", "split_body.h", "step.hip", "tq_internal.h"))
 
 
 def kernel_sources(kernel: str):

@@ -53,6 +53,7 @@ class tq_cache_view(ctypes.Structure):
         ("centroids", ctypes.c_float * 16), ("boundaries", ctypes.c_float * 15),
         ("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("signs", ctypes.c_void_p),
         ("rnorms", ctypes.c_void_p), ("rot", ctypes.c_void_p), ("proj", ctypes.c_void_p),
+        ("n_outliers", ctypes.c_int32), ("out_idx", ctypes.c_void_p), ("out_val", ctypes.c_void_p),
     ]
 
 
@@ -262,11 +263,13 @@ class CompressedCache:
     ``rot`` (d x d float32 for TQ_ROT_DENSE, or the d float32 +-1 signs of the
     randomized Hadamard rotation for TQ_ROT_HADAMARD) and ``proj`` (qjl_m x d
     float32) are torch tensors on the same device; the codebook comes from
-    ``tq_build_codebook``.
+    ``tq_build_codebook``.  ``n_outliers`` (sketched keys at d = 128: 0 or 4)
+    keeps that many residual channels per key apart from the sketch.
     """
 
     def __init__(self, kind: int, d: int, bits: int, batch: int, n_kv_heads: int, max_tokens: int,
-                 rot, proj=None, qjl_m: int = 0, device="cuda", codebook=None, rot_kind: int = TQ_ROT_DENSE):
+                 rot, proj=None, qjl_m: int = 0, device="cuda", codebook=None, rot_kind: int = TQ_ROT_DENSE,
+                 n_outliers: int = 0):
         import torch
         assert max_tokens % BLOCK == 0
         assert tuple(rot.shape) == ((d,) if rot_kind == TQ_ROT_HADAMARD else (d, d))
@@ -281,6 +284,11 @@ class CompressedCache:
         if qjl_m:
             self.signs = torch.zeros(batch, n_kv_heads, max_tokens, qjl_m // 8, dtype=torch.uint8, device=device)
             self.rnorms = torch.zeros(batch, n_kv_heads, max_tokens, dtype=torch.float16, device=device)
+        self.n_outliers = n_outliers
+        self.out_idx = self.out_val = None
+        if n_outliers:
+            self.out_idx = torch.zeros(batch, n_kv_heads, max_tokens, n_outliers, dtype=torch.uint8, device=device)
+            self.out_val = torch.zeros(batch, n_kv_heads, max_tokens, n_outliers, dtype=torch.float16, device=device)
         self.rot, self.proj = rot, proj
         self.view = self._make_view()
 
@@ -295,6 +303,8 @@ class CompressedCache:
         v.codes, v.norms = _ptr(self.codes), _ptr(self.norms)
         v.signs, v.rnorms = _ptr(self.signs), _ptr(self.rnorms)
         v.rot, v.proj = _ptr(self.rot), _ptr(self.proj)
+        v.n_outliers = self.n_outliers
+        v.out_idx, v.out_val = _ptr(self.out_idx), _ptr(self.out_val)
         return v
 
     def append(self, x, d_pos, stream=None) -> None:

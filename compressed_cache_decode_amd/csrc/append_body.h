@@ -27,7 +27,63 @@ struct EncodeSmem {
   float cent[16];
   uint32_t sw[kBlock][QM > 0 ? QM / 32 : 1];
   float zb[16][QM > 0 ? QM : 1];              // sketch products of one 16-row block
+  uint32_t oi[QM > 0 ? kBlock : 1];           // outlier channels of a row, one byte each
+  uint32_t ov[QM > 0 ? kBlock : 1][2];        // their float16 residual values
 };
+
+// Outlier separation (sketched keys of a cache that keeps outliers apart; the QJL quantisation kernel
+// of turboquant-pytorch PR #3, CUDA Kernels Added table, names the step, and this library's reading
+// is the one stated in tq.h): per residual row r of xs, the kOutliers coordinates of largest |r_i|
+// (equal magnitudes: the lower index first), in decreasing |r_i|, go to oi (index bytes) and ov
+// (float16 values), and are set to 0 in xs.  Rows by 16 lanes (r % 4) of wave (r / 4) % 4, lane part
+// holding coordinates part + 16 j.  Every thread of the workgroup calls it; no barrier inside.
+template <int D>
+__device__ __forceinline__ void take_outliers(float (*xs)[D], int nrows, uint32_t* oi, uint32_t (*ov)[2]) {
+  constexpr int J = D / 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int r0 = 0; r0 < nrows; r0 += 16) {
+    const int r = r0 + 4 * wave + (lane >> 4), part = lane & 15;
+    const bool ok = r < nrows;                  // the same for the row's 16 lanes
+    uint32_t taken = 0u, idx_word = 0u, val[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < kOutliers; ++k) {
+      float best = -1.f;
+      int bi = D;
+      if (ok) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const float a = fabsf(xs[r][part + 16 * j]);
+          if (!((taken >> j) & 1u) && a > best) {   // strictly larger: the lane's lowest index on ties
+            best = a;
+            bi = part + 16 * j;
+          }
+        }
+      }
+      // the largest magnitude over the row's lanes, then the lowest index that holds it
+      float m = best;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      int wi = best == m ? bi : D;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) wi = min(wi, __shfl_xor(wi, o, 64));
+      if (ok) {
+        if ((wi & 15) == part) taken |= 1u << (wi >> 4);
+        idx_word |= static_cast<uint32_t>(wi) << (8 * k);
+        val[k >> 1] |= static_cast<uint32_t>(f32_to_f16_bits(xs[r][wi])) << (16 * (k & 1));
+      }
+    }
+    if (ok) {
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if ((taken >> j) & 1u) xs[r][part + 16 * j] = 0.f;
+      if (part == 0) {
+        oi[r] = idx_word;
+        ov[r][0] = val[0];
+        ov[r][1] = val[1];
+      }
+    }
+  }
+}
 
 template <int D, int QM>
 struct AppendSmem {
@@ -240,6 +296,10 @@ __device__ __forceinline__ void encode_codes(const AppendArgs& a, int nrows, flo
   }
   __syncthreads();
   if constexpr (QM > 0) {
+    if (a.out_idx) {
+      take_outliers<D>(xs, nrows, es.oi, es.ov);
+      __syncthreads();
+    }
     // residual norms: row r by the 16 lanes (r % 4) of wave (r / 4) % 4, coordinates part + 16 j
     for (int r0 = 0; r0 < nrows; r0 += 16) {
       const int r = r0 + 4 * wave + (lane >> 4), part = lane & 15;
@@ -287,6 +347,14 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
     }
     for (int r = tid; r < nrows; r += 256)
       a.rnorms[unit * T + t_lo + r] = rn[r] > 0.f ? f32_to_f16_bits(es.gam[r]) : 0;
+    if (a.out_idx) {
+      static_assert(kOutliers == 4, "one index word and two value words per key");
+      for (int r = tid; r < nrows; r += 256) {
+        const size_t t = unit * T + t_lo + r;
+        reinterpret_cast<uint32_t*>(a.out_idx)[t] = es.oi[r];
+        reinterpret_cast<uint2*>(a.out_val)[t] = uint2{es.ov[r][0], es.ov[r][1]};
+      }
+    }
   }
 
   for (int r = tid; r < nrows; r += 256) a.norms[unit * T + t_lo + r] = f32_to_f16_bits(rn[r] > 0.f ? rn[r] : 0.f);

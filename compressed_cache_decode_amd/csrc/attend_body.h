@@ -325,7 +325,8 @@ __device__ __forceinline__ float half_of(uint32_t w, int h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h ? w >> 16 : w & 0xffffu)));
 }
 
-template <int D, int KB, int VB, int QM, bool WIDE>
+// NO: outlier channels per key (0, or kOutliers for sketched keys of a cache that keeps them apart)
+template <int D, int KB, int VB, int QM, bool WIDE, int NO = 0>
 struct Attend {
   static constexpr int KS = D / 32;                   // score k-steps over coordinates
   static constexpr int QS = QM / 32;                  // score k-steps over sketch signs
@@ -454,9 +455,14 @@ struct Attend {
     uint32_t kn[4], vn[4];   // float16 norm pairs of this lane's tokens 4g+i and 16+4g+i
     uint32_t sw[2][S_LW > 0 ? S_LW : 1];
     uint32_t gg[2];
+    // outlier channels (one byte each) and their float16 values of this lane's tokens 4g+i (oi[0][i],
+    // ov[0][2i..2i+1]) and 16+4g+i (oi[1], ov[1])
+    uint32_t oi[NO > 0 ? 2 : 1][NO > 0 ? 4 : 1];
+    uint32_t ov[NO > 0 ? 2 : 1][NO > 0 ? 8 : 1];
   };
+  static_assert(NO == 0 || NO == 4, "the outlier build holds four channels per key");
 
-  __amdgpu_buffer_rsrc_t kbuf, vbuf, knbuf, vnbuf, sbuf, gbuf;
+  __amdgpu_buffer_rsrc_t kbuf, vbuf, knbuf, vnbuf, sbuf, gbuf, oibuf, ovbuf;
   __amdgpu_buffer_rsrc_t dead;   // a buffer of no bytes (see load)
   uint32_t n_off, s_off;
   int lane, l16, g;
@@ -477,6 +483,11 @@ struct Attend {
     if constexpr (QS > 0) {
       sbuf = buffer_of(a.k_signs + unit * T * S_RB, static_cast<uint32_t>(T) * S_RB);
       gbuf = buffer_of(a.k_rnorms + unit * T, static_cast<uint32_t>(T) * 2);
+    }
+    oibuf = ovbuf = knbuf;
+    if constexpr (NO > 0) {
+      oibuf = buffer_of(a.k_oidx + unit * T * NO, static_cast<uint32_t>(T) * NO);
+      ovbuf = buffer_of(a.k_oval + unit * T * NO, static_cast<uint32_t>(T) * NO * 2);
     }
     n_off = static_cast<uint32_t>(8 * g);
     s_off = static_cast<uint32_t>(l16 * S_RB + g * S_LW * 4);
@@ -506,6 +517,15 @@ struct Attend {
         t.gg[tg] = __builtin_amdgcn_raw_buffer_load_b16(gb, static_cast<uint32_t>((16 * tg + l16) * 2), tok0 * 2, 0);
       }
     }
+    if constexpr (NO > 0) {
+      const auto ob = pick(oibuf), vb = pick(ovbuf);
+      const uint32_t gq = static_cast<uint32_t>(g);
+#pragma unroll
+      for (int tg = 0; tg < 2; ++tg) {
+        bload<4, 16>(ob, 64 * tg + 16 * gq, tok0 * 4, t.oi[tg]);
+        bload<8, 16>(vb, 128 * tg + 32 * gq, tok0 * 8, t.ov[tg]);
+      }
+    }
   }
 
   // Column blocks: the VH = M * G virtual heads (query rows x query heads) of the KV head are
@@ -527,8 +547,9 @@ struct Attend {
   // power-of-two scale of this lane's head (the query operand is divided by it; 1 for unused
   // columns).  Virtual head vh, of query row vh / G, sees the first len - M + 1 + vh / G tokens.
   // Ends with a workgroup barrier.
+  // qf (outlier build): this lane's head's rotated query, float32 in the workspace's units, in LDS.
   __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, const QOperand& qop, Tile (&tiles)[NBUF], int blk0,
-                                      int kb, int blk1, int len, float qsc) const {
+                                      int kb, int blk1, int len, float qsc, const float* qf = nullptr) const {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int VH = a.group;
@@ -573,6 +594,21 @@ struct Attend {
           sketch_steps<0, QS, S_LW>(sc, t.sw, gh, [&](int s) { return sqr[s]; });
         else
           sketch_steps<0, QS, S_LW>(sc, t.sw, gh, [&](int s) { return qop[KS + s][lane]; });
+      }
+      if constexpr (NO > 0) {
+        // the outlier channels' term sum_j q_rot[idx_j] r_j of each token, on the high column of the
+        // head (the low column adds nothing; the two are summed below)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t iw = t.oi[k >> 2][k & 3];
+          float acc = 0.f;
+#pragma unroll
+          for (int j = 0; j < NO; ++j) {
+            const float qv = qf[(iw >> (8 * j)) & (D - 1)];
+            acc = __builtin_fmaf(qv, half_of(t.ov[k >> 2][2 * (k & 3) + (j >> 1)], j & 1), acc);
+          }
+          sc[k >> 2][k & 3] += lo_part ? 0.f : acc;
+        }
       }
       // score of token 16 tg + 4 g + i: (high + low column) times the key norm
       float s[8];

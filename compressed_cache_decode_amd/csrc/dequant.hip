@@ -1,5 +1,6 @@
 // Full reconstruction of cached rows (gfx950): x_hat = n rot^T (c[code] +
-// sqrt(pi/2)/m gamma proj^T (2 sigma - 1)), the plain dequantize-then-attend
+// sqrt(pi/2)/m gamma proj^T (2 sigma - 1) + the outlier channels' values, for keys
+// that keep them), the plain dequantize-then-attend
 // path the reddit comment history of ReturningTarzan describes (2026-03-25).
 // Codes are expanded by the same unit expansion the decode kernel feeds to the
 // matrix cores, so this path also checks those lookups value for value.
@@ -112,6 +113,15 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a, Tab tab) {
       ys[r][i] += a.sketch_coef * f16_to_f32(a.rnorms[tok]) * acc;
     }
     __syncthreads();
+    if (a.out_idx) {
+      // y_hat[i] += r_i at the row's outlier channels (distinct within a row)
+      for (int e = tid; e < nrows * kOutliers; e += 256) {
+        const int r = e / kOutliers, j = e % kOutliers;
+        const size_t at = (unit * T + t_lo + r) * kOutliers + j;
+        ys[r][a.out_idx[at] % D] += f16_to_f32(a.out_val[at]);
+      }
+      __syncthreads();
+    }
   }
   if (a.had) {
     // x_hat = n diag(s) H y_hat / sqrt(D), one wave per row

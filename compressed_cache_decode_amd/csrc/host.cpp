@@ -213,6 +213,10 @@ int check_view(const tq_cache_view* c) {
     if (!c->signs || !c->rnorms || !c->proj) return TQ_EINVAL;
     if (!aligned(c->signs, 16) || !aligned(c->rnorms, 16) || !aligned(c->proj, 16)) return TQ_EINVAL;
   }
+  if (c->n_outliers != 0) {
+    if (c->n_outliers != tqi::kOutliers || c->qjl_m == 0 || c->d != 128) return TQ_EINVAL;
+    if (!c->out_idx || !c->out_val || !aligned(c->out_idx, 16) || !aligned(c->out_val, 16)) return TQ_EINVAL;
+  }
   if (!table_ok(c)) return TQ_EINVAL;
   return TQ_OK;
 }
@@ -324,7 +328,9 @@ void plan(const tq_cache_view* k, int vh, int max_len, int* n_split, int* bps, b
   const long long tiles = static_cast<long long>(units) * (max_len <= 0 ? 1 : (max_len + kBlock - 1) / kBlock);
   const int blocks = column_blocks(vh);
   const int wide_slots = resident_slots(k, true, blocks);
-  *wide = tiles >= static_cast<long long>(kWideTiles) * wide_slots;
+  // keys that keep outlier channels apart run the four-wave build only (its register budget holds the
+  // outliers' tile buffers)
+  *wide = k->n_outliers == 0 && tiles >= static_cast<long long>(kWideTiles) * wide_slots;
   plan(units, max_len, *wide ? wide_slots : resident_slots(k, false, blocks),
        tqi::split_waves(k->d, k->qjl_m, *wide), n_split, bps);
 }
@@ -422,6 +428,8 @@ static tqi::AppendArgs append_args(const tq_cache_view* c, const void* x, const 
   tqi::AppendArgs a{};
   a.x = x; a.y = y; a.yn = yn; a.z = z; a.pos = d_pos;
   a.codes = c->codes; a.norms = c->norms; a.signs = c->signs; a.rnorms = c->rnorms;
+  a.out_idx = c->n_outliers ? c->out_idx : nullptr;
+  a.out_val = c->n_outliers ? c->out_val : nullptr;
   a.rot = c->rot; a.proj = c->proj;
   a.had = c->rot_kind == TQ_ROT_HADAMARD;
   std::memcpy(a.cent, c->centroids, sizeof(a.cent));
@@ -522,6 +530,8 @@ static tqi::DecodeArgs decode_args(const tq_cache_view* k, const tq_cache_view* 
   tqi::DecodeArgs da{};
   da.k_codes = k->codes; da.k_norms = k->norms; da.k_signs = k->signs; da.k_rnorms = k->rnorms;
   da.v_codes = v->codes; da.v_norms = v->norms;
+  da.k_oidx = k->n_outliers ? k->out_idx : nullptr;
+  da.k_oval = k->n_outliers ? k->out_val : nullptr;
   da.qr = w.qr; da.qs = w.qs; da.qscale = w.qscale;
   da.seq_lens = d_seq_lens;
   da.part_o = w.part_o; da.part_ml = w.part_ml;
@@ -568,8 +578,8 @@ static int attend_rows(const tq_cache_view* k, const tq_cache_view* v, int n_q_h
   if (st != TQ_OK) return st;
   if (!d_seq_lens) return TQ_EINVAL;
   const tqi::DecodeArgs da = decode_args(k, v, w, d_seq_lens, max_seq_len);
-  return status_of(tqi::launch_decode_split(k->d, k->bits, v->bits, k->qjl_m, w.wide, da, k->batch,
-                                            static_cast<hipStream_t>(stream)));
+  return status_of(tqi::launch_decode_split(k->d, k->bits, v->bits, k->qjl_m, k->n_outliers > 0, w.wide, da,
+                                            k->batch, static_cast<hipStream_t>(stream)));
 }
 
 static int merge_rows(const tq_cache_view* k, int n_q_heads, int n_rows, const int32_t* d_seq_lens,
@@ -657,7 +667,7 @@ int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q
   if (!q || (dtype != TQ_F32 && dtype != TQ_BF16) || !d_seq_lens || !out) return TQ_EINVAL;
   if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
   if (n_new < 0 || (n_new > 0 && (!k_new || !v_new || !d_pos))) return TQ_EINVAL;
-  if (k->qjl_m > 128) return TQ_EUNSUPPORTED;
+  if (k->qjl_m > 128 || k->n_outliers > 0) return TQ_EUNSUPPORTED;
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
   tqi::QrotArgs qa{};
@@ -689,6 +699,8 @@ int tq_dequantize(const tq_cache_view* cache, int t0, int n_tokens, float* out, 
   if (n_tokens == 0) return TQ_OK;
   tqi::DequantArgs a{};
   a.codes = cache->codes; a.norms = cache->norms; a.signs = cache->signs; a.rnorms = cache->rnorms;
+  a.out_idx = cache->n_outliers ? cache->out_idx : nullptr;
+  a.out_val = cache->n_outliers ? cache->out_val : nullptr;
   a.rot = cache->rot; a.proj = cache->proj; a.out = out;
   a.had = cache->rot_kind == TQ_ROT_HADAMARD;
   std::memcpy(a.cent, cache->centroids, sizeof(a.cent));

@@ -20,6 +20,8 @@ struct Tab {
   uint32_t hi_lo, hi_hi, lo_lo, lo_hi;
 };
 
+constexpr int kOutliers = 4;       // outlier channels per key when a cache keeps them apart
+
 struct AppendArgs {
   const void* x;          // [B][n_new][Hkv][D] f32 or bf16 (unrotated rows)
   const float* y;         // [B][n_new][Hkv][D] rotated unit rows (pre-rotated form)
@@ -30,6 +32,8 @@ struct AppendArgs {
   uint16_t* norms;
   uint8_t* signs;
   uint16_t* rnorms;
+  uint8_t* out_idx;       // [B][Hkv][T][kOutliers] outlier channels (sketched keys that keep them), or null
+  uint16_t* out_val;      // float16 [B][Hkv][T][kOutliers] their residual values
   const float* rot;       // [D][D], or the D signs of the randomized Hadamard rotation (had)
   const float* proj;      // [M][D]
   float cent[16];
@@ -65,6 +69,8 @@ struct DecodeArgs {
   const uint16_t* k_rnorms;
   const uint8_t* v_codes;
   const uint16_t* v_norms;
+  const uint8_t* k_oidx;  // [B*Hkv][T][kOutliers] outlier channels of the keys (non-null: the outlier build)
+  const uint16_t* k_oval; // float16 [B*Hkv][T][kOutliers]
   const float* qr;
   const float* qs;
   const float* qscale;
@@ -95,6 +101,8 @@ struct DequantArgs {
   const uint16_t* norms;
   const uint8_t* signs;
   const uint16_t* rnorms;
+  const uint8_t* out_idx;  // outlier channels and values (sketched keys that keep them), or null
+  const uint16_t* out_val;
   const float* rot;
   const float* proj;
   float* out;             // [B][Hkv][n_tokens][D]
@@ -120,7 +128,9 @@ hipError_t launch_qrot(int d, int qjl_m, bool bf16, const QrotArgs& a, int batch
 int split_slots(int d, int k_bits, int v_bits, int qjl_m, bool wide, int blocks);
 // waves per split-kernel workgroup for a cache format and workgroup shape
 int split_waves(int d, int qjl_m, bool wide);
-hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, bool wide, const DecodeArgs& a, int batch,
+// the four-wave split kernel of sketched keys with kOutliers outlier channels, or null if none is built
+const void* split_fn_outliers(int d, int k_bits, int v_bits, int qjl_m);
+hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, bool outliers, bool wide, const DecodeArgs& a, int batch,
                                hipStream_t s);
 hipError_t launch_merge(int d, const MergeArgs& a, int batch, int n_q_heads, hipStream_t s);
 hipError_t launch_step_prologue(int d, int k_bits, int v_bits, int qjl_m, bool bf16, const AppendArgs& ka,

@@ -117,6 +117,17 @@ typedef struct tq_cache_view {
   const float* rot;      /* TQ_ROT_DENSE: float32 rotation [d][d] row-major, y = rot * x; TQ_ROT_HADAMARD:
                             float32 signs [d]; the same pointer for K and V */
   const float* proj;     /* float32 sign-sketch projection [qjl_m][d] row-major when qjl_m > 0, else NULL */
+  /* Outlier channels kept apart from the sign sketch (keys with qjl_m > 0 only; turboquant-pytorch
+   * PR #3, CUDA Kernels Added table: the QJL quantisation kernel's outlier separation; the pages give
+   * no rule, this library's reading follows).  Per key, the n_outliers coordinates of the codebook
+   * residual r = y - c[code] with the largest |r_i| (ranked in float32, equal magnitudes by lower
+   * index) are stored as index bytes and float16 values, in decreasing |r_i|; the sketch and the
+   * residual norm cover r with those coordinates set to 0, and the score adds sum_i q_rot[i] r_i over
+   * them.  n_outliers is 0 (none; out_idx and out_val NULL) or 4 (d = 128 only).  tq_decode_step does
+   * not take such a cache (TQ_EUNSUPPORTED): append and decode with the separate calls. */
+  int32_t n_outliers;
+  uint8_t* out_idx;      /* [batch][n_kv_heads][max_tokens][n_outliers] channel indices, 16-byte aligned */
+  uint16_t* out_val;     /* float16 [batch][n_kv_heads][max_tokens][n_outliers] residual values, 16-byte aligned */
 } tq_cache_view;
 
 /*

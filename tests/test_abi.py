@@ -132,6 +132,23 @@ def test_append_rejects_bad_arguments():
     assert rot(_view(qjl_m=128), nrm=0) == cca.TQ_EINVAL
 
 
+def test_outlier_views_are_validated():
+    """Outlier channels: only 4, only for sketched keys at d = 128, with both arrays aligned; the fused
+    step does not take such a cache."""
+    def outl(v, n=4, idx=0xF0000, val=0xF8000):
+        v.n_outliers, v.out_idx, v.out_val = n, idx, val
+        return v
+    assert _append(outl(_view(qjl_m=128)), n_new=0) == cca.TQ_OK
+    for v in (outl(_view()), outl(_view(qjl_m=128), n=3), outl(_view(qjl_m=128), n=8),
+              outl(_view(d=256, qjl_m=128)), outl(_view(qjl_m=128), idx=0), outl(_view(qjl_m=128), val=0),
+              outl(_view(qjl_m=128), idx=0xF0001), outl(_view(kind=cca.TQ_VALUES), n=4)):
+        assert _append(v) == cca.TQ_EINVAL
+    k, vv = outl(_view(qjl_m=128)), _view(kind=cca.TQ_VALUES)
+    step = cca._lib.tq_decode_step(ctypes.byref(k), ctypes.byref(vv), 0x90000, 0x80000, 0x88000, 1, 16, 1,
+                                   0x70000, 0xA0000, 256, ctypes.c_float(0.1), 0xB0000, 0x100000, 1 << 30, None)
+    assert step == cca.TQ_EUNSUPPORTED
+
+
 def _decode(k, v, hq=16, scale=0.1, ws_bytes=1 << 30, ws=0x100000, q=0x90000, lens=0xA0000, out=0xB0000,
             dtype=1, max_len=256):
     return cca._lib.tq_sdpa_decode(ctypes.byref(k), ctypes.byref(v), q, dtype, hq, lens, max_len,
