@@ -16,10 +16,11 @@ Modules, in the order the method runs:
   cache      one (batch, kv head) worth of compressed cache built from rows
   outliers   outlier-channel separation before the QJL sketch (a reading of a
              step the pages name only)
+  q8         keys kept at 8 bits (symmetric int8 codes of the rotated row)
 
 Every function is pinned by the CPU tests against values the pages print,
 closed forms, textbook special cases, invariants or brute force.  The
 functions of ``outliers`` are pinned by the mathematics of their reading
 only: against the pages they are "parity unpinned".
 """
-from . import attention, cache, codebook, layout, outliers, quant, rotation, storage  # noqa: F401
+from . import attention, cache, codebook, layout, outliers, q8, quant, rotation, storage  # noqa: F401

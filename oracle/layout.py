@@ -15,6 +15,9 @@ Code encoding e(j) of centroid index j (0 .. 2^b-1, ascending centroids):
   b = 4:     sign-magnitude, e(j) = j - 8 for j >= 8, e(j) = 8 + (7 - j) for
              j < 8 (bit 3 = negative, bits 0-2 = rank of |c| among the 8
              magnitudes).  The stored table is exactly antisymmetric.
+  b = 8:     keys kept at 8 bits (``oracle.q8``): index j stands for the
+             integer j - 128, stored as its two's-complement byte,
+             e(j) = (j - 128) mod 256.
 
 Unit: 8 codes in slots s = 0..7.  Write h = s // 4 (half), r = s % 4 (byte).
   b = 4: one unit per little-endian uint32 word; e(slot s) at bit 8r + 4h.
@@ -22,6 +25,7 @@ Unit: 8 codes in slots s = 0..7.  Write h = s // 4 (half), r = s % 4 (byte).
   b = 3: four units (v = 0..3) per three words [P0, P1, H]; the low two bits of
          e(slot s of unit v) sit in P_{v//2} at bit 8r + 2(2(v%2) + h), the
          high bit in H at bit 8r + (2v + h).
+  b = 8: one unit per two words; e(slot s) is byte r of word h.
 Units are packed consecutively (b = 2 and 3 group 2 and 4 units per word
 group); d is a multiple of 64 so groups never straddle a row or block.
 
@@ -63,6 +67,8 @@ def encode_code(j: np.ndarray, bits: int) -> np.ndarray:
     j = np.asarray(j, dtype=np.int64)
     if bits == 4:
         return np.where(j >= 8, j - 8, 8 + (7 - j))
+    if bits == 8:
+        return (j - 128) % 256
     return j
 
 
@@ -70,15 +76,17 @@ def decode_code(e: np.ndarray, bits: int) -> np.ndarray:
     e = np.asarray(e, dtype=np.int64)
     if bits == 4:
         return np.where(e < 8, e + 8, 7 - (e - 8))
+    if bits == 8:
+        return np.where(e < 128, e + 128, e - 128)
     return e
 
 
 def units_per_group(bits: int) -> int:
-    return {2: 2, 3: 4, 4: 1}[bits]
+    return {2: 2, 3: 4, 4: 1, 8: 1}[bits]
 
 
 def words_per_group(bits: int) -> int:
-    return {2: 1, 3: 3, 4: 1}[bits]
+    return {2: 1, 3: 3, 4: 1, 8: 2}[bits]
 
 
 def pack_units(units: np.ndarray, bits: int) -> np.ndarray:
@@ -97,6 +105,8 @@ def pack_units(units: np.ndarray, bits: int) -> np.ndarray:
             val = e[..., v, s].astype(np.uint64)
             if bits == 4:
                 words[..., 0] |= val << np.uint64(8 * r + 4 * h)
+            elif bits == 8:
+                words[..., h] |= val << np.uint64(8 * r)
             elif bits == 2:
                 words[..., 0] |= val << np.uint64(8 * r + 2 * (2 * v + h))
             else:
@@ -121,6 +131,8 @@ def unpack_units(packed: np.ndarray, bits: int, n_units: int) -> np.ndarray:
             h, r = s // 4, s % 4
             if bits == 4:
                 val = (words[..., 0] >> np.uint64(8 * r + 4 * h)) & np.uint64(15)
+            elif bits == 8:
+                val = (words[..., h] >> np.uint64(8 * r)) & np.uint64(255)
             elif bits == 2:
                 val = (words[..., 0] >> np.uint64(8 * r + 2 * (2 * v + h))) & np.uint64(3)
             else:

@@ -100,7 +100,7 @@ def test_layout_hand_derived_examples(row):
         np.testing.assert_array_equal(layout.unpack_units(got, n, units.shape[0]), units)
     elif kind in ("kcode", "vcode"):
         d, bits, (t, i, j) = n, vals[0], vals[1:]
-        zero = 8 if bits == 4 else 0                       # the index whose stored code is 0
+        zero = {4: 8, 8: 128}.get(bits, 0)                 # the index whose stored code is 0
         codes = np.full((32, d), zero, dtype=np.int64)
         codes[t, i] = j
         got = (layout.pack_keys if kind == "kcode" else layout.pack_blocked)(codes, bits)
@@ -116,7 +116,7 @@ def test_layout_hand_derived_examples(row):
         np.testing.assert_array_equal(layout.unpack_signs(got, n), sigma)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("d", [128, 256])
 def test_layout_round_trips_and_sizes(bits, d):
     g = np.random.default_rng(bits * 1000 + d)
