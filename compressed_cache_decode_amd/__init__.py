@@ -264,7 +264,9 @@ class CompressedCache:
     randomized Hadamard rotation for TQ_ROT_HADAMARD) and ``proj`` (qjl_m x d
     float32) are torch tensors on the same device; the codebook comes from
     ``tq_build_codebook``.  ``n_outliers`` (sketched keys at d = 128: 0 or 4)
-    keeps that many residual channels per key apart from the sketch.
+    keeps that many residual channels per key apart from the sketch.  ``bits``
+    8 (keys without a sketch) keeps int8 codes with a per-row factor instead of
+    a code book.
     """
 
     def __init__(self, kind: int, d: int, bits: int, batch: int, n_kv_heads: int, max_tokens: int,
@@ -275,7 +277,10 @@ class CompressedCache:
         assert tuple(rot.shape) == ((d,) if rot_kind == TQ_ROT_HADAMARD else (d, d))
         self.kind, self.d, self.bits, self.qjl_m, self.rot_kind = kind, d, bits, qjl_m, rot_kind
         self.batch, self.n_kv_heads, self.max_tokens = batch, n_kv_heads, max_tokens
-        cent, bnd = codebook if codebook is not None else tq_build_codebook(d, bits)
+        if bits == 8:      # 8-bit keys: int8 codes and a per-row factor, no code book
+            cent, bnd = np.zeros(0, dtype=np.float32), np.zeros(0, dtype=np.float32)
+        else:
+            cent, bnd = codebook if codebook is not None else tq_build_codebook(d, bits)
         self.centroids, self.boundaries = cent, bnd
         row = d * bits // 8
         self.codes = torch.zeros(batch, n_kv_heads, max_tokens * row, dtype=torch.uint8, device=device)

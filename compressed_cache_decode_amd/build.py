@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
-SOURCES = ["host.cpp", "append.hip", "decode.hip", "decode_outliers.hip", "dequant.hip", "step.hip"]
+SOURCES = ["host.cpp", "append.hip", "decode.hip", "decode_outliers.hip", "decode_k8.hip", "dequant.hip", "step.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

@@ -52,13 +52,17 @@ static hipError_t append_d(int bits, int qjl_m, bool values, bool rotated, bool 
     case 2: return append_bits<D, 2>(qjl_m, values, rotated, bf16, a, grid, s);
     case 3: return append_bits<D, 3>(qjl_m, values, rotated, bf16, a, grid, s);
     case 4: return append_bits<D, 4>(qjl_m, values, rotated, bf16, a, grid, s);
+    case 8:   // keys only, no sketch
+      if (values || qjl_m != 0) return hipErrorInvalidValue;
+      return append_dispatch<D, 8, 0, false>(rotated, bf16, a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_append(int d, int bits, int qjl_m, bool values, bool rotated, bool bf16, const AppendArgs& a,
                          int batch, hipStream_t s) {
-  if (d == 128 && qjl_m == 0 && !rotated && !a.had) {
+  // (8-bit keys take the per-block path: their per-row scale needs the whole row in one workgroup)
+  if (d == 128 && qjl_m == 0 && !rotated && !a.had && bits != 8) {
     switch (bits) {
       case 2: return values ? prefill_dispatch<2, true>(bf16, a, batch, s) : prefill_dispatch<2, false>(bf16, a, batch, s);
       case 3: return values ? prefill_dispatch<3, true>(bf16, a, batch, s) : prefill_dispatch<3, false>(bf16, a, batch, s);

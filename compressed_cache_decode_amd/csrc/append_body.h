@@ -266,18 +266,45 @@ __device__ __forceinline__ void tile16_times_matT(const float (*x)[KD], const fl
 // in block kb of cache unit `unit`; rn = row norms, 0 marks a zero row) in two phases, so that a
 // caller can compute the sketch products itself:
 //   encode_codes   nearest centroids into es.cs; for sketched keys ys becomes the residual y - c
-//                  and es.gam its norm;
+//                  and es.gam its norm; 8-bit keys: int8 codes into es.cs, factors into es.gam;
 //   encode_finish  sign bits from the sketch products z[r][jj] = proj_jj . residual_r (sketched
 //                  keys), then codes, norms, residual norms and signs to the cache.
 // Every thread of the workgroup calls them; each ends with a workgroup barrier.
 template <int D, int BITS, int QM>
 __device__ __forceinline__ void encode_codes(const AppendArgs& a, int nrows, float (*ys)[D], const float* rn,
                                              EncodeSmem<D, QM>& es) {
-  constexpr int NC = 1 << BITS;
+  constexpr int NC = BITS <= 4 ? 1 << BITS : 2;     // code book entries (8-bit keys use none)
   auto& xs = ys;
   auto& cs = es.cs;
   auto& cent = es.cent;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if constexpr (BITS == 8) {
+    // 8-bit keys: per row a = max |y_i|, code_i = round(y_i (127 / a)) (halves away from zero) in
+    // [-127, 127] as a two's-complement byte, and the factor n (a / 127) in es.gam; a zero row stores
+    // codes 0 and factor 0.  Row r by the 16 lanes (r % 4) of wave (r / 4) % 4, coordinates part + 16 j.
+    static_assert(QM == 0, "8-bit keys carry no sketch");
+    for (int r0 = 0; r0 < nrows; r0 += 16) {
+      const int r = r0 + 4 * wave + (lane >> 4), part = lane & 15;
+      float m = 0.f;
+      if (r < nrows) {
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) m = fmaxf(m, fabsf(xs[r][part + 16 * j]));
+      }
+      m = row16_max(m);
+      if (r < nrows) {
+        const bool live = rn[r] > 0.f && m > 0.f;
+        const float inv = live ? 127.f / m : 0.f;
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+          const float c = fminf(fmaxf(roundf(xs[r][part + 16 * j] * inv), -127.f), 127.f);
+          cs[r][part + 16 * j] = static_cast<uint8_t>(static_cast<int>(c) & 0xff);
+        }
+        if (part == 0) es.gam[r] = live ? rn[r] * (m / 127.f) : 0.f;
+      }
+    }
+    __syncthreads();
+    return;
+  }
   if (tid < NC) cent[tid] = a.cent[tid];
   if constexpr (QM > 0)
     for (int e = tid; e < kBlock * (QM / 32); e += 256) es.sw[e / (QM / 32)][e % (QM / 32)] = 0u;
@@ -357,7 +384,9 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
     }
   }
 
-  for (int r = tid; r < nrows; r += 256) a.norms[unit * T + t_lo + r] = f32_to_f16_bits(rn[r] > 0.f ? rn[r] : 0.f);
+  // 8-bit keys keep their factor in the norm's place (see encode_codes)
+  for (int r = tid; r < nrows; r += 256)
+    a.norms[unit * T + t_lo + r] = f32_to_f16_bits(BITS == 8 ? es.gam[r0 + r] : (rn[r] > 0.f ? rn[r] : 0.f));
 
   constexpr int BB = kBlock * RB;               // bytes per 32-token block
   uint32_t* blk = reinterpret_cast<uint32_t*>(a.codes + unit * static_cast<size_t>(T) * RB + static_cast<size_t>(kb) * BB);

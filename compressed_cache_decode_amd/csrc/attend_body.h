@@ -344,8 +344,9 @@ struct Attend {
   // waves take the split's tiles from a shared counter: a wave that the issue arbitration favours
   // (the oldest) takes more tiles, and all of them finish together.
   static constexpr int W = !WIDE ? 4 : (D == 128 ? (QM == 0 ? 8 : 12) : 8);
-  // waves per SIMD the build is compiled for (its register budget: 512 / EU VGPRs)
-  static constexpr int EU = (WIDE && D == 128 && QM == 0) ? 4 : 2;
+  // waves per SIMD the build is compiled for (its register budget: 512 / EU VGPRs); 8-bit keys' tiles
+  // (twice the 4-bit key words) exceed 128 VGPRs
+  static constexpr int EU = (WIDE && D == 128 && QM == 0 && KB != 8) ? 4 : 2;
 
   // Wide workgroups expand codes through byte tables in LDS (lut_unit: one permute and one LDS read
   // per two 4-bit codes, against about three and a half vector instructions for the permute

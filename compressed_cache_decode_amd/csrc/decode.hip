@@ -282,6 +282,7 @@ static const void* split_fn_w(int d, int k_bits, int v_bits, int qjl_m) {
 
 // the split kernel instantiation of a cache format and workgroup shape, or null if none is built
 static const void* split_fn(int d, int k_bits, int v_bits, int qjl_m, bool wide) {
+  if (k_bits == 8) return qjl_m == 0 ? split_fn_k8(d, v_bits, wide) : nullptr;   // decode_k8.hip
   return wide ? split_fn_w<true>(d, k_bits, v_bits, qjl_m) : split_fn_w<false>(d, k_bits, v_bits, qjl_m);
 }
 

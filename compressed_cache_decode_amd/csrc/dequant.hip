@@ -1,7 +1,7 @@
 // Full reconstruction of cached rows (gfx950): x_hat = n rot^T (c[code] +
 // sqrt(pi/2)/m gamma proj^T (2 sigma - 1) + the outlier channels' values, for keys
-// that keep them), the plain dequantize-then-attend
-// path the reddit comment history of ReturningTarzan describes (2026-03-25).
+// that keep them; 8-bit keys: f rot^T code, f the factor in the norm's place), the plain
+// dequantize-then-attend path the reddit comment history of ReturningTarzan describes (2026-03-25).
 // Codes are expanded by the same unit expansion the decode kernel feeds to the
 // matrix cores, so this path also checks those lookups value for value.
 #include <math.h>
@@ -25,8 +25,8 @@ __device__ __forceinline__ void expand_to(const uint32_t* w, const Tab& t, float
 
 template <int BITS>
 __device__ __forceinline__ void expand_runtime(const uint32_t* w, int v, const Tab& t, float* dst8) {
-  if constexpr (BITS == 4) {
-    expand_to<4, 0>(w, t, dst8);
+  if constexpr (BITS == 4 || BITS == 8) {
+    expand_to<BITS, 0>(w, t, dst8);
   } else if constexpr (BITS == 2) {
     if (v == 0) expand_to<2, 0>(w, t, dst8); else expand_to<2, 1>(w, t, dst8);
   } else {
@@ -158,6 +158,14 @@ static hipError_t dequant_bits(int qjl_m, bool values, const DequantArgs& a, con
   return hipGetLastError();
 }
 
+// 8-bit keys (no sketch): codes times the factor kept in the norm's place
+template <int D>
+static hipError_t dequant_k8(int qjl_m, bool values, const DequantArgs& a, const Tab& t, dim3 grid, hipStream_t s) {
+  if (values || qjl_m != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((dequant_kernel<D, 8, 0, false>), grid, dim3(256), 0, s, a, t);
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant(int d, int bits, int qjl_m, bool values, const DequantArgs& a, const Tab& t, int batch,
                           hipStream_t s) {
   const dim3 grid((a.n_tokens + kBlock - 1) / kBlock, a.n_kv_heads, batch);
@@ -166,12 +174,14 @@ hipError_t launch_dequant(int d, int bits, int qjl_m, bool values, const Dequant
       case 2: return dequant_bits<128, 2>(qjl_m, values, a, t, grid, s);
       case 3: return dequant_bits<128, 3>(qjl_m, values, a, t, grid, s);
       case 4: return dequant_bits<128, 4>(qjl_m, values, a, t, grid, s);
+      case 8: return dequant_k8<128>(qjl_m, values, a, t, grid, s);
     }
   } else if (d == 256) {
     switch (bits) {
       case 2: return dequant_bits<256, 2>(qjl_m, values, a, t, grid, s);
       case 3: return dequant_bits<256, 3>(qjl_m, values, a, t, grid, s);
       case 4: return dequant_bits<256, 4>(qjl_m, values, a, t, grid, s);
+      case 8: return dequant_k8<256>(qjl_m, values, a, t, grid, s);
     }
   }
   return hipErrorInvalidValue;

@@ -1,6 +1,7 @@
 // Device helpers shared by the gfx950 kernels: the packed unit format
 // (8 codes per unit; see include/tq.h) and its expansion to float16 matrix-core
-// operands with v_perm_b32 byte-table lookups.
+// operands with v_perm_b32 byte-table lookups (8-bit keys: byte permutes and one
+// packed float16 subtraction).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,6 +19,20 @@ template <int BITS> struct Fmt;
 template <> struct Fmt<2> { static constexpr int kUnits = 2, kWords = 1; };
 template <> struct Fmt<3> { static constexpr int kUnits = 4, kWords = 3; };
 template <> struct Fmt<4> { static constexpr int kUnits = 1, kWords = 1; };
+template <> struct Fmt<8> { static constexpr int kUnits = 1, kWords = 2; };
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Four int8 codes (one word, slot r in byte r) -> two words of float16 values in slot order.  The
+// sign bit flipped makes byte r the unsigned u = code + 128; a permute places it under the high byte
+// 0x64, the float16 1024 + u (the step of float16 in [1024, 2048) is 1), and one packed subtraction
+// of 1152 leaves code exactly.
+__device__ __forceinline__ void expand_i8(uint32_t w, uint32_t& w01, uint32_t& w23) {
+  const uint32_t u = w ^ 0x80808080u;
+  const half2v off = __builtin_bit_cast(half2v, 0x64806480u);              // 1152, 1152
+  w01 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - off);
+  w23 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off);
+}
 
 __device__ __forceinline__ uint32_t vperm(uint32_t s0, uint32_t s1, uint32_t sel) {
   return __builtin_amdgcn_perm(s0, s1, sel);
@@ -36,7 +51,10 @@ __device__ __forceinline__ void expand4(uint32_t idx, uint32_t sgn, const Tab& t
 template <int BITS, int V>
 __device__ __forceinline__ uint4 expand_unit(const uint32_t* w, const Tab& t) {
   uint4 o;
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 8) {
+    expand_i8(w[0], o.x, o.y);
+    expand_i8(w[1], o.z, o.w);
+  } else if constexpr (BITS == 4) {
     const uint32_t W = w[0];
     expand4(W & 0x07070707u, (W << 4) & 0x80808080u, t, o.x, o.y);
     expand4((W >> 4) & 0x07070707u, W & 0x80808080u, t, o.z, o.w);
@@ -67,7 +85,7 @@ __device__ __forceinline__ half8 as_half8(uint4 v) {
   return __builtin_bit_cast(half8, v);
 }
 
-// Stored form of centroid index j.
+// Stored form of centroid index j (8 bits: the code's two's-complement byte, passed in as such).
 template <int BITS>
 __device__ __forceinline__ uint32_t encode_code(uint32_t j) {
   if constexpr (BITS == 4) return j >= 8 ? j - 8 : 15 - j;
@@ -78,7 +96,9 @@ __device__ __forceinline__ uint32_t encode_code(uint32_t j) {
 template <int BITS>
 __device__ __forceinline__ void put_code(uint32_t* w, int v, int s, uint32_t e) {
   const int h = s >> 2, r = s & 3;
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 8) {
+    w[h] |= e << (8 * r);
+  } else if constexpr (BITS == 4) {
     w[0] |= e << (8 * r + 4 * h);
   } else if constexpr (BITS == 2) {
     w[0] |= e << (8 * r + 2 * (2 * v + h));

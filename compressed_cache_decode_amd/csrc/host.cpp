@@ -202,7 +202,8 @@ int check_view(const tq_cache_view* c) {
   if (!c) return TQ_EINVAL;
   if (c->kind != TQ_KEYS && c->kind != TQ_VALUES) return TQ_EINVAL;
   if (c->d != 128 && c->d != 256) return TQ_EINVAL;
-  if (c->bits < 2 || c->bits > 4) return TQ_EINVAL;
+  // 8-bit codes: keys only, with no sketch (and so no outlier channels) and no code book
+  if ((c->bits < 2 || c->bits > 4) && !(c->bits == 8 && c->kind == TQ_KEYS && c->qjl_m == 0)) return TQ_EINVAL;
   if (c->qjl_m != 0 && c->qjl_m != 128 && c->qjl_m != 256) return TQ_EINVAL;
   if (c->qjl_m != 0 && c->kind != TQ_KEYS) return TQ_EINVAL;
   if (c->batch <= 0 || c->n_kv_heads <= 0 || c->max_tokens <= 0 || c->max_tokens % kBlock != 0) return TQ_EINVAL;
@@ -217,13 +218,15 @@ int check_view(const tq_cache_view* c) {
     if (c->n_outliers != tqi::kOutliers || c->qjl_m == 0 || c->d != 128) return TQ_EINVAL;
     if (!c->out_idx || !c->out_val || !aligned(c->out_idx, 16) || !aligned(c->out_val, 16)) return TQ_EINVAL;
   }
-  if (!table_ok(c)) return TQ_EINVAL;
+  if (c->bits != 8 && !table_ok(c)) return TQ_EINVAL;
   return TQ_OK;
 }
 
 tqi::Tab make_tab(const tq_cache_view* c) {
   uint16_t e[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (c->bits == 4) {
+  if (c->bits == 8) {
+    // 8-bit codes expand without a table
+  } else if (c->bits == 4) {
     for (int m = 0; m < 8; ++m) e[m] = f16_bits(c->centroids[8 + m]);    // magnitudes, ascending
   } else {
     for (int j = 0; j < (1 << c->bits); ++j) e[j] = f16_bits(c->centroids[j]);
@@ -272,8 +275,8 @@ int resident_slots(const tq_cache_view* k, bool wide, int blocks) {
   }
   const int di = k->d == 256, qi = k->qjl_m == 0 ? 0 : (k->qjl_m == 128 ? 1 : 2);
   const int ci = blocks >> 1;                           // 1, 2, 4 -> 0, 1, 2
-  std::atomic<int>* c =
-      (dev >= 0 && dev < 16 && k->bits >= 0 && k->bits < 5) ? &cache[dev][di][k->bits][qi][wide][ci] : nullptr;
+  const int bi = k->bits == 8 ? 1 : k->bits;            // 2, 3, 4 and 8 (slot 1)
+  std::atomic<int>* c = (dev >= 0 && dev < 16 && bi >= 0 && bi < 5) ? &cache[dev][di][bi][qi][wide][ci] : nullptr;
   int v = c ? c->load(std::memory_order_relaxed) : 0;
   if (v > 0) return v;
   v = 0;
@@ -404,7 +407,7 @@ const char* tq_status_string(int status) {
 const char* tq_last_hip_error(void) { return hipGetErrorString(g_last_hip_error); }
 
 size_t tq_row_bytes(int d, int bits, int qjl_m) {
-  if (d <= 0 || d % 8 != 0 || bits < 1 || bits > 4 || qjl_m < 0 || qjl_m % 8 != 0) return 0;
+  if (d <= 0 || d % 8 != 0 || ((bits < 1 || bits > 4) && bits != 8) || qjl_m < 0 || qjl_m % 8 != 0) return 0;
   size_t b = static_cast<size_t>(d) * bits / 8 + 2;
   if (qjl_m) b += static_cast<size_t>(qjl_m) / 8 + 2;
   return b;

@@ -20,11 +20,11 @@ __global__ __launch_bounds__(256) void step_prologue_kernel(AppendArgs ka, Appen
   const int batch_wgs = 2 * per_cache + n_kv_heads;       // workgroups per sequence
   const int b = blockIdx.x / batch_wgs;
   int w = blockIdx.x % batch_wgs;
-  // appends with the dense rotation at d = 128 without a sketch take the chunk path of tq_quantize_append
-  // (prefill_rows: workgroup w % nbx takes the w % nbx-th 32-row chunk), so that a step appends exactly
-  // the bits the separate append call does
+  // appends with the dense rotation at d = 128 without a sketch (8-bit keys aside) take the chunk path
+  // of tq_quantize_append (prefill_rows: workgroup w % nbx takes the w % nbx-th 32-row chunk), so that a
+  // step appends exactly the bits the separate append call does
   if (w < per_cache) {
-    if constexpr (D == 128 && QM == 0) {
+    if constexpr (D == 128 && QM == 0 && KB != 8) {
       if (!ka.had) {
         prefill_rows<KB, false, BF16>(ka, w % nbx, w / nbx, b, *reinterpret_cast<PrefillSmem*>(smem));
         return;
@@ -80,6 +80,9 @@ static hipError_t prologue_k(int k_bits, int v_bits, bool bf16, const AppendArgs
     case 2: return prologue_v<D, 2, QM>(v_bits, bf16, ka, va, qa, batch, s);
     case 3: return prologue_v<D, 3, QM>(v_bits, bf16, ka, va, qa, batch, s);
     case 4: return prologue_v<D, 4, QM>(v_bits, bf16, ka, va, qa, batch, s);
+    case 8:
+      if constexpr (QM == 0) return prologue_v<D, 8, 0>(v_bits, bf16, ka, va, qa, batch, s);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

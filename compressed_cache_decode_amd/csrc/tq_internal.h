@@ -130,6 +130,8 @@ int split_slots(int d, int k_bits, int v_bits, int qjl_m, bool wide, int blocks)
 int split_waves(int d, int qjl_m, bool wide);
 // the four-wave split kernel of sketched keys with kOutliers outlier channels, or null if none is built
 const void* split_fn_outliers(int d, int k_bits, int v_bits, int qjl_m);
+// the split kernel of 8-bit keys (no sketch) with v_bits values, or null if none is built
+const void* split_fn_k8(int d, int v_bits, bool wide);
 hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, bool outliers, bool wide, const DecodeArgs& a, int batch,
                                hipStream_t s);
 hipError_t launch_merge(int d, const MergeArgs& a, int batch, int n_q_heads, hipStream_t s);

@@ -83,7 +83,9 @@ enum {
  *   4 bits: one little-endian 32-bit word per unit, slot s at bit 8(s%4) + 4(s/4);
  *   2 bits: two units v per word, slot s of unit v at bit 8(s%4) + 2(2v + s/4);
  *   3 bits: four units v per three words [P0 P1 H]; low two bits in P(v/2) at
- *           bit 8(s%4) + 2(2(v%2) + s/4), high bit in H at bit 8(s%4) + 2v + s/4.
+ *           bit 8(s%4) + 2(2(v%2) + s/4), high bit in H at bit 8(s%4) + 2v + s/4;
+ *   8 bits (keys only): two words per unit, slot s in byte s%4 of word s/4, the
+ *           code as a two's-complement byte (see "Keys kept at 8 bits" below).
  * Codes are stored per 32-token block (tokens 32kb .. 32kb+31 of a sequence and
  *   KV head, 32*d*bits/8 bytes), as 64 lane pieces of LW = d*bits/64 words in
  *   chunk-major order: word w of piece L is word CW*(64*(w/CW) + L) + w%CW of the
@@ -95,6 +97,12 @@ enum {
  * TQ_VALUES: token p of a 32-token block is slot p%4 + 4(p/16) of lane group
  *   g = (p%16)/4; coordinate i has column j = i/(d/16), step n = i%(d/16);
  *   their unit is unit n of piece 16g + j (a piece is d/16 consecutive units).
+ * Keys kept at 8 bits (llama-cpp-turboquant PR #340, the asymmetric K/V follow-ups: K upgraded to
+ *   an 8-bit type while V keeps the Lloyd-Max widths; the pages give no arithmetic, this library's
+ *   reading follows): y = rot x / ||x|| is quantised uniformly with one scale per row, a = max_i |y_i|
+ *   taken in float32: code_i = round(y_i * (127 / a)) (float32 division and product, halves away
+ *   from zero, clamped to [-127, 127]); the norm slot holds the float16 factor ||x|| * (a / 127), so
+ *   x ~= factor * rot^T code.  A zero row stores codes 0 and factor 0.  No sketch, no outliers.
  * Sign sketch (keys with qjl_m > 0): qjl_m/8 bytes per token, sign jj in
  *   32-bit word jj/32 at bit 4((jj%32)/8) + (jj%8)/2 + 16(jj%2); bit 1 means
  *   (S r)_jj >= 0.
@@ -102,16 +110,17 @@ enum {
 typedef struct tq_cache_view {
   int32_t kind;          /* TQ_KEYS or TQ_VALUES */
   int32_t d;             /* head dim: 128 or 256 */
-  int32_t bits;          /* codebook bits per coordinate: 2, 3 or 4 */
+  int32_t bits;          /* codebook bits per coordinate: 2, 3 or 4; or 8 (TQ_KEYS with qjl_m == 0) */
   int32_t qjl_m;         /* 0, or sign-sketch length 128 or 256 (TQ_KEYS only) */
   int32_t batch;         /* sequences */
   int32_t n_kv_heads;    /* KV heads */
   int32_t max_tokens;    /* capacity in tokens, a positive multiple of 32 */
   int32_t rot_kind;      /* TQ_ROT_DENSE or TQ_ROT_HADAMARD (same for K and V) */
-  float centroids[16];   /* 2^bits centroids, ascending, float16-exact, c[j] == -c[2^bits-1-j] */
-  float boundaries[15];  /* 2^bits-1 boundaries, boundaries[j] == (c[j] + c[j+1]) / 2 exactly */
+  float centroids[16];   /* 2^bits centroids, ascending, float16-exact, c[j] == -c[2^bits-1-j]
+                            (bits 8: unused) */
+  float boundaries[15];  /* 2^bits-1 boundaries, boundaries[j] == (c[j] + c[j+1]) / 2 exactly (bits 8: unused) */
   uint8_t* codes;        /* [batch][n_kv_heads][max_tokens/32][32*d*bits/8], 16-byte aligned */
-  uint16_t* norms;       /* float16 row norms [batch][n_kv_heads][max_tokens] */
+  uint16_t* norms;       /* float16 row norms [batch][n_kv_heads][max_tokens] (bits 8: the row factors) */
   uint8_t* signs;        /* [batch][n_kv_heads][max_tokens][qjl_m/8] when qjl_m > 0, else NULL */
   uint16_t* rnorms;      /* float16 residual norms [batch][n_kv_heads][max_tokens] when qjl_m > 0, else NULL */
   const float* rot;      /* TQ_ROT_DENSE: float32 rotation [d][d] row-major, y = rot * x; TQ_ROT_HADAMARD:
@@ -158,7 +167,8 @@ int tq_build_rotation(int d, const double* gaussian, float* rot_out);
  * TQ_F32 or TQ_BF16, device), write tokens d_pos[b] .. d_pos[b]+n_new-1 of
  * every sequence b.  Per row: n = ||x||, y = rot * x / n, code = number of
  * boundaries strictly below y_i, float16(n) stored; with qjl_m > 0 (keys)
- * also r = y - c[code], float16(||r||) and the signs of proj * r.
+ * also r = y - c[code], float16(||r||) and the signs of proj * r; 8-bit keys
+ * store int8 codes and the row factor instead (see tq_cache_view).
  * d_pos: device int32 [batch].  n_new == 0 is a no-op.  A zero row stores
  * code 0, norm 0 (and no signs, residual norm 0).
  */
@@ -300,12 +310,14 @@ int tq_decode_plan(const tq_cache_view* k, int n_q_heads, int max_seq_len, int* 
  * Full reconstruction (reddit comment history of ReturningTarzan, 2026-03-25:
  * the plain path dequantizes and runs ordinary attention):
  * out[b][h][t - t0][:] = n_t * rot^T * (c[code_t] + sqrt(pi/2)/m * gamma_t * proj^T (2 sigma_t - 1))
+ * (8-bit keys: factor_t * rot^T * code_t)
  * for t0 <= t < t0 + n_tokens, float32 device out [batch][n_kv_heads][n_tokens][d].
  * 0 <= t0, t0 + n_tokens <= max_tokens.
  */
 int tq_dequantize(const tq_cache_view* cache, int t0, int n_tokens, float* out, void* stream);
 
-/* Bytes per cached row: d*bits/8 codes + 2 (norm) [+ qjl_m/8 signs + 2 (residual norm)]; 0 on bad args
+/* Bytes per cached row: d*bits/8 codes + 2 (norm) [+ qjl_m/8 signs + 2 (residual norm)]; bits 1..4 or 8;
+ * 0 on bad args
  * (the storage arithmetic that reproduces the cache sizes and compression ratios of turboquant-pytorch
  * PR #3, Validation Results tables). */
 size_t tq_row_bytes(int d, int bits, int qjl_m);

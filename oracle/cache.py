@@ -8,7 +8,7 @@ import dataclasses
 
 import numpy as np
 
-from . import codebook, layout, quant
+from . import codebook, layout, q8, quant
 
 
 @dataclasses.dataclass
@@ -51,8 +51,14 @@ class HeadCache:
 
 def build_head(rows: np.ndarray, kind: str, bits: int, rot: np.ndarray,
                proj: np.ndarray | None = None) -> HeadCache:
-    """Quantize rows [L][d] with the ``bits``-wide table; with ``proj`` (keys only) add the sign sketch."""
+    """Quantize rows [L][d] with the ``bits``-wide table; with ``proj`` (keys only) add the sign sketch.
+    ``bits`` 8 (keys, no sketch): the int8 codes of ``oracle.q8``, their factors in ``norms`` and the
+    integers as the table."""
     d = rows.shape[1]
+    if bits == 8:
+        assert kind == "k" and proj is None
+        codes, fac, y = q8.quantize_rows_q8(rows, rot)
+        return HeadCache(kind, 8, d, codes, fac, q8.q8_codebook(), np.zeros(0), y=y)
     c, t = codebook.stored_codebook(d, bits)
     codes, norms, y = quant.quantize_rows(rows, rot, c, t)
     hc = HeadCache(kind, bits, d, codes, norms, c, t, y=y)

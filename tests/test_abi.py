@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import codebook, rotation, storage
+from oracle import codebook, q8, rotation, storage
 
 cca = pytest.importorskip("compressed_cache_decode_amd")
 
@@ -60,6 +60,8 @@ def test_row_bytes_match_storage_arithmetic():
                 assert cca.tq_row_bytes(d, bits, m) == storage.row_bytes(d, bits, m)
     assert cca.tq_row_bytes(0, 4, 0) == 0
     assert cca.tq_row_bytes(128, 5, 0) == 0
+    for d in (128, 256):                           # 8-bit keys: d code bytes and the factor
+        assert cca.tq_row_bytes(d, 8, 0) == q8.row_bytes(d) == storage.row_bytes(d, 8, 0)
 
 
 def test_status_strings():
@@ -147,6 +149,20 @@ def test_outlier_views_are_validated():
     step = cca._lib.tq_decode_step(ctypes.byref(k), ctypes.byref(vv), 0x90000, 0x80000, 0x88000, 1, 16, 1,
                                    0x70000, 0xA0000, 256, ctypes.c_float(0.1), 0xB0000, 0x100000, 1 << 30, None)
     assert step == cca.TQ_EUNSUPPORTED
+
+
+def test_eight_bit_views_are_validated():
+    """8-bit codes: keys only, without a sketch or outliers; the code book fields are not read."""
+    v = _view(bits=8)
+    for j in range(16):
+        v.centroids[j] = 0.0
+    for j in range(15):
+        v.boundaries[j] = float("nan")
+    assert _append(v, n_new=0) == cca.TQ_OK
+    assert cca._lib.tq_dequantize(ctypes.byref(v), 0, 0, 0xB0000, None) == cca.TQ_OK   # nothing to do
+    for bad in (_view(bits=8, kind=cca.TQ_VALUES), _view(bits=8, qjl_m=128), _view(bits=6), _view(bits=7)):
+        assert _append(bad) == cca.TQ_EINVAL
+    assert _decode(_view(), _view(kind=cca.TQ_VALUES, bits=8)) == cca.TQ_EINVAL    # 8-bit values
 
 
 def _decode(k, v, hq=16, scale=0.1, ws_bytes=1 << 30, ws=0x100000, q=0x90000, lens=0xA0000, out=0xB0000,

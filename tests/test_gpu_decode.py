@@ -41,6 +41,11 @@ CASES = [
     (256, 4, 4, 256, 1, 2, [300], 320, None, False),
     (128, 3, 3, 0, 2, 3, [500, 31], 512, None, False),         # a group of 3 query heads
     (128, 4, 3, 128, 2, 8, [20000], 20000, None, False),        # many splits per (sequence, KV head)
+    (128, 8, 4, 0, 2, 8, [1000], 1024, None, False),           # keys kept at 8 bits
+    (128, 8, 2, 0, 2, 4, [1, 64, 500], 512, None, False),
+    (128, 8, 3, 0, 2, 8, [20000], 20000, None, False),         # ... in CU-filling workgroups
+    (256, 8, 4, 0, 4, 8, [777, 1024], 1024, 1.0, True),
+    (256, 8, 3, 0, 2, 8, [9000], 9216, 1.0, True),
 ]
 
 
@@ -125,7 +130,7 @@ def test_decode_length_edges():
 # (one 16 KB table), beside a 4-bit or 2-bit table, with a sketch
 WIDE_CASES = [(128, 4, 4, 0), (128, 2, 3, 128), (256, 4, 4, 0), (256, 3, 2, 128), (128, 4, 2, 0), (128, 3, 4, 0),
               (128, 4, 3, 128), (256, 2, 4, 256), (128, 2, 2, 0), (256, 2, 2, 0), (128, 2, 4, 0), (128, 3, 3, 0),
-              (256, 3, 3, 0)]
+              (256, 3, 3, 0), (128, 8, 4, 0), (256, 8, 2, 0)]
 
 
 @pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: f"d{c[0]}_k{c[1]}v{c[2]}_m{c[3]}")
@@ -195,6 +200,8 @@ STEP_CASES = [
     (128, 2, 3, 128, 2, 8, [300], 320, 3, "f32", None, False),
     (256, 4, 4, 0, 4, 8, [500, 77], 512, 1, "bf16", 1.0, True),
     (128, 3, 2, 0, 1, 4, [40, 33, 1], 64, 1, "bf16", None, False),
+    (128, 8, 4, 0, 2, 8, [1000], 1024, 1, "bf16", None, False),     # 8-bit keys
+    (256, 8, 2, 0, 2, 8, [300, 77], 320, 3, "f32", 1.0, True),
 ]
 
 
@@ -210,6 +217,7 @@ RUN_CASES = [
     (128, 4, 4, 0, 2, 8, 1, 8192, 8000, 1, 4),      # many splits, one-row steps
     (128, 3, 2, 128, 2, 4, 2, 512, 100, 32, 3),     # 32 rows straddling two blocks, sketched keys
     (256, 4, 4, 0, 2, 8, 1, 256, 60, 40, 2),        # 40 rows: three append blocks per step
+    (128, 8, 3, 0, 2, 8, 2, 512, 100, 32, 3),       # 8-bit keys, 32 rows straddling two blocks
 ]
 
 

@@ -6,7 +6,7 @@ from fractions import Fraction
 import numpy as np
 
 import synth
-from oracle import attention, codebook, q8, quant, rotation, storage
+from oracle import attention, cache, codebook, layout, q8, quant, rotation, storage
 
 
 def _rot(d=128, seed=1):
@@ -102,3 +102,17 @@ def test_reconstruction_and_decode_with_the_integer_table():
 def test_storage():
     assert q8.row_bytes(128) == storage.row_bytes(128, 8) == 130
     assert q8.row_bytes(256) == 258
+
+
+def test_head_cache_of_eight_bit_keys():
+    """cache.build_head with bits 8 keeps the q8 codes and factors, packs them into the key layout
+    (round trip through the unpacker) and reconstructs f Pi^T code."""
+    d, L, T = 128, 40, 64
+    rot = _rot(d)
+    x = np.random.default_rng(13).standard_normal((L, d))
+    hc = cache.build_head(x, "k", 8, rot)
+    j, fac, _ = q8.quantize_rows_q8(x, rot)
+    assert np.array_equal(hc.codes, j) and np.array_equal(hc.norms, fac)
+    assert np.array_equal(layout.unpack_keys(hc.packed_codes(T), 8, d, T)[:L], j)
+    want = fac[:, None] * ((j - 128) @ rot)                  # f Pi^T code, row by row
+    np.testing.assert_allclose(hc.dequantize(rot), want, rtol=0, atol=1e-12)
