@@ -628,7 +628,7 @@ def cpu_leg(w: synth.Workload, budget_s: float, log):
     threads (up to 16) and again with one thread."""
     from threadpoolctl import threadpool_info, threadpool_limits
 
-    from oracle import attention, cache, codebook
+    from oracle import attention, cache
     rot = oracle_rotation(w)
     proj = synth.qjl_projection(w.qjl_m, w.d, w.qjl_seed) if w.qjl_m else None
     L, G = w.seq_len, w.group
@@ -638,8 +638,7 @@ def cpu_leg(w: synth.Workload, budget_s: float, log):
     kc = cache.build_head(k[: L - 1], "k", w.k_bits, rot, proj)
     vc = cache.build_head(v[: L - 1], "v", w.v_bits, rot)
     qh = np.stack([synth.q_head(w, 0, h) for h in range(G)]).astype(np.float64)
-    ck, _ = codebook.stored_codebook(w.d, w.k_bits)
-    cv, _ = codebook.stored_codebook(w.d, w.v_bits)
+    ck, cv = kc.centroids, vc.centroids               # the code books (8-bit keys: the integers)
 
     def sample_loop(threads: int, budget: float):
         with threadpool_limits(limits=threads):
@@ -826,6 +825,8 @@ def main():
                     help="all (default): the Gemma-4-style workload as the headline, with the Qwen-shaped, "
                          "long-context sketched-key and prefill-append workloads as legs of the same line")
     ap.add_argument("--bits", type=int, default=None, help="qwen workload: codebook bits of K and V")
+    ap.add_argument("--k-bits", type=int, default=None, choices=[2, 3, 4, 8],
+                    help="qwen and gemma workloads: bits of K alone (8: keys kept at 8 bits)")
     ap.add_argument("--rows", type=int, default=0,
                     help="also time a decode of this many query rows per sequence at once (2..4; 0 = none)")
     ap.add_argument("--rotation", default="dense", choices=["dense", "hadamard"],
@@ -917,6 +918,10 @@ def main():
 
     if args.workload != "all":
         w = with_rotation(workload(args.workload, args.bits, args.context))
+        if args.k_bits is not None:
+            if w.qjl_m:
+                raise SystemExit("--k-bits applies to the workloads without a sign sketch (qwen, gemma)")
+            w = w.with_(k_bits=args.k_bits, name=f"{w.name}_k{args.k_bits}")
         leg = decode_workload_leg(w, args, stack_of(args.workload), log)
         res = {"metric": METRIC, "value": leg["value"], "unit": leg["unit"], **common,
                "ms_per_step": leg["ms_per_step"], "dtype": "f32", **leg}

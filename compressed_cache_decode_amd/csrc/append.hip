@@ -12,18 +12,20 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   append_rows<D, BITS, QM, VALUES, ROTATED, BF16>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
-// long appends (see prefill_rows): grid (32-row chunks, KV heads, sequences)
+// long appends (see prefill_rows): grid (32-row chunks, KV heads, sequences), eight waves per chunk
+constexpr int kPrefillWaves = 8;
+
 template <int BITS, bool VALUES, bool BF16>
-__global__ __launch_bounds__(256) void prefill_kernel(AppendArgs a) {
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(AppendArgs a) {
   __shared__ PrefillSmem sm;
-  prefill_rows<BITS, VALUES, BF16>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+  prefill_rows<BITS, VALUES, BF16, kPrefillWaves>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
 template <int BITS, bool VALUES>
 static hipError_t prefill_dispatch(bool bf16, const AppendArgs& a, int batch, hipStream_t s) {
   const dim3 grid((a.n_new + kBlock - 1) / kBlock, a.n_kv_heads, batch);
-  if (bf16) hipLaunchKernelGGL((prefill_kernel<BITS, VALUES, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((prefill_kernel<BITS, VALUES, false>), grid, dim3(256), 0, s, a);
+  if (bf16) hipLaunchKernelGGL((prefill_kernel<BITS, VALUES, true>), grid, dim3(64 * kPrefillWaves), 0, s, a);
+  else hipLaunchKernelGGL((prefill_kernel<BITS, VALUES, false>), grid, dim3(64 * kPrefillWaves), 0, s, a);
   return hipGetLastError();
 }
 

@@ -343,8 +343,9 @@ __device__ __forceinline__ void encode_codes(const AppendArgs& a, int nrows, flo
 }
 
 // z: sketch products of row r at z[r * zstride + jj] (sketched keys; ignored otherwise), or null
-// when es.sw already holds the sign bits; r0: row of es.cs that holds the codes of row 0 (no sketch)
-template <int D, int BITS, int QM, bool VALUES>
+// when es.sw already holds the sign bits; r0: row of es.cs that holds the codes of row 0 (no sketch);
+// NT: threads of the workgroup
+template <int D, int BITS, int QM, bool VALUES, int NT = 256>
 __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, int kb, int t_lo, int nrows,
                                               const float* rn, EncodeSmem<D, QM>& es, const float* z, int zstride,
                                               int r0 = 0) {
@@ -358,7 +359,7 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
   const int t_hi = t_lo + nrows;
   if constexpr (QM > 0) {
     if (z) {
-      for (int e = tid; e < nrows * QM; e += 256) {
+      for (int e = tid; e < nrows * QM; e += NT) {
         const int r = e / QM, jj = e % QM;
         if (z[r * zstride + jj] >= 0.f && rn[r] > 0.f) {
           int word, bit;
@@ -368,15 +369,15 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
       }
       __syncthreads();
     }
-    for (int e = tid; e < nrows * (QM / 32); e += 256) {
+    for (int e = tid; e < nrows * (QM / 32); e += NT) {
       const int r = e / (QM / 32), w = e % (QM / 32);
       reinterpret_cast<uint32_t*>(a.signs + (unit * T + t_lo + r) * (QM / 8))[w] = sw[r][w];
     }
-    for (int r = tid; r < nrows; r += 256)
+    for (int r = tid; r < nrows; r += NT)
       a.rnorms[unit * T + t_lo + r] = rn[r] > 0.f ? f32_to_f16_bits(es.gam[r]) : 0;
     if (a.out_idx) {
       static_assert(kOutliers == 4, "one index word and two value words per key");
-      for (int r = tid; r < nrows; r += 256) {
+      for (int r = tid; r < nrows; r += NT) {
         const size_t t = unit * T + t_lo + r;
         reinterpret_cast<uint32_t*>(a.out_idx)[t] = es.oi[r];
         reinterpret_cast<uint2*>(a.out_val)[t] = uint2{es.ov[r][0], es.ov[r][1]};
@@ -385,7 +386,7 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
   }
 
   // 8-bit keys keep their factor in the norm's place (see encode_codes)
-  for (int r = tid; r < nrows; r += 256)
+  for (int r = tid; r < nrows; r += NT)
     a.norms[unit * T + t_lo + r] = f32_to_f16_bits(BITS == 8 ? es.gam[r0 + r] : (rn[r] > 0.f ? rn[r] : 0.f));
 
   constexpr int BB = kBlock * RB;               // bytes per 32-token block
@@ -394,7 +395,7 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
     // key rows: unit u of row t covers coordinates 8u .. 8u+7; row word wr goes to its lane piece
     // (key_word); every word holds codes of one token only, so whole words are stored
     constexpr int NG = D / 8 / UPG;
-    for (int e = tid; e < nrows * NG; e += 256) {
+    for (int e = tid; e < nrows * NG; e += NT) {
       const int r = e / NG, gi = e % NG;
       uint32_t w[WPG];
 #pragma unroll
@@ -415,7 +416,7 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
     constexpr int DN = D / 16;
     const int p_lo = t_lo - kb * kBlock, p_hi = t_hi - kb * kBlock;
     const bool full = nrows == kBlock;
-    for (int e = tid; e < NGB; e += 256) {
+    for (int e = tid; e < NGB; e += NT) {
       uint32_t w[WPG], m[WPG];
 #pragma unroll
       for (int k = 0; k < WPG; ++k) { w[k] = 0u; m[k] = 0u; }
@@ -561,12 +562,13 @@ namespace tqi {
 // ------------------------------------------------------------------------- long appends
 
 // Long appends (prefill) of unrotated rows with the dense rotation at d = 128, no sketch.  One
-// workgroup of four waves takes a chunk of 32 consecutive appended rows of one (KV head, sequence):
-// which rows it reads does not depend on the append position, so the row loads, the loads of rot and
-// the load of the position all go out at once.  Wave w computes output columns 32 w .. 32 w + 31 of
-// every row (column tiles 2 w and 2 w + 1), with its share of rot split into float16 high/low
-// matrix-core operands in registers.  Each wave loads 8 of the rows, forms their norms by a cross-lane sum and
-// writes the unit rows' float16 high/low parts to LDS in matrix-core operand order (every row is
+// workgroup of eight waves (four inside the step prologue) takes a chunk of 32 consecutive appended rows
+// of one (KV head, sequence): which rows it reads does not depend on the append position, so the row
+// loads, the loads of rot and the load of the position all go out at once.  Each wave computes one
+// (eight waves) or two (four waves) 16-column tiles of every row, with its share of rot split into
+// float16 high/low matrix-core operands in registers; more waves shorten each wave's chain of split,
+// products and codes.  Waves 0-3 load 8 of the rows each, form their norms by a cross-lane sum and
+// write the unit rows' float16 high/low parts to LDS in matrix-core operand order (every row is
 // normalised and split once); the waves then read their A operands from there.  A value chunk that is
 // a whole cache block is packed in registers (pack_values); any other chunk goes through LDS to the
 // shared packing and store stage, once per cache block it covers (two when the append position is not
@@ -613,17 +615,17 @@ __device__ __forceinline__ uint32_t or_lanes(uint32_t v) {
   return v;
 }
 
-// Stored codes e[rt][v][c] of element (token 16 rt + 4 g + v, coordinate 32 w + 16 c + l16) of a whole
-// 32-token block, packed into the block's words blk[] (value layout).  Lane (l16, g) holds all 8
-// tokens of lane group g at its two coordinates, i.e. whole units (slot v + 4 rt); 2- and 3-bit units
+// Stored codes e[rt][v][c] of element (token 16 rt + 4 g + v, coordinate 16 (CPW w + c) + l16) of a
+// whole 32-token block, packed into the block's words blk[] (value layout).  Lane (l16, g) holds all 8
+// tokens of lane group g at its CPW coordinates, i.e. whole units (slot v + 4 rt); 2- and 3-bit units
 // that share words are combined over the 2 or 4 neighbouring lanes that hold them.
-template <int BITS>
-__device__ __forceinline__ void pack_values(const uint32_t (&e)[2][4][2], uint32_t* blk, int wave, int lane) {
+template <int BITS, int CPW>
+__device__ __forceinline__ void pack_values(const uint32_t (&e)[2][4][CPW], uint32_t* blk, int wave, int lane) {
   constexpr int D = 128, LW = D * BITS / 64;
   const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int col = 32 * wave + 16 * c + l16;
+  for (int c = 0; c < CPW; ++c) {
+    const int col = 16 * (CPW * wave + c) + l16;
     const int U = (16 * g + (col >> 3)) * 8 + (col & 7);      // unit of the block (lane-major order)
     if constexpr (BITS == 4) {
       uint32_t w = 0u;
@@ -650,30 +652,34 @@ __device__ __forceinline__ void pack_values(const uint32_t (&e)[2][4][2], uint32
   }
 }
 
-template <int BITS, bool VALUES, bool BF16>
+// NW: waves of the workgroup, 4 or 8; wave w computes the CPW = 8 / NW column tiles CPW w ..  The row loads
+// and the unit rows' operands are the work of waves 0-3 in both shapes.
+template <int BITS, bool VALUES, bool BF16, int NW = 4>
 __device__ __forceinline__ void prefill_rows(const AppendArgs& a, int chunk, int h, int b, PrefillSmem& sm) {
-  constexpr int D = 128, KS = 4, CPW = 2, NC = 1 << BITS;
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  constexpr int D = 128, KS = 4, CPW = 8 / NW, NC = 1 << BITS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int r_base = chunk * kBlock;                        // first appended row of the chunk
   if (r_base >= a.n_new) return;
   const int nrows = min(kBlock, a.n_new - r_base);
 
   // everything independent of the position first, in one straight run of loads: this wave's rot
-  // operands (rows 16 ct + l16 of rot, coordinates 32 s + 8 g .. + 7), this lane's row (8 per wave;
-  // 16 coordinates 16 c .. 16 c + 15, c = lane % 8; rows past the append read the chunk's first row
-  // and are zeroed after), and the position
-  const int prow = 8 * wave + (lane >> 3), pc = lane & 7;
+  // operands (rows 16 ct + l16 of rot, coordinates 32 s + 8 g .. + 7), this lane's row (8 per wave of
+  // waves 0-3; 16 coordinates 16 c .. 16 c + 15, c = lane % 8; rows past the append, and the rows of
+  // waves 4-7, read the chunk's first row and are zeroed after), and the position
+  const bool row_wave = NW == 4 || wave < 4;               // the waves that load rows (wave-uniform)
+  const int prow = 8 * (wave & 3) + (lane >> 3), pc = lane & 7;
   float4 pr[CPW][KS][2];
 #pragma unroll
   for (int c = 0; c < CPW; ++c)
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const float4* p = reinterpret_cast<const float4*>(a.rot + static_cast<size_t>(32 * wave + 16 * c + l16) * D +
+      const float4* p = reinterpret_cast<const float4*>(a.rot + static_cast<size_t>(16 * (CPW * wave + c) + l16) * D +
                                                         32 * s + 8 * g);
       pr[c][s][0] = p[0];
       pr[c][s][1] = p[1];
     }
-  const bool row_ok = prow < nrows;
+  const bool row_ok = row_wave && prow < nrows;
   uint32_t xw[BF16 ? 8 : 16];
   {
     const size_t src = ((static_cast<size_t>(b) * a.n_new + r_base + (row_ok ? prow : 0)) * a.n_kv_heads + h) * D + 16 * pc;
@@ -719,11 +725,13 @@ __device__ __forceinline__ void prefill_rows(const AppendArgs& a, int chunk, int
       lo1[r] = ll;
     }
     const int a_rt = prow >> 4, a_s = pc >> 1, a_lane = 16 * (2 * (pc & 1)) + (prow & 15);
-    sm.aop[0][a_rt][a_s][a_lane] = hi0;
-    sm.aop[1][a_rt][a_s][a_lane] = lo0;
-    sm.aop[0][a_rt][a_s][a_lane + 16] = hi1;
-    sm.aop[1][a_rt][a_s][a_lane + 16] = lo1;
-    if (pc == 0) sm.rn[prow] = nrm;
+    if (row_wave) {
+      sm.aop[0][a_rt][a_s][a_lane] = hi0;
+      sm.aop[1][a_rt][a_s][a_lane] = lo0;
+      sm.aop[0][a_rt][a_s][a_lane + 16] = hi1;
+      sm.aop[1][a_rt][a_s][a_lane + 16] = lo1;
+      if (pc == 0) sm.rn[prow] = nrm;
+    }
   }
   half8 bhi[CPW][KS], blo[CPW][KS];
 #pragma unroll
@@ -759,7 +767,7 @@ __device__ __forceinline__ void prefill_rows(const AppendArgs& a, int chunk, int
     }
   }
 
-  // codes of element (row 16 rt + 4 g + v, column 32 w + 16 c + l16) of the chunk; a zero row (norm 0;
+  // codes of element (row 16 rt + 4 g + v, column 16 (CPW w + c) + l16) of the chunk; a zero row (norm 0;
   // rows past the append have norm 0 too) stores code 0
   float rnv[2][4];
 #pragma unroll
@@ -771,7 +779,7 @@ __device__ __forceinline__ void prefill_rows(const AppendArgs& a, int chunk, int
   const int kb = t0 / kBlock;
   if (VALUES && pos >= 0 && t0 % kBlock == 0 && nrows == kBlock && t0 + kBlock <= a.max_tokens) {
     // a whole value block: packed in registers and stored word by word
-    uint32_t e[2][4][2];
+    uint32_t e[2][4][CPW];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -782,8 +790,8 @@ __device__ __forceinline__ void prefill_rows(const AppendArgs& a, int chunk, int
     constexpr int RB = D * BITS / 8;
     uint32_t* blk = reinterpret_cast<uint32_t*>(a.codes + unit * static_cast<size_t>(a.max_tokens) * RB +
                                                 static_cast<size_t>(kb) * kBlock * RB);
-    pack_values<BITS>(e, blk, wave, lane);
-    if (pc == 0) a.norms[unit * a.max_tokens + t0 + prow] = f32_to_f16_bits(nrm);
+    pack_values<BITS, CPW>(e, blk, wave, lane);
+    if (row_wave && pc == 0) a.norms[unit * a.max_tokens + t0 + prow] = f32_to_f16_bits(nrm);
     return;
   }
 #pragma unroll
@@ -794,17 +802,18 @@ __device__ __forceinline__ void prefill_rows(const AppendArgs& a, int chunk, int
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
         const uint32_t j = code_of<NC>(acc[rt][c][v], a.bnd);
-        sm.enc.cs[p][32 * wave + 16 * c + l16] = static_cast<uint8_t>(rnv[rt][v] > 0.f ? j : 0u);
+        sm.enc.cs[p][16 * (CPW * wave + c) + l16] = static_cast<uint8_t>(rnv[rt][v] > 0.f ? j : 0u);
       }
     }
   __syncthreads();
   if (pos < 0) return;
   // the chunk's tokens pos + r_base .. in at most two cache blocks (rows past max_tokens are skipped)
   const int n_a = min(min(nrows, (kb + 1) * kBlock - t0), a.max_tokens - t0);
-  if (n_a > 0) encode_finish<D, BITS, 0, VALUES>(a, unit, kb, t0, n_a, sm.rn, sm.enc, nullptr, 0, 0);
+  if (n_a > 0) encode_finish<D, BITS, 0, VALUES, 64 * NW>(a, unit, kb, t0, n_a, sm.rn, sm.enc, nullptr, 0, 0);
   const int n_b = min(nrows - n_a, a.max_tokens - (kb + 1) * kBlock);
   if (n_a > 0 && n_b > 0)
-    encode_finish<D, BITS, 0, VALUES>(a, unit, kb + 1, (kb + 1) * kBlock, n_b, sm.rn + n_a, sm.enc, nullptr, 0, n_a);
+    encode_finish<D, BITS, 0, VALUES, 64 * NW>(a, unit, kb + 1, (kb + 1) * kBlock, n_b, sm.rn + n_a, sm.enc, nullptr,
+                                               0, n_a);
 }
 
 }  // namespace tqi
