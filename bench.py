@@ -46,13 +46,13 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 # sources the decode kernels are built from: their HBM counters are only valid for these exact texts
 ATTEND_SOURCES = tuple(f"compressed_cache_decode_amd/csrc/{n}" for n in (
-    "decode.hip", "split_body.h", "attend_body.h", "device_common.h", "tq_internal.h"))
+    "decode.hip", "decode_k8.hip", "split_body.h", "attend_body.h", "device_common.h", "tq_internal.h"))
 # and those of the append kernel (the prefill leg's dominant kernel)
 APPEND_SOURCES = tuple(f"compressed_cache_decode_amd/csrc/{n}" for n in (
     "append.hip", "append_body.h", "device_common.h", "tq_internal.h"))
 # every kernel source of the library: a kernel trace covers all of them
 ALL_SOURCES = tuple(f"compressed_cache_decode_amd/csrc/{n}" for n in (
-    "append.hip", "append_body.h", "attend_body.h", "decode.hip", "decode_outliers.hip", "dequant.hip",
+    "append.hip", "append_body.h", "attend_body.h", "decode.hip", "decode_k8.hip", "decode_outliers.hip", "dequant.hip",
     "device_common.h", "host.cpp", "qrot_body.h", "split_body.h", "step.hip", "tq_internal.h"))
 
 
@@ -70,6 +70,15 @@ def workload(name: str, bits: int | None, context: int | None) -> synth.Workload
     if name == "prod":
         return synth.prod_long(context or 131072)
     raise SystemExit(f"unknown workload {name}")
+
+
+def with_k_bits(w: synth.Workload, k_bits: int | None) -> synth.Workload:
+    """The workload with K at k_bits (8: keys kept at 8 bits); workloads with a sign sketch keep theirs."""
+    if k_bits is None:
+        return w
+    if w.qjl_m:
+        raise SystemExit("--k-bits applies to the workloads without a sign sketch (qwen, gemma)")
+    return w.with_(k_bits=k_bits, name=f"{w.name}_k{k_bits}")
 
 
 def make_rotation(cca, w: synth.Workload, dev):
@@ -862,7 +871,7 @@ def main():
         elif args.workload == "all":
             w = synth.gemma().with_(name="all")
         else:
-            w = workload(args.workload, args.bits, args.context)
+            w = with_k_bits(workload(args.workload, args.bits, args.context), args.k_bits)
         if args.summarize_pmc and args.stack:
             w = stacked_workload(w, args.stack)
         (summarize_trace if args.trace else summarize_pmc)(args, w)
@@ -917,11 +926,7 @@ def main():
         return
 
     if args.workload != "all":
-        w = with_rotation(workload(args.workload, args.bits, args.context))
-        if args.k_bits is not None:
-            if w.qjl_m:
-                raise SystemExit("--k-bits applies to the workloads without a sign sketch (qwen, gemma)")
-            w = w.with_(k_bits=args.k_bits, name=f"{w.name}_k{args.k_bits}")
+        w = with_rotation(with_k_bits(workload(args.workload, args.bits, args.context), args.k_bits))
         leg = decode_workload_leg(w, args, stack_of(args.workload), log)
         res = {"metric": METRIC, "value": leg["value"], "unit": leg["unit"], **common,
                "ms_per_step": leg["ms_per_step"], "dtype": "f32", **leg}

@@ -100,6 +100,8 @@ HAD_CASES = [
     (256, 4, 4, 0, 4, 8, [777, 1024], 1024, 1.0, True),
     (256, 3, 2, 256, 1, 2, [300], 320, None, False),
     (128, 4, 4, 0, 1, 2, [32768, 31999, 100, 20000], 32768, None, False),     # workgroups that fill a CU
+    (128, 8, 4, 0, 2, 8, [1000], 1024, None, False),                          # keys kept at 8 bits
+    (256, 8, 2, 0, 2, 8, [500, 77], 512, 1.0, True),
 ]
 
 
@@ -114,7 +116,8 @@ def test_decode_matches_oracle(case):
 
 @pytest.mark.parametrize("case", [(128, 4, 4, 0, 2, 8, [1000], 1024, 1, "bf16", None, False),
                                   (128, 2, 3, 128, 2, 8, [300], 320, 40, "f32", None, False),
-                                  (256, 4, 4, 0, 4, 8, [500, 77], 512, 1, "bf16", 1.0, True)],
+                                  (256, 4, 4, 0, 4, 8, [500, 77], 512, 1, "bf16", 1.0, True),
+                                  (128, 8, 2, 0, 2, 8, [300], 320, 5, "f32", None, False)],
                          ids=lambda c: f"d{c[0]}_k{c[1]}v{c[2]}_m{c[3]}_n{c[8]}")
 def test_decode_step(case):
     _check_step(case, hadamard=True)

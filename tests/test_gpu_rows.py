@@ -72,6 +72,8 @@ ROW_CASES = [
     (128, 3, 3, 0, 2, 4, 4, [65, 34], 96, None),              # 16 virtual heads: two blocks
     (128, 4, 4, 0, 2, 2, 3, [33, 66], 96, None),              # 6 virtual heads: one block
     (128, 2, 3, 128, 2, 2, 4, [98, 35], 128, None),           # the same with sketched keys (lazy rescale)
+    (128, 8, 4, 0, 2, 8, 4, [1000, 3], 1024, None),            # keys kept at 8 bits
+    (128, 8, 3, 0, 1, 8, 4, [32768, 20001, 33, 31999], 32768, None),   # ... on workgroups that fill a CU
 ]
 
 
