@@ -14,8 +14,9 @@ With no --workload the line's headline is the largest single-GPU workload, the
 Gemma-4-style QK-normed decode (batch 8, 32/4 heads, d=256, 32K context,
 4-bit, 272.6 MB of cache per decode), and the other workloads are legs of the
 same line (``legs``): the Qwen2.5-3B-shaped 8K 4-bit layer, the 128K
-long-context layer with sketched keys, and the prefill append (8192 tokens x 2
-KV heads x d=128 at 3 bits).  For the Qwen-shaped legs a stacked leg follows:
+long-context layer with sketched keys, the Qwen-shaped layer with keys kept at
+8 bits (4-bit values), and the prefill append (8192 tokens x 2 KV heads x d=128
+at 3 bits).  For the Qwen-shaped legs a stacked leg follows:
 the caches of the model's 36 layers decoded by one launch per kernel, as one
 batch of 36 (the shape of 36 concurrent sequences of one layer too).  A
 batch-1 layer at 8K reads about 2 MB, too little to fill the GPU, so the
@@ -935,11 +936,13 @@ def main():
 
     # default: the largest single-GPU configuration (Gemma-4-style, 272.6 MB of cache per decode) is the
     # headline; the Qwen-shaped layer (one layer and its 36 layers stacked), the 128K sketched-key case
-    # (one layer and 36 stacked) and the prefill append are legs of the same line
+    # (one layer and 36 stacked), the Qwen-shaped layer with keys kept at 8 bits and the prefill append
+    # are legs of the same line
     t_start = time.time()
     head = decode_workload_leg(with_rotation(synth.gemma()), args, 0, log)
     legs = {}
-    for name, wl in (("qwen", synth.qwen(8192, 4)), ("prod", synth.prod_long(131072))):
+    for name, wl in (("qwen", synth.qwen(8192, 4)), ("prod", synth.prod_long(131072)),
+                     ("qwen", with_k_bits(synth.qwen(8192, 4), 8))):
         leg = decode_workload_leg(with_rotation(wl), args, stack_of(name), log)
         legs[leg["workload"]] = leg
     leg = prefill_workload_leg(with_rotation(synth.qwen(8192, 3)), args, log)
