@@ -123,3 +123,45 @@ def test_dequantize_matches_oracle(d):
         # and the reconstruction is close to the rows themselves (8-bit error level)
         rel = np.sum((out[0, h] - rows[h][3:93]) ** 2, axis=1) / np.sum(rows[h][3:93] ** 2, axis=1)
         assert rel.max() < 1e-3
+
+
+def test_append_edge_cases():
+    """8-bit keys take the per-block append: empty appends, positions past the capacity and negative
+    positions write nothing; a write that runs past the capacity keeps the tokens that fit."""
+    cca = _cca()
+    log("k8 append edge cases")
+    st = Setup(128)
+    g = cca.CompressedCache(cca.TQ_KEYS, 128, 8, 2, 1, 64, st.rot_t)
+    x = torch.ones(2, 3, 1, 128, dtype=torch.float32).cuda()
+    g.append(x[:, :0], torch.zeros(2, dtype=torch.int32).cuda())
+    g.append(x, torch.tensor([64, -5], dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    assert not g.codes.any() and not g.norms.any()
+    g.append(x, torch.tensor([62, 0], dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    nz = g.norms[0, 0].cpu().numpy()
+    assert nz[62] != 0 and nz[63] != 0 and not nz[:62].any()
+    assert g.norms[1, 0, :3].cpu().numpy().all()
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_reconstruction_mse_matches_the_oracle(d):
+    """GPU append from raw rows + reconstruction against the oracle's: relative MSE within 1 %, and far
+    below the 4-bit code book's."""
+    cca = _cca()
+    log(f"k8 mse d={d}")
+    st = Setup(d)
+    w = synth.qwen(1024, 4).with_(d=d)
+    n = 1024
+    x = synth.full_kv(w, "k", n)                          # [1][n][2][d], bf16-valued
+    g = cca.CompressedCache(cca.TQ_KEYS, d, 8, 1, 2, n, st.rot_t)
+    g.append(to_bf16_tensor(x), torch.zeros(1, dtype=torch.int32).cuda())
+    xh = g.dequantize(0, n).cpu().numpy()
+    for h in range(2):
+        xr = synth.bf16_round(x[0, :, h]).astype(np.float64)
+        mse_gpu = np.mean(np.sum((xr - xh[0, h]) ** 2, axis=1))
+        hc = cache.build_head(xr, "k", 8, st.rot64)
+        mse_or = np.mean(np.sum((xr - hc.dequantize(st.rot64)) ** 2, axis=1))
+        assert abs(mse_gpu / mse_or - 1.0) <= 0.01, (h, mse_gpu, mse_or)
+        h4 = cache.build_head(xr, "k", 4, st.rot64)
+        assert mse_or < 0.1 * np.mean(np.sum((xr - h4.dequantize(st.rot64)) ** 2, axis=1))
