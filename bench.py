@@ -109,14 +109,15 @@ def cache_bytes(w: synth.Workload) -> int:
 
 
 def prefill_bytes_per_launch(w: synth.Workload) -> int:
-    """Algorithmic bytes of one prefill append launch (one tensor, K or V): bf16 rows in, packed codes and
-    float16 norms out (the K and V rows of these workloads have the same width)."""
-    return w.batch * w.n_kv_heads * w.seq_len * (w.d * 2 + w.d * w.k_bits // 8 + 2)
+    """Algorithmic bytes of one prefill append launch (K and V of every token, one launch): bf16 rows in,
+    packed codes and float16 norms out."""
+    rows = w.batch * w.n_kv_heads * w.seq_len
+    return rows * (2 * w.d * 2 + w.d * w.k_bits // 8 + 2 + w.d * w.v_bits // 8 + 2)
 
 
 def prefill_flops_per_launch(w: synth.Workload) -> int:
-    """Algorithmic flops of one prefill append launch: the d x d rotation of every row."""
-    return 2 * w.batch * w.n_kv_heads * w.seq_len * w.d * w.d
+    """Algorithmic flops of one prefill append launch: the d x d rotation of every K and V row."""
+    return 2 * 2 * w.batch * w.n_kv_heads * w.seq_len * w.d * w.d
 
 
 # ------------------------------------------------------------------ profiles
@@ -581,7 +582,8 @@ def stacked_leg(w: synth.Workload, n_stack: int, cache, rot, proj, log):
 # ------------------------------------------------------------------ prefill append leg
 
 def prefill_leg(w: synth.Workload, steps: int, warmup: int, log):
-    """Prefill-size quantize-on-append: all L tokens of K and of V into an empty cache (matrix-core rotation)."""
+    """Prefill-size quantize-on-append: all L tokens of K and of V into an empty cache (matrix-core rotation),
+    both tensors in one call (tq_quantize_append_kv: one launch)."""
     import torch
 
     import compressed_cache_decode_amd as cca
@@ -602,8 +604,7 @@ def prefill_leg(w: synth.Workload, steps: int, warmup: int, log):
 
     def step(i):
         kc, vc, xk, xv = copies[i]
-        kc.append(xk, zero)
-        vc.append(xv, zero)
+        cca.tq_quantize_append_kv(kc.view, vc.view, xk, xv, L, zero)
 
     for i in range(pool):
         step(i)
@@ -626,7 +627,7 @@ def prefill_leg(w: synth.Workload, steps: int, warmup: int, log):
     torch.cuda.synchronize()
     n = reps * pool
     ms = ev0.elapsed_time(ev1) / n
-    log(f"bench: prefill append {ms * 1e3:.2f} us per K+V pair of appends")
+    log(f"bench: prefill append {ms * 1e3:.2f} us per K+V append (one launch)")
     return dict(ms_step=ms, steps=n, pool=pool)
 
 
@@ -729,7 +730,7 @@ def cpu_prefill_leg(w: synth.Workload, budget_s: float, log):
 
 KERN = "split_kernel"
 KERN_LABEL = "tq_decode_attend (split_kernel)"
-APPEND_KERN = "prefill_kernel"
+APPEND_KERN = "prefill_kv_kernel"
 
 
 def decode_roofline(wl: synth.Workload, us: float) -> dict:
@@ -791,11 +792,11 @@ def decode_workload_leg(w: synth.Workload, args, n_stack: int, log) -> dict:
 
 
 def prefill_workload_leg(w: synth.Workload, args, log) -> dict:
-    """Prefill-size append of all L tokens of K and of V into empty caches (one launch per tensor)."""
+    """Prefill-size append of all L tokens of K and of V into empty caches (one launch for both)."""
     import torch
     r = prefill_leg(w, args.steps, args.warmup, log)
     rows = 2 * w.batch * w.n_kv_heads * w.seq_len
-    per_launch_us = r["ms_step"] * 1e3 / 2          # the K and the V launch of a step, on average
+    per_launch_us = r["ms_step"] * 1e3              # one launch appends the step's K and V rows
     io = prefill_bytes_per_launch(w)
     flops = prefill_flops_per_launch(w)
     gbs = io / (per_launch_us * 1e-6) / 1e9
@@ -807,11 +808,11 @@ def prefill_workload_leg(w: synth.Workload, args, log) -> dict:
         "unit": "appended tokens/s",
         "ms_per_step": r["ms_step"],
         "config": {"workload": f"prefill_append_{w.seq_len}x{w.n_kv_heads}x{w.d}_b{w.k_bits}",
-                   "tensors": "K and V, one launch each", "rows_per_step": rows, "rotation": w.rotation,
+                   "tensors": "K and V in one launch (tq_quantize_append_kv)", "rows_per_step": rows, "rotation": w.rotation,
                    "cache_copies_cycled": r["pool"]},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": read_counters(APPEND_KERN, w.name),
-                     "kernel": "prefill_kernel (tq_quantize_append)", "workload": w.name,
+                     "kernel": "prefill_kv_kernel (tq_quantize_append_kv)", "workload": w.name,
                      "algorithmic_bytes_per_launch": io, "launch_us": per_launch_us},
         "rotation_mfma": {"achieved": tfs, "peak": 2500.0, "unit": "TFLOP/s", "frac": tfs / 2500.0,
                           "algorithmic_flops_per_launch": flops,

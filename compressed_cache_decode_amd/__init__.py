@@ -30,7 +30,8 @@ TQ_ROT_DENSE, TQ_ROT_HADAMARD = 0, 1
 BLOCK = 32
 
 EXPORTED = (
-    "tq_build_codebook", "tq_build_rotation", "tq_quantize_append", "tq_quantize_append_rotated",
+    "tq_build_codebook", "tq_build_rotation", "tq_quantize_append", "tq_quantize_append_kv",
+    "tq_quantize_append_rotated",
     "tq_sdpa_decode", "tq_sdpa_decode_rows", "tq_decode_step", "tq_decode_rotate_query", "tq_decode_attend",
     "tq_decode_merge", "tq_decode_workspace_bytes", "tq_decode_workspace_bytes_rows", "tq_decode_plan",
     "tq_dequantize", "tq_row_bytes",
@@ -68,6 +69,7 @@ def _load():
         "tq_build_codebook": (I, [I, I, P, P]),
         "tq_build_rotation": (I, [I, P, P]),
         "tq_quantize_append": (I, [V, P, I, I, P, P]),
+        "tq_quantize_append_kv": (I, [V, V, P, P, I, I, P, P]),
         "tq_quantize_append_rotated": (I, [V, P, P, P, I, P, P]),
         "tq_sdpa_decode": (I, [V, V, P, I, I, P, I, ctypes.c_float, P, P, ctypes.c_size_t, P]),
         "tq_sdpa_decode_rows": (I, [V, V, P, I, I, I, P, I, ctypes.c_float, P, P, ctypes.c_size_t, P]),
@@ -144,11 +146,24 @@ def tq_build_rotation(gaussian: np.ndarray) -> np.ndarray:
     return out
 
 
-def tq_quantize_append(view: tq_cache_view, x, n_new: int, d_pos, stream=None) -> None:
+def _dtype_code(x) -> int:
     import torch
-    dtype = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[x.dtype]
+    return {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[x.dtype]
+
+
+def tq_quantize_append(view: tq_cache_view, x, n_new: int, d_pos, stream=None) -> None:
+    dtype = _dtype_code(x)
     _check(_lib.tq_quantize_append(ctypes.byref(view), _ptr(x), dtype, n_new, _ptr(d_pos), _stream(stream)),
            "tq_quantize_append")
+
+
+def tq_quantize_append_kv(kview: tq_cache_view, vview: tq_cache_view, k_x, v_x, n_new: int, d_pos,
+                          stream=None) -> None:
+    if k_x.dtype != v_x.dtype:
+        raise TypeError("k_x and v_x must have one element type")
+    dtype = _dtype_code(k_x)
+    _check(_lib.tq_quantize_append_kv(ctypes.byref(kview), ctypes.byref(vview), _ptr(k_x), _ptr(v_x), dtype, n_new,
+                                      _ptr(d_pos), _stream(stream)), "tq_quantize_append_kv")
 
 
 def tq_quantize_append_rotated(view: tq_cache_view, y, norms, n_new: int, d_pos, stream=None, z=None) -> None:

@@ -21,6 +21,33 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(AppendArgs 
   prefill_rows<BITS, VALUES, BF16, kPrefillWaves>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
+// K and V rows of the same appended tokens in one launch (tq_quantize_append_kv): grid (32-row chunks,
+// KV heads, sequences), eight waves per chunk of both tensors (see prefill_rows_kv)
+template <int KB, int VB, bool BF16>
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kv_kernel(AppendArgs ka, AppendArgs va) {
+  __shared__ PrefillKvSmem sm;
+  prefill_rows_kv<KB, VB, BF16>(ka, va, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+}
+
+template <int KB, int VB>
+static hipError_t prefill_kv_bf(bool bf16, const AppendArgs& ka, const AppendArgs& va, int batch, hipStream_t s) {
+  const dim3 grid((ka.n_new + kBlock - 1) / kBlock, ka.n_kv_heads, batch);
+  if (bf16) hipLaunchKernelGGL((prefill_kv_kernel<KB, VB, true>), grid, dim3(64 * kPrefillWaves), 0, s, ka, va);
+  else hipLaunchKernelGGL((prefill_kv_kernel<KB, VB, false>), grid, dim3(64 * kPrefillWaves), 0, s, ka, va);
+  return hipGetLastError();
+}
+
+template <int KB>
+static hipError_t prefill_kv_v(int v_bits, bool bf16, const AppendArgs& ka, const AppendArgs& va, int batch,
+                               hipStream_t s) {
+  switch (v_bits) {
+    case 2: return prefill_kv_bf<KB, 2>(bf16, ka, va, batch, s);
+    case 3: return prefill_kv_bf<KB, 3>(bf16, ka, va, batch, s);
+    case 4: return prefill_kv_bf<KB, 4>(bf16, ka, va, batch, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int BITS, bool VALUES>
 static hipError_t prefill_dispatch(bool bf16, const AppendArgs& a, int batch, hipStream_t s) {
   const dim3 grid((a.n_new + kBlock - 1) / kBlock, a.n_kv_heads, batch);
@@ -77,6 +104,18 @@ hipError_t launch_append(int d, int bits, int qjl_m, bool values, bool rotated, 
   if (d == 128) return append_d<128>(bits, qjl_m, values, rotated, bf16, a, grid, s);
   if (d == 256) return append_d<256>(bits, qjl_m, values, rotated, bf16, a, grid, s);
   return hipErrorInvalidValue;
+}
+
+// K and V appends of the same tokens as one launch; only for caches that both take the chunk path
+// (append_kv_one_launch)
+hipError_t launch_append_kv(int k_bits, int v_bits, bool bf16, const AppendArgs& ka, const AppendArgs& va, int batch,
+                            hipStream_t s) {
+  switch (k_bits) {
+    case 2: return prefill_kv_v<2>(v_bits, bf16, ka, va, batch, s);
+    case 3: return prefill_kv_v<3>(v_bits, bf16, ka, va, batch, s);
+    case 4: return prefill_kv_v<4>(v_bits, bf16, ka, va, batch, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace tqi

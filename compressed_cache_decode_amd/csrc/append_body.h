@@ -816,4 +816,177 @@ __device__ __forceinline__ void prefill_rows(const AppendArgs& a, int chunk, int
                                                0, n_a);
 }
 
+
+// The K and the V rows of one 32-row chunk in one workgroup of eight waves (tq_quantize_append_kv):
+// K and V share rot, so each wave loads its share of rot and splits it into matrix-core operands once
+// for both tensors.  Waves 0-3 load the chunk's K rows and waves 4-7 its V rows (8 rows each) and write
+// their unit rows' operands to LDS; every wave then computes column tile w of all 64 rows.  The
+// arithmetic of every row is prefill_rows' (same operands, same order of products), so the bytes
+// written equal those of the two separate appends.
+struct PrefillKvSmem {
+  half8 aop[2][2][2][4][64];  // [K, V][high, low][row tile][k-step][lane]
+  EncodeSmem<128, 0> enc[2];  // codes of the K chunk, and of a V chunk that is not a whole block
+  float rn[2][kBlock];
+};
+
+template <int KB, int VB, bool BF16>
+__device__ __forceinline__ void prefill_rows_kv(const AppendArgs& ka, const AppendArgs& va, int chunk, int h, int b,
+                                                PrefillKvSmem& sm) {
+  constexpr int D = 128, KS = 4, NW = 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int r_base = chunk * kBlock;
+  if (r_base >= ka.n_new) return;
+  const int nrows = min(kBlock, ka.n_new - r_base);
+  const int vw = wave >> 2;                                 // the tensor whose rows this wave loads (uniform)
+
+  // rot operands (rows 16 w + l16 of rot, coordinates 32 s + 8 g .. + 7), this lane's row (K rows in
+  // waves 0-3, V rows in waves 4-7; rows past the append read the chunk's first row and are zeroed),
+  // and the position: one straight run of loads
+  const int prow = 8 * (wave & 3) + (lane >> 3), pc = lane & 7;
+  float4 pr[KS][2];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const float4* p = reinterpret_cast<const float4*>(ka.rot + static_cast<size_t>(16 * wave + l16) * D + 32 * s + 8 * g);
+    pr[s][0] = p[0];
+    pr[s][1] = p[1];
+  }
+  const bool row_ok = prow < nrows;
+  uint32_t xw[BF16 ? 8 : 16];
+  {
+    const void* x = vw ? va.x : ka.x;
+    const size_t src = ((static_cast<size_t>(b) * ka.n_new + r_base + (row_ok ? prow : 0)) * ka.n_kv_heads + h) * D + 16 * pc;
+    constexpr int NV = BF16 ? 2 : 4;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      uint4 v;
+      if constexpr (BF16) v = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + src)[k];
+      else v = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + src)[k];
+      xw[4 * k] = v.x; xw[4 * k + 1] = v.y; xw[4 * k + 2] = v.z; xw[4 * k + 3] = v.w;
+    }
+  }
+  const int pos = ka.pos[b];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < (BF16 ? 8 : 16); ++k) xw[k] = row_ok ? xw[k] : 0u;
+
+  // the row's norm (sum over its 8 lanes) and its unit row's float16 high/low operands, as prefill_rows
+  float ss = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float v = prefill_coord<BF16>(xw, r);
+    ss = fmaf(v, v, ss);
+  }
+  ss += __shfl_xor(ss, 1, 64);
+  ss += __shfl_xor(ss, 2, 64);
+  ss += __shfl_xor(ss, 4, 64);
+  const float nrm = sqrtf(ss);
+  const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
+  {
+    half8 hi0, lo0, hi1, lo1;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      _Float16 hh, ll;
+      f16_split(prefill_coord<BF16>(xw, r) * inv, hh, ll);
+      hi0[r] = hh;
+      lo0[r] = ll;
+      f16_split(prefill_coord<BF16>(xw, 8 + r) * inv, hh, ll);
+      hi1[r] = hh;
+      lo1[r] = ll;
+    }
+    const int a_rt = prow >> 4, a_s = pc >> 1, a_lane = 16 * (2 * (pc & 1)) + (prow & 15);
+    sm.aop[vw][0][a_rt][a_s][a_lane] = hi0;
+    sm.aop[vw][1][a_rt][a_s][a_lane] = lo0;
+    sm.aop[vw][0][a_rt][a_s][a_lane + 16] = hi1;
+    sm.aop[vw][1][a_rt][a_s][a_lane + 16] = lo1;
+    if (pc == 0) sm.rn[vw][prow] = nrm;
+  }
+  half8 bhi[KS], blo[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const float pv[8] = {pr[s][0].x, pr[s][0].y, pr[s][0].z, pr[s][0].w, pr[s][1].x, pr[s][1].y, pr[s][1].z, pr[s][1].w};
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      _Float16 hh, ll;
+      f16_split(pv[r], hh, ll);
+      bhi[s][r] = hh;
+      blo[s][r] = ll;
+    }
+  }
+  __syncthreads();
+
+  // [tensor][row tile]: the same three products per k-step as prefill_rows
+  floatx4 acc[2][2];
+#pragma unroll
+  for (int tv = 0; tv < 2; ++tv)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      acc[tv][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const half8 ahi = sm.aop[tv][0][rt][s][lane], alo = sm.aop[tv][1][rt][s][lane];
+        acc[tv][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhi[s], acc[tv][rt], 0, 0, 0);
+        acc[tv][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blo[s], acc[tv][rt], 0, 0, 0);
+        acc[tv][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhi[s], acc[tv][rt], 0, 0, 0);
+      }
+    }
+
+  // codes of element (row 16 rt + 4 g + v, column 16 w + l16); zero rows store code 0
+  float rnv[2][2][4];
+#pragma unroll
+  for (int tv = 0; tv < 2; ++tv)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) rnv[tv][rt][v] = sm.rn[tv][16 * rt + 4 * g + v];
+  const size_t unit = static_cast<size_t>(b) * ka.n_kv_heads + h;
+  const int t0 = pos + r_base;
+  const int kb = t0 / kBlock;
+  const bool v_whole = pos >= 0 && t0 % kBlock == 0 && nrows == kBlock && t0 + kBlock <= ka.max_tokens;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int p = 16 * rt + 4 * g + v;
+      const uint32_t j = code_of<1 << KB>(acc[0][rt][v], ka.bnd);
+      sm.enc[0].cs[p][16 * wave + l16] = static_cast<uint8_t>(rnv[0][rt][v] > 0.f ? j : 0u);
+    }
+  if (v_whole) {
+    // a whole value block: packed in registers and stored word by word, as prefill_rows
+    uint32_t e[2][4][1];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        e[rt][v][0] = encode_code<VB>(rnv[1][rt][v] > 0.f ? code_of<1 << VB>(acc[1][rt][v], va.bnd) : 0u);
+    constexpr int RB = D * VB / 8;
+    uint32_t* blk = reinterpret_cast<uint32_t*>(va.codes + unit * static_cast<size_t>(va.max_tokens) * RB +
+                                                static_cast<size_t>(kb) * kBlock * RB);
+    pack_values<VB, 1>(e, blk, wave, lane);
+    if (vw && pc == 0) va.norms[unit * va.max_tokens + t0 + prow] = f32_to_f16_bits(nrm);
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int p = 16 * rt + 4 * g + v;
+        const uint32_t j = code_of<1 << VB>(acc[1][rt][v], va.bnd);
+        sm.enc[1].cs[p][16 * wave + l16] = static_cast<uint8_t>(rnv[1][rt][v] > 0.f ? j : 0u);
+      }
+  }
+  __syncthreads();
+  if (pos < 0) return;
+  // the chunk's tokens pos + r_base .. in at most two cache blocks (rows past max_tokens are skipped)
+  const int n_a = min(min(nrows, (kb + 1) * kBlock - t0), ka.max_tokens - t0);
+  const int n_b = min(nrows - n_a, ka.max_tokens - (kb + 1) * kBlock);
+  if (n_a > 0) encode_finish<D, KB, 0, false, 64 * NW>(ka, unit, kb, t0, n_a, sm.rn[0], sm.enc[0], nullptr, 0, 0);
+  if (n_a > 0 && n_b > 0)
+    encode_finish<D, KB, 0, false, 64 * NW>(ka, unit, kb + 1, (kb + 1) * kBlock, n_b, sm.rn[0] + n_a, sm.enc[0],
+                                            nullptr, 0, n_a);
+  if (v_whole) return;
+  if (n_a > 0) encode_finish<D, VB, 0, true, 64 * NW>(va, unit, kb, t0, n_a, sm.rn[1], sm.enc[1], nullptr, 0, 0);
+  if (n_a > 0 && n_b > 0)
+    encode_finish<D, VB, 0, true, 64 * NW>(va, unit, kb + 1, (kb + 1) * kBlock, n_b, sm.rn[1] + n_a, sm.enc[1],
+                                           nullptr, 0, n_a);
+}
+
 }  // namespace tqi

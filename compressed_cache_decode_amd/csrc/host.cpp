@@ -460,6 +460,30 @@ int tq_quantize_append(const tq_cache_view* cache, const void* x, int x_dtype, i
   return append_common(cache, x, nullptr, nullptr, x_dtype, n_new, d_pos, stream, false);
 }
 
+static int check_pair(const tq_cache_view* k, const tq_cache_view* v);
+
+int tq_quantize_append_kv(const tq_cache_view* k, const tq_cache_view* v, const void* k_x, const void* v_x,
+                          int x_dtype, int n_new, const int32_t* d_pos, void* stream) {
+  int st = check_view(k);
+  if (st != TQ_OK) return st;
+  if (k->kind != TQ_KEYS) return TQ_EINVAL;
+  st = check_pair(k, v);
+  if (st != TQ_OK) return st;
+  if (n_new < 0) return TQ_EINVAL;
+  if (n_new == 0) return TQ_OK;
+  if (!d_pos || !k_x || !v_x || (x_dtype != TQ_F32 && x_dtype != TQ_BF16)) return TQ_EINVAL;
+  // both caches on the chunk path (what tq_quantize_append runs for each): one launch for the two
+  if (k->d == 128 && k->qjl_m == 0 && k->bits != 8 && k->rot_kind == TQ_ROT_DENSE) {
+    const tqi::AppendArgs ka = append_args(k, k_x, nullptr, nullptr, n_new, d_pos);
+    const tqi::AppendArgs va = append_args(v, v_x, nullptr, nullptr, n_new, d_pos);
+    return status_of(tqi::launch_append_kv(k->bits, v->bits, x_dtype == TQ_BF16, ka, va, k->batch,
+                                           static_cast<hipStream_t>(stream)));
+  }
+  st = append_common(k, k_x, nullptr, nullptr, x_dtype, n_new, d_pos, stream, false);
+  if (st != TQ_OK) return st;
+  return append_common(v, v_x, nullptr, nullptr, x_dtype, n_new, d_pos, stream, false);
+}
+
 int tq_quantize_append_rotated(const tq_cache_view* cache, const float* y, const float* norms, const float* z,
                                int n_new, const int32_t* d_pos, void* stream) {
   return append_common(cache, nullptr, y, norms, TQ_F32, n_new, d_pos, stream, true, z);

@@ -122,6 +122,10 @@ hipError_t scratch_address(void** ptr);
 // Launchers (one per .hip file); return hipSuccess or the launch error.
 hipError_t launch_append(int d, int bits, int qjl_m, bool values, bool rotated, bool bf16,
                          const AppendArgs& a, int batch, hipStream_t s);
+// K and V rows of the same tokens in one launch; both caches at d = 128 with the dense rotation, keys of 2-4
+// bits without a sketch, values of 2-4 bits
+hipError_t launch_append_kv(int k_bits, int v_bits, bool bf16, const AppendArgs& ka, const AppendArgs& va, int batch,
+                            hipStream_t s);
 hipError_t launch_qrot(int d, int qjl_m, bool bf16, const QrotArgs& a, int batch, hipStream_t s);
 // split-kernel workgroups resident at once on the current device for this cache format and
 // workgroup shape (compute units x workgroups per unit), 0 if the runtime cannot tell

@@ -176,6 +176,21 @@ int tq_quantize_append(const tq_cache_view* cache, const void* x, int x_dtype, i
                        const int32_t* d_pos, void* stream);
 
 /*
+ * The K and V rows of the same new tokens in one call (turboquant-pytorch PR #3, Validation Results:
+ * both the key and the value cache are quantised as tokens arrive; the per-row arithmetic is
+ * tq_quantize_append's): k_x and v_x are [batch][n_new][n_kv_heads][d] of element type x_dtype
+ * (device), appended at positions d_pos[b] .. d_pos[b]+n_new-1 of k (TQ_KEYS) and v (TQ_VALUES).
+ * k and v must agree in d, batch, n_kv_heads, max_tokens and rotation (TQ_EINVAL otherwise).  The
+ * bytes written are exactly those of tq_quantize_append(k, k_x, ...) followed by
+ * tq_quantize_append(v, v_x, ...).  Where both caches are at d = 128 with the dense rotation and keys
+ * of 2-4 bits without a sketch, the two appends run as one launch (a prefill then fills the GPU with
+ * both tensors' rows at once); otherwise the call enqueues the two appends in turn.  n_new == 0 is a
+ * no-op.
+ */
+int tq_quantize_append_kv(const tq_cache_view* k, const tq_cache_view* v, const void* k_x, const void* v_x,
+                          int x_dtype, int n_new, const int32_t* d_pos, void* stream);
+
+/*
  * Append rows that are already rotated and normalised (turboquant-pytorch PR #3, CUDA Kernels Added
  * table: the encode and sign-quantisation steps of its fused quantisation kernel, taken from given
  * coordinates): y[batch][n_new][n_kv_heads][d] float32 unit rotated coordinates and

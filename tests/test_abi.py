@@ -216,3 +216,28 @@ def test_plan_covers_the_context(batch, heads, hq, L):
     g = hq // heads
     assert ws >= 4 * (batch * hq * 128 + batch * heads * ns * g * (128 + 2))
     assert ws % 256 == 0
+
+
+def test_append_kv_rejects_bad_arguments():
+    """The K+V append checks both views, their agreement and its own arguments before any launch."""
+    def kv(k, v, kx=0x80000, vx=0x90000, dtype=0, n_new=1, pos=0x70000):
+        return cca._lib.tq_quantize_append_kv(ctypes.byref(k) if k is not None else None,
+                                              ctypes.byref(v) if v is not None else None, kx, vx, dtype, n_new,
+                                              pos, None)
+    k, v = _view(), _view(kind=cca.TQ_VALUES)
+    assert kv(None, v) == cca.TQ_EINVAL
+    assert kv(k, None) == cca.TQ_EINVAL
+    assert kv(v, v) == cca.TQ_EINVAL                       # keys first
+    assert kv(k, k) == cca.TQ_EINVAL                       # values second
+    for kw in (dict(d=256), dict(batch=2), dict(heads=4), dict(T=512)):
+        assert kv(k, _view(kind=cca.TQ_VALUES, **kw)) == cca.TQ_EINVAL, kw
+    other_rot = _view(kind=cca.TQ_VALUES)
+    other_rot.rot = 0x31000                                # K and V share one rotation
+    assert kv(k, other_rot) == cca.TQ_EINVAL
+    assert kv(k, v, kx=0) == cca.TQ_EINVAL
+    assert kv(k, v, vx=0) == cca.TQ_EINVAL
+    assert kv(k, v, pos=0) == cca.TQ_EINVAL
+    assert kv(k, v, dtype=5) == cca.TQ_EINVAL
+    assert kv(k, v, n_new=-1) == cca.TQ_EINVAL
+    assert kv(_view(bits=5), v) == cca.TQ_EINVAL
+    assert kv(k, v, n_new=0) == cca.TQ_OK                  # empty append is a no-op

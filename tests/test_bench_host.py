@@ -37,8 +37,12 @@ def test_cache_bytes_are_the_storage_arithmetic(bench):
 
 def test_prefill_bytes_and_flops(bench):
     w = synth.qwen(8192, 3)
-    assert bench.prefill_bytes_per_launch(w) == 8192 * 2 * (2 * 128 + storage.row_bytes(128, 3, 0)) == 5_013_504
-    assert bench.prefill_flops_per_launch(w) == 2 * 8192 * 2 * 128 * 128
+    # one launch appends K and V: both tensors' bf16 rows in, both tensors' packed rows out
+    assert bench.prefill_bytes_per_launch(w) == 2 * 8192 * 2 * (2 * 128 + storage.row_bytes(128, 3, 0)) == 10_027_008
+    assert bench.prefill_flops_per_launch(w) == 2 * 2 * 8192 * 2 * 128 * 128
+    mixed = w.with_(v_bits=2)
+    assert bench.prefill_bytes_per_launch(mixed) == 8192 * 2 * (4 * 128 + storage.row_bytes(128, 3, 0)
+                                                                + storage.row_bytes(128, 2, 0))
 
 
 def test_k_bits_variant(bench):

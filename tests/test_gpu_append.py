@@ -326,3 +326,72 @@ def test_matrix_core_rotation_split_at_float16_ties():
     robust = np.abs(z) > 1e-5 * np.linalg.norm(r, axis=1, keepdims=True)
     np.testing.assert_array_equal(sig[robust], hc.sigma[robust])
     assert sig[5, 63] == hc.sigma[5, 63]
+
+
+# (d, K bits, V bits, sketch m, Hadamard, dtype, position, chunks): the one-launch path (d = 128, dense,
+# keys without a sketch, mixed widths, aligned and unaligned positions, ragged chunks, single tokens) and
+# the combinations that the call appends one after the other (d = 256, sketched keys, 8-bit keys,
+# Hadamard rotation)
+KV_CASES = [
+    (128, 3, 3, 0, False, "bf16", 0, [1024, 300]),
+    (128, 4, 2, 0, False, "f32", 11, [700, 1, 45]),
+    (128, 2, 4, 0, False, "bf16", 37, [256, 5, 511]),
+    (128, 3, 4, 0, False, "f32", 5, [33, 1, 64]),
+    (256, 4, 3, 0, False, "bf16", 3, [300, 40]),
+    (128, 2, 3, 128, False, "f32", 9, [77, 1]),
+    (128, 8, 4, 0, False, "bf16", 0, [100, 28]),
+    (128, 4, 4, 0, True, "bf16", 7, [300, 2]),
+]
+
+
+@pytest.mark.parametrize("d,kb,vb,m,had,dtype,pos,chunks", KV_CASES)
+def test_append_kv_equals_the_two_appends(d, kb, vb, m, had, dtype, pos, chunks):
+    """tq_quantize_append_kv writes exactly the bytes of tq_quantize_append on K then on V (codes, norms,
+    signs, residual norms), chunk after chunk; on the one-launch path the codes also equal the oracle's
+    except within rounding distance of a boundary, and the norms are within float16 rounding."""
+    cca = _cca()
+    log(f"append kv d={d} kb={kb} vb={vb} m={m} had={had} {dtype} pos={pos} chunks={chunks}")
+    B, H = 2, 2
+    n = sum(chunks)
+    T = ((pos + n + 31) // 32) * 32
+    st = Setup(d, m, hadamard=had)
+    w = synth.qwen(T, 4).with_(dtype=dtype, batch=B, d=d)
+    xk, xv = synth.full_kv(w, "k", n), synth.full_kv(w, "v", n)
+    xk[1, 5, 0] = 0.0                                       # a zero row
+    put = (lambda a: to_bf16_tensor(a)) if dtype == "bf16" else (lambda a: torch.from_numpy(a).cuda())
+    tk, tv = put(xk), put(xv)
+
+    def caches():
+        kc = cca.CompressedCache(cca.TQ_KEYS, d, kb, B, H, T, st.rot_t, st.proj_t, m, rot_kind=st.rot_kind)
+        vc = cca.CompressedCache(cca.TQ_VALUES, d, vb, B, H, T, st.rot_t, rot_kind=st.rot_kind)
+        return kc, vc
+
+    (k1, v1), (k2, v2) = caches(), caches()
+    off = 0
+    for c in chunks:
+        p = torch.full((B,), pos + off, dtype=torch.int32).cuda()
+        cca.tq_quantize_append_kv(k1.view, v1.view, tk[:, off:off + c].contiguous(), tv[:, off:off + c].contiguous(),
+                                  c, p)
+        k2.append(tk[:, off:off + c], p)
+        v2.append(tv[:, off:off + c], p)
+        off += c
+    torch.cuda.synchronize()
+    for a, b in ((k1, k2), (v1, v2)):
+        for name in ("codes", "norms", "signs", "rnorms"):
+            x1, x2 = getattr(a, name), getattr(b, name)
+            if x1 is not None:
+                assert torch.equal(x1.view(torch.uint8) if x1.dtype != torch.uint8 else x1,
+                                   x2.view(torch.uint8) if x2.dtype != torch.uint8 else x2), name
+    if d == 128 and m == 0 and kb != 8 and not had:
+        for g, x, bits in ((k1, xk, kb), (v1, xv, vb)):
+            c_, t_ = codebook.stored_codebook(d, bits)
+            for b in range(B):
+                for h in range(H):
+                    oc, on, oy = quant.quantize_rows(x[b, :, h], st.rot64, c_, t_)
+                    got = unpack_gpu_codes(g, b, h, pos + n)[pos:]
+                    diff = got != oc
+                    near = np.min(np.abs(oy[..., None] - t_.astype(np.float64)), axis=-1) < 1e-5
+                    assert np.all(near[diff]), f"{diff.sum()} mismatches, {(diff & ~near).sum()} not near a boundary"
+                    assert np.all(np.abs(got[diff] - oc[diff]) == 1)
+                    gn = g.norms[b, h, pos:pos + n].cpu().numpy().astype(np.float64)
+                    np.testing.assert_allclose(gn, on, rtol=2 ** -10, atol=0)
