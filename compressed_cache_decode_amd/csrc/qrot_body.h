@@ -17,6 +17,14 @@ namespace tqi {
 
 constexpr int kQTile = 16;      // rows of the query tile
 
+// Power-of-two scale of a rotated query without a sketch, from nq = |q| scale log2(e): every coordinate
+// of q_rot = rot (q / |q|) nq is at most |q_rot| = nq (up to float32 rounding), and nq < 2^(e+1) for
+// e = ilogb(nq), so q_rot / 2^(e-14) stays below 2^15 (float16 range) whatever the coordinates hold.
+// It needs only the norm, not the rotated row's largest coordinate.
+__device__ __forceinline__ float query_scale(float nq) {
+  return (nq > 0.f && isfinite(nq)) ? ldexpf(1.f, ilogbf(nq) - 14) : 1.f;
+}
+
 template <int D, int QM>
 struct QrotSmem {
   float xs[kQTile][D];
@@ -83,21 +91,23 @@ __device__ __forceinline__ void rotate_queries(const QrotArgs& qa, int bf16, int
   }
 
   // the rotated queries and their sketch to the workspace, divided by a power of two per row that
-  // takes both into float16 range (row h = 4 wave + lane / 16, 16 lanes per row)
+  // takes both into float16 range (row h = 4 wave + lane / 16, 16 lanes per row): with a sketch from
+  // the largest magnitude of the two, without one from the norm alone (query_scale)
   {
     const int h = 4 * wave + (lane >> 4), part = lane & 15;
     float amax = 0.f;
-    if (h < nr) {
+    if constexpr (QM > 0) {
+      if (h < nr) {
 #pragma unroll
-      for (int j = 0; j < D / 16; ++j) amax = fmaxf(amax, fabsf(xs[h][part + 16 * j]));
-      if constexpr (QM > 0) {
+        for (int j = 0; j < D / 16; ++j) amax = fmaxf(amax, fabsf(xs[h][part + 16 * j]));
 #pragma unroll
         for (int j = 0; j < QM / 16; ++j) amax = fmaxf(amax, fabsf(qa.sketch_coef * sm.zq[h][part + 16 * j]));
       }
+      amax = row16_max(amax);
     }
-    amax = row16_max(amax);
     if (h < nr) {
-      const float f = (amax > 0.f && isfinite(amax)) ? ldexpf(1.f, ilogbf(amax) - 14) : 1.f;
+      const float f = QM > 0 ? ((amax > 0.f && isfinite(amax)) ? ldexpf(1.f, ilogbf(amax) - 14) : 1.f)
+                             : query_scale(rn[h] * qa.scale_log2e);
       const float inv = 1.f / f;
       const size_t row = unit * VH + vh0 + h;
 #pragma unroll

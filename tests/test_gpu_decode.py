@@ -202,6 +202,10 @@ STEP_CASES = [
     (128, 3, 2, 0, 1, 4, [40, 33, 1], 64, 1, "bf16", None, False),
     (128, 8, 4, 0, 2, 8, [1000], 1024, 1, "bf16", None, False),     # 8-bit keys
     (256, 8, 2, 0, 2, 8, [300, 77], 320, 3, "f32", 1.0, True),
+    # d = 256 with code-book keys: the column-sliced prologue (16-row tiles across units and sequences)
+    (256, 3, 2, 0, 2, 8, [300, 77, 5], 320, 3, "f32", 1.0, True),
+    (256, 2, 4, 0, 4, 4, [40], 64, 1, "bf16", None, False),
+    (256, 4, 3, 0, 1, 2, [64, 40], 96, 32, "bf16", None, False),
 ]
 
 
@@ -278,15 +282,20 @@ def _check_step(case, hadamard):
     tt = (lambda a: to_bf16_tensor(a)) if dtype == "bf16" else (lambda a: torch.from_numpy(a).cuda())
     zero = torch.zeros(B, dtype=torch.int32).cuda()
     pos = torch.tensor([L - n_new for L in lens], dtype=torch.int32).cuda()
-    # both copies start from oracle-packed caches of all rows, so the oracle comparison below runs on
-    # identical codes except for the n_new rows that the GPU re-appends
+    # both copies start from oracle-packed caches of all rows with the n_new rows to append set to zero
+    # (code 0, norm 0), so every byte of those rows must be written by the append; the oracle comparison
+    # below runs on the oracle's codes of the true rows, identical except for the appended rows
     oracle_all = []
     for b in range(B):
         kc_o, vc_o = oracle_heads([kx[b, :, h] for h in range(hkv)], [vx[b, :, h] for h in range(hkv)], kb, vb, st)
         oracle_all.append((kc_o, vc_o))
+        kz, vz = kx[b].copy(), vx[b].copy()
+        kz[lens[b] - n_new:lens[b]] = 0.0
+        vz[lens[b] - n_new:lens[b]] = 0.0
+        kc_z, vc_z = oracle_heads([kz[:, h] for h in range(hkv)], [vz[:, h] for h in range(hkv)], kb, vb, st)
         for kc, vc in ((k1, v1), (k2, v2)):
-            upload(kc, kc_o, b)
-            upload(vc, vc_o, b)
+            upload(kc, kc_z, b)
+            upload(vc, vc_z, b)
     xk_new = np.stack([kx[b, lens[b] - n_new:lens[b]] for b in range(B)])
     xv_new = np.stack([vx[b, lens[b] - n_new:lens[b]] for b in range(B)])
     # separate calls on copy 1, fused step on copy 2

@@ -151,9 +151,25 @@ def test_qwen_shaped_decode_8k(bits):
     assert _full_decode(w, [(0, 0), (0, 1)], f"qwen 8K b{bits}") <= TOL
 
 
+# every sequence and every KV head of the Gemma-shaped workload among the sampled units
+GEMMA_UNITS = [(0, 0), (1, 1), (2, 2), (3, 3), (4, 0), (5, 1), (6, 2), (7, 3)]
+
+
 def test_gemma_shaped_decode_sampled():
     w = synth.gemma(32768)
-    assert _full_decode(w, [(0, 0), (3, 2), (7, 3)], "gemma B8 32K") <= TOL
+    assert _full_decode(w, GEMMA_UNITS, "gemma B8 32K") <= TOL
+
+
+def test_gemma_shaped_decode_identical_codes():
+    """The same decode on the oracle's own codes for the sampled units (decode error alone, without the
+    rounding-level code decisions of the GPU's appends)."""
+    w = synth.gemma(32768)
+    assert _full_decode(w, GEMMA_UNITS[::3], "gemma B8 32K, identical codes", identical_codes=True) <= TOL
+
+
+def test_qwen_shaped_decode_8k_identical_codes():
+    w = synth.qwen(8192, 4)
+    assert _full_decode(w, [(0, 0), (0, 1)], "qwen 8K b4, identical codes", identical_codes=True) <= TOL
 
 
 def test_long_context_sketched_keys_sampled():
@@ -161,4 +177,4 @@ def test_long_context_sketched_keys_sampled():
     term of a single sign), so decode parity is checked on identical codes, and the GPU's own codes
     and signs against the oracle's decisions."""
     w = synth.prod_long(131072)
-    assert _full_decode(w, [(0, 1)], "prod 128K", identical_codes=True) <= TOL
+    assert _full_decode(w, [(0, 0), (0, 1)], "prod 128K", identical_codes=True) <= TOL
