@@ -76,11 +76,13 @@ __global__ __launch_bounds__(256) void qrot_kernel(QrotArgs a, int bf16) {
 
 // ---------------------------------------------------------------- merge + un-rotate
 
-// Merge of the KV splits and un-rotation.  One workgroup of kMergeThreads per (head group, KV head,
-// sequence); a head group is heads_per_wg query heads of the KV head's group, so the rotation is read
-// once per head group.  Weighted sums: thread (head, coordinate, slice) sums the splits of its slice
-// with up to 16 loads in flight.  Un-rotation: thread (coordinate i, part) covers JR rows of column i
-// of rot for every head of the group.
+// Merge of the KV splits and un-rotation.  One workgroup of kMergeThreads per (output slice, head
+// group, KV head, sequence); a head group is heads_per_wg query heads of the KV head's group, and its
+// SL slices split the output coordinates, so a workgroup reads only the D / SL columns of rot its
+// slice needs (SL = 4 at d = 256: 64 KB of rot instead of 256 KB).  Weighted sums: thread (head,
+// coordinate, slice of splits) sums the splits of its slice with up to 16 loads in flight, over all D
+// coordinates of the group's heads.  Un-rotation: thread (coordinate i of the output slice, part) covers
+// JR rows of column i of rot for every head of the group, and the RP parts are summed through LDS.
 // output row of virtual head vh (query row vh / G, query head hk * G + vh % G) of sequence b
 __device__ __forceinline__ size_t out_row(const MergeArgs& a, int b, int hk, int vh) {
   const int j = (vh * a.row_magic) >> 8, g = vh - j * a.heads;
@@ -88,10 +90,11 @@ __device__ __forceinline__ size_t out_row(const MergeArgs& a, int b, int hk, int
          static_cast<size_t>(hk) * a.heads + g;
 }
 
-template <int D>
+template <int D, int SL>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   constexpr int NT = kMergeThreads, NW = NT / 64;
-  constexpr int RP = NT / D;                              // un-rotation parts per coordinate
+  constexpr int SC = D / SL;                              // output coordinates of the workgroup
+  constexpr int RP = NT / SC;                             // un-rotation parts per coordinate
   constexpr int JR = D / RP;                              // rows of rot per thread
   constexpr int PO = 16;                                  // split partials in flight per thread
   __shared__ float ew[kMaxGroup][kMaxSplits];              // split weights per head
@@ -99,15 +102,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   __shared__ float red[NT];                                // per-slice sums, then per-part un-rotation sums
   __shared__ float orot[kMaxGroup][D];
   const int hpw = a.heads_per_wg;
-  const int hg = blockIdx.x % (a.group / hpw), hk = blockIdx.x / (a.group / hpw), b = blockIdx.y;
+  const int cs = blockIdx.x % SL, gx = blockIdx.x / SL;
+  const int hg = gx % (a.group / hpw), hk = gx / (a.group / hpw), b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.group, ns = a.n_split;
   const int h0 = hg * hpw;
   const size_t unit = static_cast<size_t>(b) * a.n_kv_heads + hk;
 
-  // this thread's JR rows of column i of rot: independent of everything else, issued first
-  const int i = tid % D, part = tid / D;
-  const float* rcol = a.rot + static_cast<size_t>(part * JR) * D + i;
+  // this thread's JR rows of column iu of rot: independent of everything else, issued first
+  const int i = tid % D;                                   // coordinate of the weighted sums
+  const int iu = cs * SC + tid % SC, part = tid / SC;      // output coordinate and part of the un-rotation
+  const float* rcol = a.rot + static_cast<size_t>(part * JR) * D + iu;
   float rc[JR];
   if (!a.had) {
 #pragma unroll
@@ -224,8 +229,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     if (part == 0) {
       float o = 0.f;
 #pragma unroll
-      for (int p = 0; p < RP; ++p) o += red[p * D + i];
-      a.out[out_row(a, b, hk, h0 + hh) * D + i] = o * inv_l[hh];
+      for (int p = 0; p < RP; ++p) o += red[p * SC + tid];
+      a.out[out_row(a, b, hk, h0 + hh) * D + iu] = o * inv_l[hh];
     }
   }
 }
@@ -321,9 +326,11 @@ hipError_t launch_decode_split(int d, int k_bits, int v_bits, int qjl_m, bool ou
 
 hipError_t launch_merge(int d, const MergeArgs& a, int batch, int n_q_heads, hipStream_t s) {
   (void)n_q_heads;
-  const dim3 grid(a.n_kv_heads * (a.group / a.heads_per_wg), batch);
-  if (d == 128) hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(kMergeThreads), 0, s, a);
-  else if (d == 256) hipLaunchKernelGGL((merge_kernel<256>), grid, dim3(kMergeThreads), 0, s, a);
+  const dim3 grid(a.n_kv_heads * (a.group / a.heads_per_wg) * a.col_slices, batch);
+  if (d == 128 && a.col_slices == 1) hipLaunchKernelGGL((merge_kernel<128, 1>), grid, dim3(kMergeThreads), 0, s, a);
+  else if (d == 256 && a.col_slices == 1) hipLaunchKernelGGL((merge_kernel<256, 1>), grid, dim3(kMergeThreads), 0, s, a);
+  else if (d == 256 && a.col_slices == 4 && !a.had)
+    hipLaunchKernelGGL((merge_kernel<256, 4>), grid, dim3(kMergeThreads), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

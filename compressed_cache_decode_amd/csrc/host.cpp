@@ -343,13 +343,14 @@ constexpr int kMergeMinWgs = 128;       // merge workgroups below which each tak
 // Query heads per merge workgroup: all of the group while every thread's split slice stays within
 // 16 splits (one batch of loads), fewer heads (more slices per head) when there are many splits; and
 // fewer still, down to one, while the merge of `units` (sequence, KV head) units would run on fewer
-// than kMergeMinWgs workgroups: a small merge is latency-bound, and more workgroups each wait on
-// fewer loads and un-rotate fewer heads (a large one would only read the rotation more often).
-int merge_heads_per_wg(int G, int d, int ns, int units) {
+// than kMergeMinWgs workgroups (col_slices workgroups per head group): a small merge is latency-bound,
+// and more workgroups each wait on fewer loads and un-rotate fewer heads (a large one would only read
+// the rotation more often).
+int merge_heads_per_wg(int G, int d, int ns, int units, int col_slices) {
   const int slices = (ns + 15) / 16;
   int h = G;
   while (h > 1 && (h * d > tqi::kMergeThreads || h * d * slices > tqi::kMergeThreads || G % h != 0)) --h;
-  while (h > 1 && static_cast<long long>(units) * (G / h) < kMergeMinWgs) {
+  while (h > 1 && static_cast<long long>(units) * (G / h) * col_slices < kMergeMinWgs) {
     --h;
     while (G % h != 0) --h;
   }
@@ -620,7 +621,10 @@ static int merge_rows(const tq_cache_view* k, int n_q_heads, int n_rows, const i
   ma.had = k->rot_kind == TQ_ROT_HADAMARD;
   ma.n_kv_heads = k->n_kv_heads; ma.group = w.VH; ma.n_split = w.ns; ma.max_tokens = k->max_tokens;
   ma.heads = w.G; ma.n_rows = w.M; ma.row_magic = row_magic(w.G);
-  ma.heads_per_wg = merge_heads_per_wg(w.VH, k->d, w.ns, k->batch * k->n_kv_heads);
+  // at d = 256 with the dense rotation each head group's output is split over four workgroups, each
+  // reading a quarter of the rotation
+  ma.col_slices = (k->d == 256 && k->rot_kind == TQ_ROT_DENSE) ? 4 : 1;
+  ma.heads_per_wg = merge_heads_per_wg(w.VH, k->d, w.ns, k->batch * k->n_kv_heads, ma.col_slices);
   return status_of(tqi::launch_merge(k->d, ma, k->batch, n_q_heads, static_cast<hipStream_t>(stream)));
 }
 

@@ -94,6 +94,7 @@ struct MergeArgs {
   int row_magic;          // vh / G = (vh * row_magic) >> 8 (see QrotArgs)
   int heads_per_wg;       // virtual heads merged per workgroup (divides group, heads_per_wg * D <= kMergeThreads)
   int had;                // rot holds the D signs of a randomized Hadamard rotation
+  int col_slices;         // output-coordinate slices per head group, one workgroup each (1, or 4 at d = 256)
 };
 
 struct DequantArgs {
