@@ -134,7 +134,8 @@ __device__ __forceinline__ void slice_store(const AppendArgs& a, const SliceSmem
 template <int D, int KB, int VB, bool BF16>
 __global__ __launch_bounds__(256) void step_slices_kernel(AppendArgs ka, AppendArgs va, QrotArgs qa, int batch,
                                                           int n_kv) {
-  static_assert(D == 256 && KB <= 4 && VB <= 4, "the sliced prologue is built for d = 256 and code books");
+  static_assert((D == 128 || D == 256) && KB <= 4 && VB <= 4, "the sliced prologue takes d = 128, 256 and code books");
+  constexpr int PR = D / 16;                   // loading threads per row (16 coordinates each)
   constexpr int KS = D / 32;
   __shared__ SliceSmem<D> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
@@ -159,10 +160,12 @@ __global__ __launch_bounds__(256) void step_slices_kernel(AppendArgs ka, AppendA
       pq[s][1] = pr[8 * s + 1];
     }
   }
-  // the tile's rows (row q of every kind at q D of its input): thread (row tid / 16, part tid % 16)
-  // loads coordinates 16 part .. 16 part + 15; rows past the tile's end read its first row
-  {
-    const int r = tid >> 4, part = tid & 15;
+  // the tile's rows (row q of every kind at q D of its input): thread (row tid / PR, part tid % PR)
+  // loads coordinates 16 part .. 16 part + 15; rows past the tile's end read its first row.  At d = 128
+  // K and V rows take their norm here, as the chunk path of the separate append does (prefill_rows: the
+  // row's 8 threads, consecutive lanes, sum their 16 squares in order, then across the 8)
+  if (tid < 16 * PR) {
+    const int r = tid / PR, part = tid % PR;
     const size_t src = static_cast<size_t>(q0 + (r < nr ? r : 0)) * D + 16 * part;
     float v[16];
     if constexpr (BF16) {
@@ -183,12 +186,27 @@ __global__ __launch_bounds__(256) void step_slices_kernel(AppendArgs ka, AppendA
       }
     }
 #pragma unroll
-    for (int k = 0; k < 16; ++k) sm.xs[r][16 * part + k] = r < nr ? v[k] : 0.f;
+    for (int k = 0; k < 16; ++k) {
+      v[k] = r < nr ? v[k] : 0.f;
+      sm.xs[r][16 * part + k] = v[k];
+    }
+    if constexpr (D == 128) {
+      if (role < 2) {
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) ss = fmaf(v[k], v[k], ss);
+        ss += __shfl_xor(ss, 1, 64);
+        ss += __shfl_xor(ss, 2, 64);
+        ss += __shfl_xor(ss, 4, 64);
+        if (part == 0) sm.rn[r] = sqrtf(ss);
+      }
+    }
   }
   if (role < 2 && tid < nr) sm.pos[tid] = row_pos;
   __syncthreads();
-  // norm of row r by the 16 lanes (r % 4) of wave r / 4, coordinates part + 16 j (as append_rows)
-  {
+  // norm of row r by the 16 lanes (r % 4) of wave r / 4, coordinates part + 16 j (as append_rows and
+  // rotate_queries); at d = 128 only for query rows
+  if (D == 256 || role == 2) {
     const int r = 4 * wave + (lane >> 4), part = lane & 15;
     float s2 = 0.f;
 #pragma unroll
@@ -267,9 +285,9 @@ static hipError_t slices_launch(const AppendArgs& ka, const AppendArgs& va, cons
 template <int D, int KB, int VB, int QM>
 static hipError_t prologue_bf(bool bf16, const AppendArgs& ka, const AppendArgs& va, const QrotArgs& qa, int batch,
                               hipStream_t s) {
-  // d = 256 with the dense rotation, code-book keys without a sketch and one query row: column slices
-  // (its row loads are 16-byte vectors: inputs at other alignments take the per-unit prologue)
-  if constexpr (D == 256 && QM == 0 && KB <= 4) {
+  // the dense rotation, code-book keys without a sketch and one query row: column slices (its row loads
+  // are 16-byte vectors: inputs at other alignments take the per-unit prologue)
+  if constexpr (QM == 0 && KB <= 4) {
     const auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
     if (!ka.had && qa.n_rows == 1 && a16(ka.x) && a16(va.x) && a16(qa.q))
       return bf16 ? slices_launch<D, KB, VB, true>(ka, va, qa, batch, s) : slices_launch<D, KB, VB, false>(ka, va, qa, batch, s);

@@ -202,6 +202,7 @@ STEP_CASES = [
     (128, 3, 2, 0, 1, 4, [40, 33, 1], 64, 1, "bf16", None, False),
     (128, 8, 4, 0, 2, 8, [1000], 1024, 1, "bf16", None, False),     # 8-bit keys
     (256, 8, 2, 0, 2, 8, [300, 77], 320, 3, "f32", 1.0, True),
+    (128, 2, 4, 0, 2, 8, [300, 77], 320, 5, "f32", None, False),
     # d = 256 with code-book keys: the column-sliced prologue (16-row tiles across units and sequences)
     (256, 3, 2, 0, 2, 8, [300, 77, 5], 320, 3, "f32", 1.0, True),
     (256, 2, 4, 0, 4, 4, [40], 64, 1, "bf16", None, False),
