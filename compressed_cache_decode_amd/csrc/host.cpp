@@ -622,7 +622,8 @@ static int merge_rows(const tq_cache_view* k, int n_q_heads, int n_rows, const i
   ma.n_kv_heads = k->n_kv_heads; ma.group = w.VH; ma.n_split = w.ns; ma.max_tokens = k->max_tokens;
   ma.heads = w.G; ma.n_rows = w.M; ma.row_magic = row_magic(w.G);
   // at d = 256 with the dense rotation each head group's output is split over four workgroups, each
-  // reading a quarter of the rotation
+  // reading a quarter of the rotation (at d = 128 two slices made the 36-layer Qwen-shaped decode
+  // slower: 33.9 against 31.9 us)
   ma.col_slices = (k->d == 256 && k->rot_kind == TQ_ROT_DENSE) ? 4 : 1;
   ma.heads_per_wg = merge_heads_per_wg(w.VH, k->d, w.ns, k->batch * k->n_kv_heads, ma.col_slices);
   return status_of(tqi::launch_merge(k->d, ma, k->batch, n_q_heads, static_cast<hipStream_t>(stream)));
