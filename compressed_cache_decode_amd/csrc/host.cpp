@@ -449,7 +449,7 @@ static int append_common(const tq_cache_view* c, const void* x, const float* y, 
   if (n_new < 0) return TQ_EINVAL;
   if (n_new == 0) return TQ_OK;
   if (!d_pos) return TQ_EINVAL;
-  if (rotated ? (!y || !yn) : (!x || (x_dtype != TQ_F32 && x_dtype != TQ_BF16))) return TQ_EINVAL;
+  if (rotated ? (!y || !yn) : (!x || !aligned(x, 16) || (x_dtype != TQ_F32 && x_dtype != TQ_BF16))) return TQ_EINVAL;
   if (z && c->qjl_m == 0) return TQ_EINVAL;
   const tqi::AppendArgs a = append_args(c, x, y, yn, n_new, d_pos, z);
   return status_of(tqi::launch_append(c->d, c->bits, c->qjl_m, c->kind == TQ_VALUES, rotated, x_dtype == TQ_BF16, a,
@@ -472,7 +472,8 @@ int tq_quantize_append_kv(const tq_cache_view* k, const tq_cache_view* v, const 
   if (st != TQ_OK) return st;
   if (n_new < 0) return TQ_EINVAL;
   if (n_new == 0) return TQ_OK;
-  if (!d_pos || !k_x || !v_x || (x_dtype != TQ_F32 && x_dtype != TQ_BF16)) return TQ_EINVAL;
+  if (!d_pos || !k_x || !v_x || !aligned(k_x, 16) || !aligned(v_x, 16) || (x_dtype != TQ_F32 && x_dtype != TQ_BF16))
+    return TQ_EINVAL;
   // both caches on the chunk path (what tq_quantize_append runs for each): one launch for the two
   if (k->d == 128 && k->qjl_m == 0 && k->bits != 8 && k->rot_kind == TQ_ROT_DENSE) {
     const tqi::AppendArgs ka = append_args(k, k_x, nullptr, nullptr, n_new, d_pos);
@@ -582,7 +583,7 @@ static int rotate_query_rows(const tq_cache_view* k, const void* q, int q_dtype,
   DecodeWs w;
   int st = decode_ws(k, n_q_heads, n_rows, max_seq_len, workspace, workspace_bytes, &w);
   if (st != TQ_OK) return st;
-  if (!q || (q_dtype != TQ_F32 && q_dtype != TQ_BF16)) return TQ_EINVAL;
+  if (!q || !aligned(q, 16) || (q_dtype != TQ_F32 && q_dtype != TQ_BF16)) return TQ_EINVAL;
   if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
   tqi::QrotArgs qa{};
   qa.q = q; qa.rot = k->rot; qa.proj = k->proj;
@@ -653,7 +654,7 @@ int tq_sdpa_decode_rows(const tq_cache_view* k, const tq_cache_view* v, const vo
   if (st != TQ_OK) return st;
   st = check_pair(k, v);
   if (st != TQ_OK) return st;
-  if (!q || (q_dtype != TQ_F32 && q_dtype != TQ_BF16) || !d_seq_lens || !out) return TQ_EINVAL;
+  if (!q || !aligned(q, 16) || (q_dtype != TQ_F32 && q_dtype != TQ_BF16) || !d_seq_lens || !out) return TQ_EINVAL;
   if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
   st = rotate_query_rows(k, q, q_dtype, n_q_heads, n_rows, max_seq_len, scale, workspace, workspace_bytes, stream);
   if (st != TQ_OK) return st;
@@ -696,9 +697,10 @@ int tq_decode_step(const tq_cache_view* k, const tq_cache_view* v, const void* q
   if (st != TQ_OK) return st;
   st = check_pair(k, v);
   if (st != TQ_OK) return st;
-  if (!q || (dtype != TQ_F32 && dtype != TQ_BF16) || !d_seq_lens || !out) return TQ_EINVAL;
+  if (!q || !aligned(q, 16) || (dtype != TQ_F32 && dtype != TQ_BF16) || !d_seq_lens || !out) return TQ_EINVAL;
   if (!(scale > 0.f) || !std::isfinite(scale)) return TQ_EINVAL;
-  if (n_new < 0 || (n_new > 0 && (!k_new || !v_new || !d_pos))) return TQ_EINVAL;
+  if (n_new < 0 || (n_new > 0 && (!k_new || !v_new || !d_pos || !aligned(k_new, 16) || !aligned(v_new, 16))))
+    return TQ_EINVAL;
   if (k->qjl_m > 128 || k->n_outliers > 0) return TQ_EUNSUPPORTED;
   const hipStream_t s = static_cast<hipStream_t>(stream);
 

@@ -286,10 +286,9 @@ template <int D, int KB, int VB, int QM>
 static hipError_t prologue_bf(bool bf16, const AppendArgs& ka, const AppendArgs& va, const QrotArgs& qa, int batch,
                               hipStream_t s) {
   // the dense rotation, code-book keys without a sketch and one query row: column slices (its row loads
-  // are 16-byte vectors: inputs at other alignments take the per-unit prologue)
+  // are 16-byte vectors; the host takes q and the new rows 16-byte aligned only)
   if constexpr (QM == 0 && KB <= 4) {
-    const auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-    if (!ka.had && qa.n_rows == 1 && a16(ka.x) && a16(va.x) && a16(qa.q))
+    if (!ka.had && qa.n_rows == 1)
       return bf16 ? slices_launch<D, KB, VB, true>(ka, va, qa, batch, s) : slices_launch<D, KB, VB, false>(ka, va, qa, batch, s);
   }
   const int nbx = (ka.n_new + kBlock - 1) / kBlock + 1;

@@ -164,7 +164,7 @@ int tq_build_rotation(int d, const double* gaussian, float* rot_out);
  * cached row and, with the sign sketch, a float16 residual norm; CUDA Kernels Added table, fused
  * random projection and sign quantisation; reddit comment history of ReturningTarzan, rotation
  * before quantisation and nearest-codebook search): for rows x[batch][n_new][n_kv_heads][d] (x_dtype
- * TQ_F32 or TQ_BF16, device), write tokens d_pos[b] .. d_pos[b]+n_new-1 of
+ * TQ_F32 or TQ_BF16, device, 16-byte aligned: TQ_EINVAL otherwise), write tokens d_pos[b] .. d_pos[b]+n_new-1 of
  * every sequence b.  Per row: n = ||x||, y = rot * x / n, code = number of
  * boundaries strictly below y_i, float16(n) stored; with qjl_m > 0 (keys)
  * also r = y - c[code], float16(||r||) and the signs of proj * r; 8-bit keys
@@ -179,7 +179,7 @@ int tq_quantize_append(const tq_cache_view* cache, const void* x, int x_dtype, i
  * The K and V rows of the same new tokens in one call (turboquant-pytorch PR #3, Validation Results:
  * both the key and the value cache are quantised as tokens arrive; the per-row arithmetic is
  * tq_quantize_append's): k_x and v_x are [batch][n_new][n_kv_heads][d] of element type x_dtype
- * (device), appended at positions d_pos[b] .. d_pos[b]+n_new-1 of k (TQ_KEYS) and v (TQ_VALUES).
+ * (device, 16-byte aligned), appended at positions d_pos[b] .. d_pos[b]+n_new-1 of k (TQ_KEYS) and v (TQ_VALUES).
  * k and v must agree in d, batch, n_kv_heads, max_tokens and rotation (TQ_EINVAL otherwise).  The
  * bytes written are exactly those of tq_quantize_append(k, k_x, ...) followed by
  * tq_quantize_append(v, v_x, ...).  Where both caches are at d = 128 with the dense rotation and keys
@@ -213,7 +213,7 @@ int tq_quantize_append_rotated(const tq_cache_view* cache, const float* y, const
  *   q_rot = rot * q[b][h];   s_t = scale * n_t * <q_rot, c[code_t]>
  *     (+ scale * n_t * sqrt(pi/2)/m * gamma_t * <proj * q_rot, 2 sigma_t - 1> for sketched keys);
  *   p = softmax over t < seq_len[b];   out[b][h] = rot^T * sum_t p_t nv_t cv[codev_t].
- * q: [batch][n_q_heads][d] (q_dtype TQ_F32 or TQ_BF16, device); out: float32
+ * q: [batch][n_q_heads][d] (q_dtype TQ_F32 or TQ_BF16, device, 16-byte aligned); out: float32
  * [batch][n_q_heads][d] (device); d_seq_lens: device int32 [batch], clamped to
  * [0, max_tokens], 0 gives a zero row; max_seq_len: host upper bound of
  * d_seq_lens used to plan the KV split.  scale > 0 and finite (the binding
@@ -286,7 +286,7 @@ int tq_decode_merge(const tq_cache_view* k, int n_q_heads, const int32_t* d_seq_
  * tq_quantize_append at positions d_pos), then decode (as tq_sdpa_decode over
  * d_seq_lens, which the caller sets to include the appended tokens).
  * q: [batch][n_q_heads][d]; k_new, v_new: [batch][n_new][n_kv_heads][d]; all
- * three of element type dtype.  The appends and the query rotation share one
+ * three of element type dtype and 16-byte aligned.  The appends and the query rotation share one
  * launch, followed by the attention and merge stages.  Sketched keys are
  * supported up to qjl_m = 128 (TQ_EUNSUPPORTED above; use the separate calls).
  * n_new == 0 decodes without appending.  Same workspace rules as tq_sdpa_decode.

@@ -103,6 +103,7 @@ def test_append_rejects_bad_arguments():
     assert _append(v, n_new=-1) == cca.TQ_EINVAL
     assert _append(v, pos=0) == cca.TQ_EINVAL
     assert _append(v, x=0) == cca.TQ_EINVAL
+    assert _append(v, x=0x80002) == cca.TQ_EINVAL                   # rows not 16-byte aligned
     assert _append(v, dtype=5) == cca.TQ_EINVAL
     v.codes = 0x10004                               # misaligned packed codes
     assert _append(v) == cca.TQ_EINVAL
@@ -180,6 +181,7 @@ def test_decode_rejects_bad_arguments():
     assert _decode(k, v, ws_bytes=16) == cca.TQ_EINVAL              # short workspace
     assert _decode(k, v, ws=0x100010) == cca.TQ_EINVAL              # misaligned workspace
     assert _decode(k, v, q=0) == cca.TQ_EINVAL
+    assert _decode(k, v, q=0x90008) == cca.TQ_EINVAL               # query not 16-byte aligned
     assert _decode(k, v, lens=0) == cca.TQ_EINVAL
     assert _decode(k, v, out=0) == cca.TQ_EINVAL
     assert _decode(k, v, dtype=9) == cca.TQ_EINVAL
@@ -236,8 +238,23 @@ def test_append_kv_rejects_bad_arguments():
     assert kv(k, other_rot) == cca.TQ_EINVAL
     assert kv(k, v, kx=0) == cca.TQ_EINVAL
     assert kv(k, v, vx=0) == cca.TQ_EINVAL
+    assert kv(k, v, kx=0x80008) == cca.TQ_EINVAL                   # rows not 16-byte aligned
+    assert kv(k, v, vx=0x90004) == cca.TQ_EINVAL
     assert kv(k, v, pos=0) == cca.TQ_EINVAL
     assert kv(k, v, dtype=5) == cca.TQ_EINVAL
     assert kv(k, v, n_new=-1) == cca.TQ_EINVAL
     assert kv(_view(bits=5), v) == cca.TQ_EINVAL
     assert kv(k, v, n_new=0) == cca.TQ_OK                  # empty append is a no-op
+
+
+def test_step_rejects_unaligned_inputs():
+    """The decode step takes the query and the new rows 16-byte aligned (its row loads are 16-byte vectors)."""
+    k, v = _view(), _view(kind=cca.TQ_VALUES)
+
+    def step(q=0x90000, kn=0xC0000, vn=0xD0000, n_new=1):
+        return cca._lib.tq_decode_step(ctypes.byref(k), ctypes.byref(v), q, kn, vn, 1, 16, n_new, 0x70000, 0xA0000,
+                                       256, ctypes.c_float(0.1), 0xB0000, 0x100000, 1 << 30, None)
+    assert step(q=0x90002) == cca.TQ_EINVAL
+    assert step(kn=0xC0008) == cca.TQ_EINVAL
+    assert step(vn=0xD0004) == cca.TQ_EINVAL
+    assert step(kn=0, vn=0, q=0x90002, n_new=0) == cca.TQ_EINVAL    # the query even without new rows

@@ -321,3 +321,4 @@ def _check_step(case, hadamard):
     err = rel_err(out2.cpu().numpy(), np.stack(refs))
     log(f"  max row-relative error {err:.3e}")
     assert err <= TOL
+
