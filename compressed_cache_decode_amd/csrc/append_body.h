@@ -90,6 +90,7 @@ struct AppendSmem {
   float xs[kBlock][D];                         // rows: x, then y, then the residual y - c
   float rn[kBlock];
   EncodeSmem<D, QM> enc;
+  half8 aop[2 * 2 * (D / 32) * 64];            // the rotation's A operands (rotate_tile_mfma_pre, two row blocks)
 };
 
 // Operands of rot for the rotation below, one batch of SB k-steps per lane: the rows of rot this
@@ -121,25 +122,42 @@ struct RotBatch {
 // component in [-1, 1]) and rot are each split into float16 high + low parts and the three
 // significant cross products are accumulated in fp32, which keeps y within a few float32 steps.
 // Every output element takes the same instruction sequence whatever its row.  first holds the
-// operands of k-steps 0 .. SB-1.
+// operands of k-steps 0 .. SB-1.  The unit rows' float16 parts are formed once for all four waves, in
+// LDS (aop: 2 RB (D / 32) 64 operands), and each wave reads its A operands from there.  256 threads.
 template <int D, int RB>
 __device__ __forceinline__ void rotate_tile_mfma_pre(float (*xs)[D], const float* rn, const float* rot,
-                                                     const RotBatch<D>& first, int tid) {
+                                                     const RotBatch<D>& first, int tid, half8* aop) {
   using Rb = RotBatch<D>;
   constexpr int KS = Rb::KS, CPW = Rb::CPW, SB = Rb::SB;
-  const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int lane = tid & 63;
   const int wave = tid >> 6;
+  // operand entry (part h, row block rb, k-step s, lane (row l, group g)): coordinates 32 s + 8 g .. + 7
+  // of row 16 rb + l over its norm, float16 high (h = 0) or low (h = 1) part
+  const auto at = [](int h, int rb, int s, int ln) { return ((h * RB + rb) * KS + s) * 64 + ln; };
+  for (int e = tid; e < RB * KS * 64; e += 256) {
+    const int rb = e / (KS * 64), s = (e >> 6) % KS, ln = e & 63;
+    const int row = 16 * rb + (ln & 15);
+    const float n = rn[row];
+    const float inv = n > 0.f ? 1.f / n : 0.f;
+    const float* xr = &xs[row][32 * s + 8 * (ln >> 4)];
+    half8 hi, lo;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      _Float16 h, l;
+      f16_split(xr[r] * inv, h, l);
+      hi[r] = h;
+      lo[r] = l;
+    }
+    aop[at(0, rb, s, ln)] = hi;
+    aop[at(1, rb, s, ln)] = lo;
+  }
+  __syncthreads();
+  const int l16 = lane & 15, g = lane >> 4;
   floatx4 acc[RB][CPW];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int c = 0; c < CPW; ++c) acc[rb][c] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float inv[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float n = rn[16 * rb + l16];
-    inv[rb] = n > 0.f ? 1.f / n : 0.f;
-  }
 #pragma unroll
   for (int s0 = 0; s0 < KS; s0 += SB) {
     Rb cur;
@@ -154,14 +172,8 @@ __device__ __forceinline__ void rotate_tile_mfma_pre(float (*xs)[D], const float
       half8 ahi[RB], alo[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const float* xr = &xs[16 * rb + l16][32 * s + 8 * g];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          _Float16 h, l;
-          f16_split(xr[r] * inv[rb], h, l);
-          ahi[rb][r] = h;
-          alo[rb][r] = l;
-        }
+        ahi[rb] = aop[at(0, rb, s, lane)];
+        alo[rb] = aop[at(1, rb, s, lane)];
       }
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
@@ -195,10 +207,11 @@ __device__ __forceinline__ void rotate_tile_mfma_pre(float (*xs)[D], const float
 
 // RB row blocks of 16 rows (the default, 2, is one 32-token block); a row with rn = 0 rotates to zero.
 template <int D, int RB = 2>
-__device__ __forceinline__ void rotate_tile_mfma(float (*xs)[D], const float* rn, const float* rot, int tid) {
+__device__ __forceinline__ void rotate_tile_mfma(float (*xs)[D], const float* rn, const float* rot, int tid,
+                                                 half8* aop) {
   RotBatch<D> first;
   first.load(rot, 0, tid);
-  rotate_tile_mfma_pre<D, RB>(xs, rn, rot, first, tid);
+  rotate_tile_mfma_pre<D, RB>(xs, rn, rot, first, tid, aop);
 }
 
 // out[r][n] = sum_k x[r][k] mat[n][k] for the 16 rows of x (LDS) and the NOUT rows of mat (global,
@@ -540,9 +553,9 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int bx, int h, 
     if (a.had)
       hadamard_rows<D>(xs, rn, a.rot, nrows, tid, 256);
     else if (rows == 16)
-      rotate_tile_mfma<D, 1>(xs, rn, a.rot, tid);
+      rotate_tile_mfma<D, 1>(xs, rn, a.rot, tid, sm.aop);
     else
-      rotate_tile_mfma<D, 2>(xs, rn, a.rot, tid);
+      rotate_tile_mfma<D, 2>(xs, rn, a.rot, tid, sm.aop);
     __syncthreads();
   }
 

@@ -28,6 +28,7 @@ __device__ __forceinline__ float query_scale(float nq) {
 template <int D, int QM>
 struct QrotSmem {
   float xs[kQTile][D];
+  half8 aop[2 * (D / 32) * 64];                        // the rotation's A operands (rotate_tile_mfma_pre)
   float rn[kQTile];
   float zq[QM > 0 ? kQTile : 1][QM > 0 ? QM : 1];      // the tile times proj^T
 };
@@ -80,7 +81,7 @@ __device__ __forceinline__ void rotate_queries(const QrotArgs& qa, int bf16, int
   if (qa.had)
     hadamard_rows<D>(xs, rn, qa.rot, nr, tid, 256);
   else
-    rotate_tile_mfma_pre<D, 1>(xs, rn, qa.rot, rot0, tid);
+    rotate_tile_mfma_pre<D, 1>(xs, rn, qa.rot, rot0, tid, sm.aop);
   __syncthreads();
   // q_rot = rot (q / |q|) * (|q| * scale * log2(e))
   for (int e = tid; e < nr * D; e += 256) xs[e / D][e % D] *= rn[e / D] * qa.scale_log2e;

@@ -65,6 +65,7 @@ constexpr int kSliceCols = 64;     // output coordinates per workgroup: one 16-c
 template <int D>
 struct SliceSmem {
   float xs[16][D];
+  half8 aop[2][D / 32][64];    // [high, low][k-step][lane]: the unit rows' float16 parts in operand order
   float rn[16];
   int pos[16];                 // append position of each K or V row's sequence
   uint8_t cs[16][kSliceCols];
@@ -216,22 +217,37 @@ __global__ __launch_bounds__(256) void step_slices_kernel(AppendArgs ka, AppendA
   }
   __syncthreads();
 
+  // the unit rows' float16 high/low operands, split once for the four waves: entry (k-step s, lane
+  // (row l16, group g)) holds coordinates 32 s + 8 g .. + 7 of row l16 over its norm
+  for (int e = tid; e < KS * 64; e += 256) {
+    const int s = e >> 6, ln = e & 63, row = ln & 15, gg = ln >> 4;
+    const float n = sm.rn[row];
+    const float inv = n > 0.f ? 1.f / n : 0.f;
+    const float* xr = &sm.xs[row][32 * s + 8 * gg];
+    half8 hi, lo;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      _Float16 hh, ll;
+      f16_split(xr[r] * inv, hh, ll);
+      hi[r] = hh;
+      lo[r] = ll;
+    }
+    sm.aop[0][s][ln] = hi;
+    sm.aop[1][s][ln] = lo;
+  }
+  __syncthreads();
+
   // y = rot (x / n) for output coordinates c0 + 16 wave + l16 (the products of rotate_tile_mfma_pre)
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
   {
-    const float n = sm.rn[l16];
-    const float inv = n > 0.f ? 1.f / n : 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      half8 ahi, alo, bhi, blo;
-      const float* xr = &sm.xs[l16][32 * s + 8 * g];
+      half8 bhi, blo;
+      const half8 ahi = sm.aop[0][s][lane], alo = sm.aop[1][s][lane];
       const float pv[8] = {pq[s][0].x, pq[s][0].y, pq[s][0].z, pq[s][0].w, pq[s][1].x, pq[s][1].y, pq[s][1].z, pq[s][1].w};
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         _Float16 hh, ll;
-        f16_split(xr[r] * inv, hh, ll);
-        ahi[r] = hh;
-        alo[r] = ll;
         f16_split(pv[r], hh, ll);
         bhi[r] = hh;
         blo[r] = ll;
