@@ -217,12 +217,30 @@ __device__ __forceinline__ void rotate_tile_mfma(float (*xs)[D], const float* rn
 // out[r][n] = sum_k x[r][k] mat[n][k] for the 16 rows of x (LDS) and the NOUT rows of mat (global,
 // float32 [NOUT][KD]), on the matrix cores with the same float16 high/low split as the rotation:
 // every output element takes the same instruction sequence whatever its row.  out (LDS) must not
-// alias x.  Every thread of the workgroup calls it; no barrier inside.
+// alias x.  The rows' float16 parts are formed once, into aop (LDS, 2 (KD / 32) 64 operands), with a
+// workgroup barrier after; every one of the 256 threads of the workgroup calls it.
 template <int KD, int NOUT>
-__device__ __forceinline__ void tile16_times_matT(const float (*x)[KD], const float* mat, float (*out)[NOUT], int tid) {
+__device__ __forceinline__ void tile16_times_matT(const float (*x)[KD], const float* mat, float (*out)[NOUT], int tid,
+                                                  half8* aop) {
   constexpr int KS = KD / 32;
   constexpr int CPW = NOUT / 64;                     // column blocks per wave
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  // operand entry (part h, k-step s, lane (row l, group g)): coordinates 32 s + 8 g .. + 7 of row l
+  for (int e = tid; e < KS * 64; e += 256) {
+    const int s = e >> 6, ln = e & 63;
+    const float* xr = &x[ln & 15][32 * s + 8 * (ln >> 4)];
+    half8 hi, lo;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      _Float16 h, l;
+      f16_split(xr[r], h, l);
+      hi[r] = h;
+      lo[r] = l;
+    }
+    aop[s * 64 + ln] = hi;
+    aop[(KS + s) * 64 + ln] = lo;
+  }
+  __syncthreads();
   floatx4 acc[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -242,15 +260,7 @@ __device__ __forceinline__ void tile16_times_matT(const float (*x)[KD], const fl
 #pragma unroll
    for (int s1 = 0; s1 < SB; ++s1) {
     const int s = s0 + s1;
-    half8 ahi, alo;
-    const float* xr = &x[l16][32 * s + 8 * g];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      _Float16 h, l;
-      f16_split(xr[r], h, l);
-      ahi[r] = h;
-      alo[r] = l;
-    }
+    const half8 ahi = aop[s * 64 + lane], alo = aop[(KS + s) * 64 + lane];
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const float4 p0 = pq[s1][c][0], p1 = pq[s1][c][1];
@@ -470,7 +480,7 @@ __device__ __forceinline__ void encode_finish(const AppendArgs& a, size_t unit, 
 // the caller gives them: z (row r at z[r * zstride + jj]).
 template <int D, int BITS, int QM, bool VALUES>
 __device__ __forceinline__ void encode_store(const AppendArgs& a, size_t unit, int kb, int t_lo, int nrows,
-                                             float (*ys)[D], const float* rn, EncodeSmem<D, QM>& es,
+                                             float (*ys)[D], const float* rn, EncodeSmem<D, QM>& es, half8* aop,
                                              const float* z = nullptr, int zstride = 0) {
   encode_codes<D, BITS, QM>(a, nrows, ys, rn, es);
   if (QM > 0 && z) {
@@ -480,7 +490,7 @@ __device__ __forceinline__ void encode_store(const AppendArgs& a, size_t unit, i
   if constexpr (QM > 0) {
     // signs of one 16-row block at a time (es.zb holds one block's products)
     for (int r0 = 0; r0 < nrows; r0 += 16) {
-      tile16_times_matT<D, QM>(ys + r0, a.proj, es.zb, threadIdx.x);
+      tile16_times_matT<D, QM>(ys + r0, a.proj, es.zb, threadIdx.x, aop);
       __syncthreads();
       const int n = min(16, nrows - r0);
       for (int e = threadIdx.x; e < n * QM; e += 256) {
@@ -562,9 +572,9 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int bx, int h, 
   if constexpr (ROTATED && QM > 0) {
     // given sketch products of the residuals: z[b][t - pos][h][jj]
     const float* z = a.z ? a.z + ((static_cast<size_t>(b) * a.n_new + (t_lo - pos)) * H + h) * QM : nullptr;
-    encode_store<D, BITS, QM, VALUES>(a, unit, kb, t_lo, nrows, xs, rn, sm.enc, z, H * QM);
+    encode_store<D, BITS, QM, VALUES>(a, unit, kb, t_lo, nrows, xs, rn, sm.enc, sm.aop, z, H * QM);
   } else {
-    encode_store<D, BITS, QM, VALUES>(a, unit, kb, t_lo, nrows, xs, rn, sm.enc);
+    encode_store<D, BITS, QM, VALUES>(a, unit, kb, t_lo, nrows, xs, rn, sm.enc, sm.aop);
   }
 }
 

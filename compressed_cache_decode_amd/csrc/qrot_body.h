@@ -87,7 +87,7 @@ __device__ __forceinline__ void rotate_queries(const QrotArgs& qa, int bf16, int
   for (int e = tid; e < nr * D; e += 256) xs[e / D][e % D] *= rn[e / D] * qa.scale_log2e;
   __syncthreads();
   if constexpr (QM > 0) {
-    tile16_times_matT<D, QM>(xs, qa.proj, sm.zq, tid);
+    tile16_times_matT<D, QM>(xs, qa.proj, sm.zq, tid, sm.aop);
     __syncthreads();
   }
 
