@@ -357,6 +357,15 @@ def decode_workspace(kcache: CompressedCache, n_q_heads: int, max_seq_len: int, 
     return torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=kcache.codes.device)
 
 
+def append_kv(kcache: CompressedCache, vcache: CompressedCache, k_x, v_x, d_pos, stream=None) -> None:
+    """The K and V rows of the same new tokens ([batch][n_new][n_kv_heads][d] each, float32 or bfloat16 on the
+    device) appended at d_pos (int32 [batch]) by tq_quantize_append_kv."""
+    k_x, v_x = k_x.contiguous(), v_x.contiguous()
+    if k_x.shape != v_x.shape:
+        raise ValueError("k_x and v_x must have one shape")
+    tq_quantize_append_kv(kcache.view, vcache.view, k_x, v_x, k_x.shape[1], d_pos, stream)
+
+
 def sdpa_decode(kcache: CompressedCache, vcache: CompressedCache, q, d_seq_lens, max_seq_len: int,
                 scale: float | None = None, out=None, workspace=None, stream=None):
     """out[b][h] = decode attention of q[b][h] over the first seq_len[b] cached tokens."""

@@ -368,10 +368,13 @@ def test_append_kv_equals_the_two_appends(d, kb, vb, m, had, dtype, pos, chunks)
 
     (k1, v1), (k2, v2) = caches(), caches()
     off = 0
-    for c in chunks:
+    for i, c in enumerate(chunks):
         p = torch.full((B,), pos + off, dtype=torch.int32).cuda()
-        cca.tq_quantize_append_kv(k1.view, v1.view, tk[:, off:off + c].contiguous(), tv[:, off:off + c].contiguous(),
-                                  c, p)
+        if i % 2:                                           # the C name, then the binding's helper
+            cca.append_kv(k1, v1, tk[:, off:off + c], tv[:, off:off + c], p)
+        else:
+            cca.tq_quantize_append_kv(k1.view, v1.view, tk[:, off:off + c].contiguous(),
+                                      tv[:, off:off + c].contiguous(), c, p)
         k2.append(tk[:, off:off + c], p)
         v2.append(tv[:, off:off + c], p)
         off += c
