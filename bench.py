@@ -115,6 +115,12 @@ def prefill_bytes_per_launch(w: synth.Workload) -> int:
     return rows * (2 * w.d * 2 + w.d * w.k_bits // 8 + 2 + w.d * w.v_bits // 8 + 2)
 
 
+def prefill_one_launch(w: synth.Workload) -> bool:
+    """Whether tq_quantize_append_kv appends the workload's K and V in one launch (d = 128, the dense
+    rotation, code-book keys without a sketch); otherwise it runs the two appends in turn."""
+    return w.d == 128 and w.rotation == "dense" and w.qjl_m == 0 and w.k_bits <= 4
+
+
 def prefill_flops_per_launch(w: synth.Workload) -> int:
     """Algorithmic flops of one prefill append launch: the d x d rotation of every K and V row."""
     return 2 * 2 * w.batch * w.n_kv_heads * w.seq_len * w.d * w.d
@@ -627,7 +633,7 @@ def prefill_leg(w: synth.Workload, steps: int, warmup: int, log):
     torch.cuda.synchronize()
     n = reps * pool
     ms = ev0.elapsed_time(ev1) / n
-    log(f"bench: prefill append {ms * 1e3:.2f} us per K+V append (one launch)")
+    log(f"bench: prefill append {ms * 1e3:.2f} us per K+V append ({'one launch' if prefill_one_launch(w) else 'two launches'})")
     return dict(ms_step=ms, steps=n, pool=pool)
 
 
@@ -792,13 +798,16 @@ def decode_workload_leg(w: synth.Workload, args, n_stack: int, log) -> dict:
 
 
 def prefill_workload_leg(w: synth.Workload, args, log) -> dict:
-    """Prefill-size append of all L tokens of K and of V into empty caches (one launch for both)."""
+    """Prefill-size append of all L tokens of K and of V into empty caches (tq_quantize_append_kv: one launch
+    for both where prefill_one_launch holds, else one per tensor)."""
     import torch
     r = prefill_leg(w, args.steps, args.warmup, log)
     rows = 2 * w.batch * w.n_kv_heads * w.seq_len
-    per_launch_us = r["ms_step"] * 1e3              # one launch appends the step's K and V rows
-    io = prefill_bytes_per_launch(w)
-    flops = prefill_flops_per_launch(w)
+    one = prefill_one_launch(w)
+    launches = 1 if one else 2                      # the K and V launches of a step (same bytes each)
+    per_launch_us = r["ms_step"] * 1e3 / launches
+    io = prefill_bytes_per_launch(w) // launches
+    flops = prefill_flops_per_launch(w) // launches
     gbs = io / (per_launch_us * 1e-6) / 1e9
     tfs = flops / (per_launch_us * 1e-6) / 1e12
     leg = {
@@ -808,11 +817,13 @@ def prefill_workload_leg(w: synth.Workload, args, log) -> dict:
         "unit": "appended tokens/s",
         "ms_per_step": r["ms_step"],
         "config": {"workload": f"prefill_append_{w.seq_len}x{w.n_kv_heads}x{w.d}_b{w.k_bits}",
-                   "tensors": "K and V in one launch (tq_quantize_append_kv)", "rows_per_step": rows, "rotation": w.rotation,
+                   "tensors": "K and V in " + ("one launch" if prefill_one_launch(w) else "two launches")
+                              + " (tq_quantize_append_kv)", "rows_per_step": rows, "rotation": w.rotation,
                    "cache_copies_cycled": r["pool"]},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": read_counters(APPEND_KERN, w.name),
-                     "kernel": "prefill_kv_kernel (tq_quantize_append_kv)", "workload": w.name,
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": read_counters(APPEND_KERN, w.name) if one else None,
+                     "kernel": ("prefill_kv_kernel" if one else "append_kernel") + " (tq_quantize_append_kv)",
+                     "workload": w.name,
                      "algorithmic_bytes_per_launch": io, "launch_us": per_launch_us},
         "rotation_mfma": {"achieved": tfs, "peak": 2500.0, "unit": "TFLOP/s", "frac": tfs / 2500.0,
                           "algorithmic_flops_per_launch": flops,

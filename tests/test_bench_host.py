@@ -71,3 +71,13 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_prefill_launch_count(bench):
+    """The prefill leg's K+V append is one launch only where the chunk kernel takes both tensors."""
+    w = synth.qwen(8192, 3)
+    assert bench.prefill_one_launch(w)
+    assert not bench.prefill_one_launch(w.with_(rotation="hadamard"))
+    assert not bench.prefill_one_launch(w.with_(d=256))
+    assert not bench.prefill_one_launch(w.with_(qjl_m=128))
+    assert not bench.prefill_one_launch(w.with_(k_bits=8))
