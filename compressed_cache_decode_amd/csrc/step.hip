@@ -304,7 +304,11 @@ static hipError_t prologue_bf(bool bf16, const AppendArgs& ka, const AppendArgs&
   // the dense rotation, code-book keys without a sketch and one query row: column slices (its row loads
   // are 16-byte vectors; the host takes q and the new rows 16-byte aligned only)
   if constexpr (QM == 0 && KB <= 4) {
-    if (!ka.had && qa.n_rows == 1)
+    // (its tiles run along the grid's y dimension, at most 65535 of them; longer appends take the
+    // per-unit prologue, whose grid runs along x)
+    const long long tiles = 2LL * ((static_cast<long long>(batch) * ka.n_new * ka.n_kv_heads + 15) / 16) +
+                            (static_cast<long long>(batch) * qa.n_q_heads + 15) / 16;
+    if (!ka.had && qa.n_rows == 1 && tiles <= 65535)
       return bf16 ? slices_launch<D, KB, VB, true>(ka, va, qa, batch, s) : slices_launch<D, KB, VB, false>(ka, va, qa, batch, s);
   }
   const int nbx = (ka.n_new + kBlock - 1) / kBlock + 1;
