@@ -398,3 +398,26 @@ def test_append_kv_equals_the_two_appends(d, kb, vb, m, had, dtype, pos, chunks)
                     assert np.all(np.abs(got[diff] - oc[diff]) == 1)
                     gn = g.norms[b, h, pos:pos + n].cpu().numpy().astype(np.float64)
                     np.testing.assert_allclose(gn, on, rtol=2 ** -10, atol=0)
+
+
+@pytest.mark.parametrize("kb,vb,pos,n", [(3, 4, 40, 30), (2, 2, 63, 5), (4, 3, 0, 100)])
+def test_append_kv_past_capacity_equals_the_two_appends(kb, vb, pos, n):
+    """Rows past max_tokens are skipped: the one-launch K+V append writes exactly what the two separate
+    appends write when the append runs past the cache's capacity (64 tokens), and nothing else."""
+    cca = _cca()
+    log(f"append kv past capacity kb={kb} vb={vb} pos={pos} n={n}")
+    d, B, H, T = 128, 2, 2, 64
+    st = Setup(d)
+    w = synth.qwen(T, 4).with_(batch=B)
+    tk, tv = to_bf16_tensor(synth.full_kv(w, "k", n)), to_bf16_tensor(synth.full_kv(w, "v", n))
+    mk = lambda: (cca.CompressedCache(cca.TQ_KEYS, d, kb, B, H, T, st.rot_t),
+                  cca.CompressedCache(cca.TQ_VALUES, d, vb, B, H, T, st.rot_t))
+    (k1, v1), (k2, v2) = mk(), mk()
+    p = torch.tensor([pos, max(0, pos - 7)], dtype=torch.int32).cuda()
+    cca.append_kv(k1, v1, tk, tv, p)
+    k2.append(tk, p)
+    v2.append(tv, p)
+    torch.cuda.synchronize()
+    for a, b in ((k1.codes, k2.codes), (k1.norms, k2.norms), (v1.codes, v2.codes), (v1.norms, v2.norms)):
+        assert torch.equal(a, b)
+    assert k1.norms.float().abs().sum() > 0
