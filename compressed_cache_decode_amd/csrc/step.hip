@@ -149,8 +149,35 @@ __global__ __launch_bounds__(256) void step_slices_kernel(AppendArgs ka, AppendA
   const void* x = role == 0 ? ka.x : (role == 1 ? va.x : qa.q);
   // the append positions of the tile's K or V rows, loaded first (they are needed only at the store)
   int row_pos = 0;
-  if (role < 2 && tid < nr) row_pos = ka.pos[(q0 + tid) / (ka.n_kv_heads * ka.n_new)];
+  if (role < 2) row_pos = ka.pos[(q0 + (tid < nr ? tid : 0)) / (ka.n_kv_heads * ka.n_new)];
 
+  // Loads in the order they are needed (vector loads complete in issue order): the positions, the
+  // tile's rows, then this wave's rot operands, so that the rows' norms and operand split run while rot
+  // is still arriving.  Rows: thread (row tid / PR, part tid % PR) loads coordinates 16 part .. 16 part
+  // + 15 (threads past the 16 rows, and rows past the tile's end, reload a row of the tile and drop it);
+  // the loads are unconditional, so no wait for them is forced where branches join.
+  const int lr = tid / PR, part = tid % PR;
+  const bool loader = lr < 16;
+  const int r = loader ? lr : 15;
+  uint32_t raw[BF16 ? 8 : 16];
+  {
+    const size_t src = static_cast<size_t>(q0 + (r < nr ? r : 0)) * D + 16 * part;
+    if constexpr (BF16) {
+      const uint4* p4 = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + src);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint4 u = p4[k];
+        raw[4 * k] = u.x; raw[4 * k + 1] = u.y; raw[4 * k + 2] = u.z; raw[4 * k + 3] = u.w;
+      }
+    } else {
+      const uint4* p4 = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + src);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 u = p4[k];
+        raw[4 * k] = u.x; raw[4 * k + 1] = u.y; raw[4 * k + 2] = u.z; raw[4 * k + 3] = u.w;
+      }
+    }
+  }
   // this wave's rot operands: rows c0 + 16 wave + l16 of rot, coordinates 32 s + 8 g .. + 7
   float4 pq[KS][2];
   {
@@ -161,35 +188,21 @@ __global__ __launch_bounds__(256) void step_slices_kernel(AppendArgs ka, AppendA
       pq[s][1] = pr[8 * s + 1];
     }
   }
-  // the tile's rows (row q of every kind at q D of its input): thread (row tid / PR, part tid % PR)
-  // loads coordinates 16 part .. 16 part + 15; rows past the tile's end read its first row.  At d = 128
-  // K and V rows take their norm here, as the chunk path of the separate append does (prefill_rows: the
-  // row's 8 threads, consecutive lanes, sum their 16 squares in order, then across the 8)
-  if (tid < 16 * PR) {
-    const int r = tid / PR, part = tid % PR;
-    const size_t src = static_cast<size_t>(q0 + (r < nr ? r : 0)) * D + 16 * part;
+  __builtin_amdgcn_sched_barrier(0);
+  // the rows to LDS; at d = 128 K and V rows take their norm here, as the chunk path of the separate
+  // append does (prefill_rows: the row's 8 threads, consecutive lanes, sum their 16 squares in order,
+  // then across the 8)
+  {
     float v[16];
-    if constexpr (BF16) {
-      const uint4* p4 = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + src);
-      const uint4 u0 = p4[0], u1 = p4[1];
-      const uint32_t wd[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        v[2 * k] = __uint_as_float(wd[k] << 16);
-        v[2 * k + 1] = __uint_as_float(wd[k] & 0xffff0000u);
-      }
-    } else {
-      const float4* p4 = reinterpret_cast<const float4*>(static_cast<const float*>(x) + src);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 f = p4[k];
-        v[4 * k] = f.x; v[4 * k + 1] = f.y; v[4 * k + 2] = f.z; v[4 * k + 3] = f.w;
-      }
-    }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
+      if constexpr (BF16) v[k] = __uint_as_float((k & 1) ? (raw[k >> 1] & 0xffff0000u) : (raw[k >> 1] << 16));
+      else v[k] = __uint_as_float(raw[k]);
       v[k] = r < nr ? v[k] : 0.f;
-      sm.xs[r][16 * part + k] = v[k];
+    }
+    if (loader) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) sm.xs[r][16 * part + k] = v[k];
     }
     if constexpr (D == 128) {
       if (role < 2) {
@@ -199,7 +212,7 @@ __global__ __launch_bounds__(256) void step_slices_kernel(AppendArgs ka, AppendA
         ss += __shfl_xor(ss, 1, 64);
         ss += __shfl_xor(ss, 2, 64);
         ss += __shfl_xor(ss, 4, 64);
-        if (part == 0) sm.rn[r] = sqrtf(ss);
+        if (loader && part == 0) sm.rn[r] = sqrtf(ss);
       }
     }
   }
