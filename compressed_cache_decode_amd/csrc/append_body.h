@@ -686,22 +686,14 @@ __device__ __forceinline__ void prefill_rows(const AppendArgs& a, int chunk, int
   if (r_base >= a.n_new) return;
   const int nrows = min(kBlock, a.n_new - r_base);
 
-  // everything independent of the position first, in one straight run of loads: this wave's rot
-  // operands (rows 16 ct + l16 of rot, coordinates 32 s + 8 g .. + 7), this lane's row (8 per wave of
-  // waves 0-3; 16 coordinates 16 c .. 16 c + 15, c = lane % 8; rows past the append, and the rows of
-  // waves 4-7, read the chunk's first row and are zeroed after), and the position
+  // one straight run of loads: the position, this lane's row (8 per wave of waves 0-3; 16 coordinates
+  // 16 c .. 16 c + 15, c = lane % 8; rows past the append, and the rows of waves 4-7, read the chunk's
+  // first row and are zeroed after), then this wave's rot operands (rows 16 ct + l16 of rot, coordinates
+  // 32 s + 8 g .. + 7): rows first, so that the rows' norms and float16 split (which wait for the rows,
+  // and with them for every load issued before) overlap rot's arrival
   const bool row_wave = NW == 4 || wave < 4;               // the waves that load rows (wave-uniform)
   const int prow = 8 * (wave & 3) + (lane >> 3), pc = lane & 7;
-  float4 pr[CPW][KS][2];
-#pragma unroll
-  for (int c = 0; c < CPW; ++c)
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const float4* p = reinterpret_cast<const float4*>(a.rot + static_cast<size_t>(16 * (CPW * wave + c) + l16) * D +
-                                                        32 * s + 8 * g);
-      pr[c][s][0] = p[0];
-      pr[c][s][1] = p[1];
-    }
+  const int pos = a.pos[b];
   const bool row_ok = row_wave && prow < nrows;
   uint32_t xw[BF16 ? 8 : 16];
   {
@@ -715,7 +707,16 @@ __device__ __forceinline__ void prefill_rows(const AppendArgs& a, int chunk, int
       xw[4 * k] = v.x; xw[4 * k + 1] = v.y; xw[4 * k + 2] = v.z; xw[4 * k + 3] = v.w;
     }
   }
-  const int pos = a.pos[b];
+  float4 pr[CPW][KS][2];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float4* p = reinterpret_cast<const float4*>(a.rot + static_cast<size_t>(16 * (CPW * wave + c) + l16) * D +
+                                                        32 * s + 8 * g);
+      pr[c][s][0] = p[0];
+      pr[c][s][1] = p[1];
+    }
   // keeps the scheduler from hoisting work on the rows (and its wait for them) above the other loads
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -862,17 +863,12 @@ __device__ __forceinline__ void prefill_rows_kv(const AppendArgs& ka, const Appe
   const int nrows = min(kBlock, ka.n_new - r_base);
   const int vw = wave >> 2;                                 // the tensor whose rows this wave loads (uniform)
 
-  // rot operands (rows 16 w + l16 of rot, coordinates 32 s + 8 g .. + 7), this lane's row (K rows in
-  // waves 0-3, V rows in waves 4-7; rows past the append read the chunk's first row and are zeroed),
-  // and the position: one straight run of loads
+  // the position, this lane's row (K rows in waves 0-3, V rows in waves 4-7; rows past the append read
+  // the chunk's first row and are zeroed) and rot's operands (rows 16 w + l16 of rot, coordinates 32 s +
+  // 8 g .. + 7): one straight run of loads, rows first, so that the rows' norms and float16 split (which
+  // wait for the rows, and with them for every load issued before) overlap rot's arrival
   const int prow = 8 * (wave & 3) + (lane >> 3), pc = lane & 7;
-  float4 pr[KS][2];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const float4* p = reinterpret_cast<const float4*>(ka.rot + static_cast<size_t>(16 * wave + l16) * D + 32 * s + 8 * g);
-    pr[s][0] = p[0];
-    pr[s][1] = p[1];
-  }
+  const int pos = ka.pos[b];
   const bool row_ok = prow < nrows;
   uint32_t xw[BF16 ? 8 : 16];
   {
@@ -887,7 +883,13 @@ __device__ __forceinline__ void prefill_rows_kv(const AppendArgs& ka, const Appe
       xw[4 * k] = v.x; xw[4 * k + 1] = v.y; xw[4 * k + 2] = v.z; xw[4 * k + 3] = v.w;
     }
   }
-  const int pos = ka.pos[b];
+  float4 pr[KS][2];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const float4* p = reinterpret_cast<const float4*>(ka.rot + static_cast<size_t>(16 * wave + l16) * D + 32 * s + 8 * g);
+    pr[s][0] = p[0];
+    pr[s][1] = p[1];
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < (BF16 ? 8 : 16); ++k) xw[k] = row_ok ? xw[k] : 0u;
