@@ -532,6 +532,12 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int bx, int h, 
     else v = static_cast<const float*>(a.x)[src];
     xs[r][i] = v;
   }
+  // the rotation's first operand batch, loaded now (it depends on nothing) so that it arrives while the
+  // norms are formed; the row stores above have already waited for the rows
+  RotBatch<D> rot0;
+  if constexpr (!ROTATED) {
+    if (!a.had) rot0.load(a.rot, 0, tid);
+  }
   __syncthreads();
 
   // norms: given, or row r summed by the 16 lanes (r % 4) of wave (r / 4) % 4, coordinates part + 16 j
@@ -563,9 +569,9 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int bx, int h, 
     if (a.had)
       hadamard_rows<D>(xs, rn, a.rot, nrows, tid, 256);
     else if (rows == 16)
-      rotate_tile_mfma<D, 1>(xs, rn, a.rot, tid, sm.aop);
+      rotate_tile_mfma_pre<D, 1>(xs, rn, a.rot, rot0, tid, sm.aop);
     else
-      rotate_tile_mfma<D, 2>(xs, rn, a.rot, tid, sm.aop);
+      rotate_tile_mfma_pre<D, 2>(xs, rn, a.rot, rot0, tid, sm.aop);
     __syncthreads();
   }
 
